@@ -1,0 +1,222 @@
+"""Plain fp64 CPU oracle for masked scaled-dot-product attention: forward with
+per-row logsumexp, and the closed-form gradient (dQ, dK, dV).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of bench.py use it. It shares no code with the HIP library.
+
+What is computed, and where the pages define it
+------------------------------------------------
+* The forward keeps "the per-row softmax normalizer the backward reuses", the
+  logsumexp (page "Lab 028 lab detail: Off NVIDIA, you fix the platform
+  yourself", section "What I changed, in plain terms", item 1). The backward
+  recomputes the softmax probability P from the scores and that lse and forms
+  P and dS per element (same page, section "2026-10-21", "What the code says";
+  page "Training - design (ORPO, flash-CCE head, prefix sharing, segmented
+  backward)", section 6, which lists a fused backward that stores per-row LSE
+  and recomputes P).
+* Masks: above the causal diagonal P is zero; a window additionally zeroes P
+  where the key index is below ``i + diag_off - window_size + 1`` (Lab 028
+  page, "Plan for the build", step 4, and "What I changed", items 3-4). With
+  queries a suffix of the keys, ``diag_off = Lk - Lq``.
+* GQA: query head h reads kv head ``h // group`` (page "MiniCPM5 Decode
+  Megakernel - end-to-end build plan (handoff)", section 4, per-layer stage 5).
+
+The pages name these pieces but never print the gradient formulas, so the
+oracle writes out the textbook chain rule of the plain definition:
+
+    S   = scale * Q K^T                        (all keys, one row at a time)
+    S_ij = -inf where (i, j) is not allowed
+    lse_i = logsumexp_j S_ij                   (natural log)
+    P   = exp(S - lse)                         (exactly 0 where masked)
+    O   = P V
+    dP  = dO V^T
+    Delta_i = <dO_i, O_i>                      (= sum_j P_ij dP_ij)
+    dS  = P * (dP - Delta)
+    dQ  = scale * dS K
+    dK  = scale * dS^T Q      (summed over the q-heads of the kv group)
+    dV  = P^T dO              (summed over the q-heads of the kv group)
+
+The score matrix is materialised in full-width row blocks (``row_block`` query
+rows x every key). Softmax rows are independent, so row blocking changes no
+value; nothing else is blocked, fused or reordered.
+
+Readings where the pages are silent: lse uses the natural log; a row with no
+allowed key (impossible for Lq == Lk) gets lse = -inf, O = 0 and zero
+gradients; ``window >= Lk`` is identical to plain causal.
+
+Pins: tests/test_oracle.py checks this module against central finite
+differences, an independent float64 autograd of the plain forward, the
+library SDPA routine, pure-Python brute force on tiny inputs, a hand-derived
+worked example and exact invariants.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASKS = ("none", "causal", "causal_window")
+
+
+def allowed_block(rows: np.ndarray, Lk: int, mask: str, window: int, diag_off: int) -> np.ndarray:
+    """Boolean [len(rows), Lk]: True where query row i may attend key j.
+
+    causal:        j <= i + diag_off
+    causal_window: additionally j >= i + diag_off - window + 1
+    none:          every key
+    """
+    if mask not in MASKS:
+        raise ValueError(f"unknown mask {mask!r}")
+    j = np.arange(Lk)[None, :]
+    i = np.asarray(rows)[:, None]
+    if mask == "none":
+        return np.ones((len(rows), Lk), dtype=bool)
+    ok = j <= i + diag_off
+    if mask == "causal_window":
+        if window < 1:
+            raise ValueError("window must be >= 1")
+        ok &= j >= i + diag_off - window + 1
+    return ok
+
+
+def rows_attending(keys, Lq: int, Lk: int, mask: str, window: int) -> np.ndarray:
+    """Sorted query rows that attend at least one of ``keys`` (for sampled key gradients)."""
+    diag_off = Lk - Lq
+    keys = np.asarray(keys)
+    rows = set()
+    for j in keys:
+        if mask == "none":
+            return np.arange(Lq)
+        lo = max(0, int(j) - diag_off)
+        hi = Lq - 1 if mask == "causal" else min(Lq - 1, int(j) - diag_off + window - 1)
+        rows.update(range(lo, hi + 1))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _softmax_rows(S: np.ndarray, ok: np.ndarray):
+    """Masked row softmax in fp64: returns (P, lse). Empty rows: P = 0, lse = -inf."""
+    S = np.where(ok, S, -np.inf)
+    m = S.max(axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(under="ignore"):
+        E = np.exp(S - m_safe[:, None])        # exp(-inf) = 0 at masked entries
+    tot = E.sum(axis=1)
+    with np.errstate(divide="ignore"):
+        lse = m_safe + np.log(tot)              # log(0) = -inf for an empty row
+    nonempty = tot > 0
+    P = np.zeros_like(S)
+    P[nonempty] = np.exp(S[nonempty] - lse[nonempty, None])
+    return P, lse
+
+
+def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True):
+    """Forward (and, with ``do_h``, backward) for one q-head and a set of query rows.
+
+    q_h, do_h: [Lq, D]; k_g, v_g: [Lk, D] (fp64). Returns a dict with
+    O[rows], lse[rows], Delta[rows] and, if want_grad, dQ[rows] plus the
+    additive contributions of these rows to dK and dV ([Lk, D] each).
+    """
+    Lq, Lk = q_h.shape[0], k_g.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    ok = allowed_block(rows, Lk, mask, window, Lk - Lq)
+    qb = q_h[rows]
+    S = scale * (qb @ k_g.T)
+    P, lse = _softmax_rows(S, ok)
+    O = P @ v_g
+    out = {"O": O, "lse": lse}
+    if not want_grad:
+        return out
+    dob = do_h[rows]
+    dP = dob @ v_g.T
+    delta = np.sum(dob * O, axis=1)
+    dS = P * (dP - delta[:, None])
+    out["Delta"] = delta
+    out["dQ"] = scale * (dS @ k_g)
+    out["dK"] = scale * (dS.T @ qb)
+    out["dV"] = P.T @ dob
+    return out
+
+
+def _f64(x):
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: torch is only needed to unwrap tensors
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024):
+    """O [B,Hq,Lq,D] and lse [B,Hq,Lq] for inputs [B,H,L,D] (any float dtype, upcast to fp64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Lq, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    O = np.zeros_like(q)
+    lse = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for r0 in range(0, Lq, row_block):
+                rows = np.arange(r0, min(Lq, r0 + row_block))
+                res = head_rows(q[b, h], k[b, g], v[b, g], None, scale, mask, window, rows, want_grad=False)
+                O[b, h, rows] = res["O"]
+                lse[b, h, rows] = res["lse"]
+    return O, lse
+
+
+def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024):
+    """Forward and closed-form backward. Returns dict O, lse, Delta, dQ, dK, dV (fp64 numpy)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    O = np.zeros_like(q)
+    lse = np.zeros((B, Hq, Lq))
+    delta = np.zeros((B, Hq, Lq))
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for r0 in range(0, Lq, row_block):
+                rows = np.arange(r0, min(Lq, r0 + row_block))
+                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h], scale, mask, window, rows)
+                O[b, h, rows] = res["O"]
+                lse[b, h, rows] = res["lse"]
+                delta[b, h, rows] = res["Delta"]
+                dQ[b, h, rows] = res["dQ"]
+                dK[b, g] += res["dK"]
+                dV[b, g] += res["dV"]
+    return {"O": O, "lse": lse, "Delta": delta, "dQ": dQ, "dK": dK, "dV": dV}
+
+
+def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows):
+    """O, lse and dQ of selected query rows of head (b, h), from the full key range."""
+    q, k, v, do = (_f64(x[b]) for x in (q, k, v, do))
+    group = q.shape[0] // k.shape[0]
+    g = h // group
+    res = head_rows(q[h], k[g], v[g], do[h], scale, mask, window, rows)
+    return {"O": res["O"], "lse": res["lse"], "dQ": res["dQ"]}
+
+
+def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024):
+    """dK, dV of selected keys of kv head (b, g): every row that attends them, every q-head of the group."""
+    q, k, v, do = (_f64(x[b]) for x in (q, k, v, do))
+    Hq, Lq = q.shape[0], q.shape[1]
+    Lk = k.shape[1]
+    group = Hq // k.shape[0]
+    rows = rows_attending(keys, Lq, Lk, mask, window)
+    dK = np.zeros_like(k[g])
+    dV = np.zeros_like(v[g])
+    for h in range(g * group, (g + 1) * group):
+        for r0 in range(0, len(rows), row_block):
+            rr = rows[r0:r0 + row_block]
+            res = head_rows(q[h], k[g], v[g], do[h], scale, mask, window, rr)
+            dK += res["dK"]
+            dV += res["dV"]
+    keys = np.asarray(keys)
+    return {"dK": dK[keys], "dV": dV[keys]}

@@ -1,0 +1,187 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the
+oracle itself. Each pin takes the oracle module as an argument so the same
+checks can be run against deliberately broken copies of it (mutation tests).
+
+Pins:
+  golden       hand-derived worked example (tests/golden/worked_L2_D1.json)
+  brute        pure-Python loops over the definition (forward: O, lse)
+  fd           central finite differences of l = sum(dO * O) (dQ, dK, dV)
+  autograd     torch float64 autograd of a plain matmul/softmax forward
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _num(x):
+    if isinstance(x, str):
+        env = {"ln2": math.log(2), "ln3": math.log(3), "ln4": math.log(4)}
+        return float(eval(x, {"__builtins__": {}}, env))  # fixture-only arithmetic on ln constants
+    if isinstance(x, list):
+        return [_num(y) for y in x]
+    return float(x)
+
+
+def load_golden():
+    with open(os.path.join(GOLDEN, "worked_L2_D1.json")) as f:
+        return json.load(f)
+
+
+def pin_golden(mod, tol=1e-14):
+    """Max abs error of the oracle against the hand-derived worked example."""
+    g = load_golden()
+    inp = {k: np.array(_num(v)) for k, v in g["inputs"].items() if k in ("q", "k", "v", "do")}
+    inp = {k: v[None] for k, v in inp.items()}  # add B=1
+    worst = 0.0
+    for case, mask, window in (("causal", "causal", 0), ("window1", "causal_window", 1)):
+        res = mod.sdpa_fwd_bwd(inp["q"], inp["k"], inp["v"], inp["do"], g["inputs"]["scale"], mask, window)
+        for name in ("O", "lse", "dQ", "dK", "dV"):
+            ref = np.array(_num(g[case][name]))[None]
+            worst = max(worst, float(np.max(np.abs(res[name] - ref))))
+    return worst
+
+
+def brute_forward(q, k, v, scale, mask, window):
+    """O and lse from the definition with Python loops and math.exp (no numpy linear algebra)."""
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    O = np.zeros((B, Hq, L, D))
+    lse = np.zeros((B, Hq, L))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(L):
+                keys = [j for j in range(L) if j <= i and (mask == "causal" or j > i - window)]
+                s = [scale * sum(float(q[b, h, i, d]) * float(k[b, g, j, d]) for d in range(D)) for j in keys]
+                mx = max(s)
+                z = sum(math.exp(x - mx) for x in s)
+                lse[b, h, i] = mx + math.log(z)
+                for d in range(D):
+                    O[b, h, i, d] = sum(math.exp(x - lse[b, h, i]) * float(v[b, g, j, d]) for x, j in zip(s, keys))
+    return O, lse
+
+
+def tiny_inputs(Hq, Hkv, L, D, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, Hq, L, D))
+    k = rng.standard_normal((1, Hkv, L, D))
+    v = rng.standard_normal((1, Hkv, L, D))
+    do = rng.standard_normal((1, Hq, L, D))
+    return q, k, v, do
+
+
+def pin_brute(mod, cases=None):
+    """Max abs error of oracle O/lse against brute force over a few tiny cases."""
+    cases = cases or [
+        (2, 1, 7, 3, 0.7, "causal", 0),
+        (4, 2, 9, 4, 1.0, "causal_window", 3),
+        (2, 2, 6, 2, 3.0, "causal_window", 1),
+        (3, 1, 5, 5, 0.45, "causal_window", 2),
+    ]
+    worst = 0.0
+    for n, (Hq, Hkv, L, D, s, mask, W) in enumerate(cases):
+        q, k, v, _ = tiny_inputs(Hq, Hkv, L, D, 100 + n)
+        O, lse = mod.sdpa_forward(q, k, v, s, mask, W)
+        Ob, lb = brute_forward(q, k, v, s, mask, W)
+        worst = max(worst, float(np.max(np.abs(O - Ob))), float(np.max(np.abs(lse - lb))))
+    return worst
+
+
+def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0):
+    """max|FD - analytic| / max|analytic| over every coordinate of Q, K and V."""
+    q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed)
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
+    grads = {"q": res["dQ"], "k": res["dK"], "v": res["dV"]}
+
+    def loss(qq, kk, vv):
+        O, _ = mod.sdpa_forward(qq, kk, vv, scale, mask, window)
+        return float(np.sum(do * O))
+
+    worst = 0.0
+    scale_ref = max(float(np.max(np.abs(g))) for g in grads.values())
+    for name in ("q", "k", "v"):
+        base = {"q": q, "k": k, "v": v}
+        x = base[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            x0 = x[idx]
+            h = 1e-6 * max(1.0, abs(x0))
+            xp = x.copy()
+            xp[idx] = x0 + h
+            xm = x.copy()
+            xm[idx] = x0 - h
+            args_p = dict(base, **{name: xp})
+            args_m = dict(base, **{name: xm})
+            fd[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        worst = max(worst, float(np.max(np.abs(fd - grads[name]))))
+    return worst / scale_ref
+
+
+def fd_directional_error(mod, Hq, Hkv, L, D, scale, mask, window, ndir=16, seed=0):
+    """Directional central differences along random unit directions in (Q, K, V) jointly."""
+    q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed)
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
+    rng = np.random.default_rng(seed + 1)
+
+    def loss(qq, kk, vv):
+        O, _ = mod.sdpa_forward(qq, kk, vv, scale, mask, window)
+        return float(np.sum(do * O))
+
+    worst = 0.0
+    for _ in range(ndir):
+        u = [rng.standard_normal(x.shape) for x in (q, k, v)]
+        nrm = math.sqrt(sum(float(np.sum(x * x)) for x in u))
+        u = [x / nrm for x in u]
+        h = 1e-6
+        lp = loss(q + h * u[0], k + h * u[1], v + h * u[2])
+        lm = loss(q - h * u[0], k - h * u[1], v - h * u[2])
+        fd = (lp - lm) / (2 * h)
+        an = float(np.sum(res["dQ"] * u[0]) + np.sum(res["dK"] * u[1]) + np.sum(res["dV"] * u[2]))
+        gn = math.sqrt(sum(float(np.sum(res[n] ** 2)) for n in ("dQ", "dK", "dV")))
+        worst = max(worst, abs(fd - an) / gn)
+    return worst
+
+
+def torch_plain(q, k, v, do, scale, mask, window):
+    """float64 autograd of the plain forward: matmul -> -inf mask -> softmax -> matmul."""
+    q = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    group = q.shape[1] // k.shape[1]
+    kk = k.repeat_interleave(group, dim=1)
+    vv = v.repeat_interleave(group, dim=1)
+    L, Lk = q.shape[2], k.shape[2]
+    i = torch.arange(L)[:, None]
+    j = torch.arange(Lk)[None, :]
+    ok = j <= i + (Lk - L)
+    if mask == "causal_window":
+        ok = ok & (j > i + (Lk - L) - window)
+    S = scale * torch.matmul(q, kk.transpose(-1, -2).contiguous())
+    S = S.masked_fill(~ok, float("-inf"))
+    lse = torch.logsumexp(S, dim=-1)
+    O = torch.matmul(torch.softmax(S, dim=-1), vv)
+    O.backward(torch.tensor(do, dtype=torch.float64))
+    return {"O": O.detach().numpy(), "lse": lse.detach().numpy(), "dQ": q.grad.numpy(),
+            "dK": k.grad.numpy(), "dV": v.grad.numpy()}
+
+
+def rel_fro(x, ref):
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(np.asarray(x) - ref))
+    return num / den if den > 0 else num
+
+
+def autograd_error(mod, q, k, v, do, scale, mask, window):
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
+    ref = torch_plain(q, k, v, do, scale, mask, window)
+    return max(rel_fro(res[n], ref[n]) for n in ("O", "lse", "dQ", "dK", "dV"))
