@@ -1,0 +1,119 @@
+/*
+ * sdpa.h - C ABI of the MI355X (gfx950) memory-efficient scaled-dot-product
+ * attention library: a forward that also writes the per-row logsumexp, and a
+ * tiled backward that returns dQ, dK and dV at O(L) device memory.
+ *
+ * What the operations compute
+ * ---------------------------
+ * For query head h (kv head g = h / group), query row i and key j:
+ *   S_ij  = scale * <Q[h,i], K[g,j]>
+ *   P_ij  = exp(S_ij - lse_i) on allowed pairs, exactly 0 elsewhere
+ *   lse_i = log(sum over allowed j of exp(S_ij))   (natural log)
+ *   O[h,i] = sum_j P_ij V[g,j]
+ * and the backward is the gradient of sum(dO * O) with respect to Q, K, V,
+ * summed over the q-heads of each kv group for dK and dV.
+ *
+ * The forward "writes the logsumexp (the per-row softmax normalizer the
+ * backward reuses)" and the backward "recomputes the softmax probability P"
+ * tile by tile, skipping tiles above the causal diagonal and tiles entirely
+ * outside the window: page "Lab 028 lab detail: Off NVIDIA, you fix the
+ * platform yourself", sections "2026-10-21" ("What the code says") and
+ * "What I changed, in plain terms" (items 1, 3, 4). GQA maps q-head h to kv
+ * head h / group: page "MiniCPM5 Decode Megakernel - end-to-end build plan
+ * (handoff)", section 4, stage 5.
+ *
+ * Masks (allowed pairs; Lq == Lk == L in this version):
+ *   SDPA_MASK_CAUSAL         j <= i
+ *   SDPA_MASK_CAUSAL_WINDOW  j <= i and j > i - window   (window counts the
+ *                            diagonal: window 1 = self only; window >= L is
+ *                            identical to causal)
+ * Keys j >= L and rows i >= L do not exist.
+ *
+ * Layout and ownership
+ * --------------------
+ * Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
+ * contiguous row-major: Q, O, dO, dQ [B, Hq, L, D]; K, V, dK, dV
+ * [B, Hq/group, L, D]; lse [B, Hq, L] float32. Element type: bfloat16
+ * (SDPA_BF16) or float32 (SDPA_F32) for Q, K, V, O, dO, dQ, dK, dV; lse is
+ * always float32. Pointers must be 16-byte aligned. Outputs must not alias
+ * inputs. The library never allocates device memory: the backward's scratch
+ * space is the caller's `workspace` buffer.
+ *
+ * Execution and errors
+ * --------------------
+ * Work is enqueued on `stream` (0 = the null stream) and the call returns
+ * after the enqueue. There is no global state; calls are thread-safe. All
+ * argument checks happen before any launch: on error nothing is launched and
+ * no output is touched. A problem with B == 0 or L == 0 (or Hq == 0) is valid
+ * and launches nothing. There is no silent fallback to another algorithm:
+ * unsupported combinations return SDPA_ERR_UNSUPPORTED.
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % group != 0,
+                                window < 1 with CAUSAL_WINDOW, scale not
+                                finite or <= 0, unknown enum, misaligned ptr */
+  SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: MASK_NONE, D not in
+                                {64,128,256,512} (bf16) / {64,128} (f32) */
+  SDPA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
+  SDPA_ERR_LAUNCH = -4       /* the HIP runtime reported a launch error */
+};
+
+enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F32 = 1 };
+
+enum sdpa_mask {
+  SDPA_MASK_NONE = 0, /* reserved; returns SDPA_ERR_UNSUPPORTED */
+  SDPA_MASK_CAUSAL = 1,
+  SDPA_MASK_CAUSAL_WINDOW = 2
+};
+
+/* Forward. Reads q, k, v; writes o (input dtype, fully overwritten for every
+ * row i < L) and lse (float32, natural log, one value per query row).
+ * `window` is ignored unless mask == SDPA_MASK_CAUSAL_WINDOW. */
+int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+                 int32_t dtype, int32_t mask, int32_t window, float scale,
+                 hipStream_t stream);
+
+/* Bytes of caller-provided workspace sdpa_bwd needs for this shape: a float32
+ * dQ accumulator [B, Hq, L, D] (bf16 only) and the row terms
+ * Delta_i = <dO_i, O_i> [B, Hq, L]. Linear in L. Returns 0 for empty shapes
+ * and for invalid arguments. */
+size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t L, int32_t D, int32_t dtype);
+
+/* Backward. Reads q, k, v, o, dO and lse as written by sdpa_fwd_lse for the
+ * same arguments; writes dq [B, Hq, L, D] and dk, dv [B, Hq/group, L, D] in
+ * the input dtype, every element fully overwritten (keys no query attends get
+ * exact zeros). `workspace` is device memory of at least
+ * sdpa_bwd_workspace_bytes(...) bytes; its contents on entry do not matter
+ * and are clobbered. Calls that share a workspace must be stream-ordered. */
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+             int32_t dtype, int32_t mask, int32_t window, float scale,
+             hipStream_t stream);
+
+/* Static description of a status code. */
+const char* sdpa_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H */

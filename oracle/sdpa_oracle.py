@@ -196,26 +196,27 @@ def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024):
 
 def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows):
     """O, lse and dQ of selected query rows of head (b, h), from the full key range."""
-    q, k, v, do = (_f64(x[b]) for x in (q, k, v, do))
-    group = q.shape[0] // k.shape[0]
+    group = q.shape[1] // k.shape[1]
     g = h // group
-    res = head_rows(q[h], k[g], v[g], do[h], scale, mask, window, rows)
+    qh, kg, vg, doh = _f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g]), _f64(do[b, h])
+    res = head_rows(qh, kg, vg, doh, scale, mask, window, rows)
     return {"O": res["O"], "lse": res["lse"], "dQ": res["dQ"]}
 
 
 def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024):
     """dK, dV of selected keys of kv head (b, g): every row that attends them, every q-head of the group."""
-    q, k, v, do = (_f64(x[b]) for x in (q, k, v, do))
-    Hq, Lq = q.shape[0], q.shape[1]
-    Lk = k.shape[1]
-    group = Hq // k.shape[0]
+    Hq, Lq = q.shape[1], q.shape[2]
+    Lk = k.shape[2]
+    group = Hq // k.shape[1]
     rows = rows_attending(keys, Lq, Lk, mask, window)
-    dK = np.zeros_like(k[g])
-    dV = np.zeros_like(v[g])
+    kg, vg = _f64(k[b, g]), _f64(v[b, g])
+    dK = np.zeros_like(kg)
+    dV = np.zeros_like(vg)
     for h in range(g * group, (g + 1) * group):
+        qh, doh = _f64(q[b, h]), _f64(do[b, h])
         for r0 in range(0, len(rows), row_block):
             rr = rows[r0:r0 + row_block]
-            res = head_rows(q[h], k[g], v[g], do[h], scale, mask, window, rr)
+            res = head_rows(qh, kg, vg, doh, scale, mask, window, rr)
             dK += res["dK"]
             dV += res["dV"]
     keys = np.asarray(keys)

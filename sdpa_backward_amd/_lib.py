@@ -1,0 +1,146 @@
+"""ctypes binding of libsdpa.so: argument marshalling only.
+
+Every step of the attention forward and backward runs in the HIP library.
+This module checks tensor dtypes, shapes, devices and contiguity, allocates
+outputs and the backward workspace with torch (torch owns device memory and
+streams), and passes raw device pointers plus the current HIP stream. There is
+no CPU path: if the library is missing or a call fails, it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+SDPA_OK = 0
+STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", -3: "SDPA_ERR_WORKSPACE",
+          -4: "SDPA_ERR_LAUNCH"}
+DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+MASK = {"none": 0, "causal": 1, "causal_window": 2}
+
+EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_status_string", "sdpa_abi_version")
+
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libsdpa.so and declare its signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sdpa_backward_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    shape = [i32, i32, i32, i32, i32, i32, i32, i32, f32, p]  # B Hq group L D dtype mask window scale stream
+    lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + shape
+    lib.sdpa_fwd_lse.restype = ctypes.c_int
+    lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape
+    lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.sdpa_bwd_workspace_bytes.restype = sz
+    lib.sdpa_status_string.argtypes = [ctypes.c_int]
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_abi_version.argtypes = []
+    lib.sdpa_abi_version.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != SDPA_OK:
+        raise SdpaError(fn, status, load().sdpa_status_string(status).decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _validate(q, k, v, extra=()):
+    for name, t in (("q", q), ("k", k), ("v", v), *extra):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, L, D]")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if q.dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    B, Hq, L, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hq // Hkv, L, D
+
+
+def _mask_args(mask, window):
+    if mask not in MASK:
+        raise ValueError(f"mask must be one of {tuple(MASK)}")
+    return MASK[mask], int(window) if mask == "causal_window" else 0
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)
+
+
+def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None):
+    """O [B,Hq,L,D] (q.dtype) and lse [B,Hq,L] (float32, natural log)."""
+    B, Hq, group, L, D = _validate(q, k, v)
+    scale = default_scale(D) if scale is None else float(scale)
+    m, w = _mask_args(mask, window)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q")
+    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    st = load().sdpa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, D,
+                             DTYPE[q.dtype], m, w, scale, _stream(q.device))
+    _check("sdpa_fwd_lse", st)
+    return o, lse
+
+
+def workspace_bytes(B, Hq, L, D, dtype):
+    return int(load().sdpa_bwd_workspace_bytes(B, Hq, L, D, DTYPE[dtype]))
+
+
+def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None):
+    """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse)."""
+    B, Hq, group, L, D = _validate(q, k, v, (("o", o), ("do", do)))
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must match q")
+    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    scale = default_scale(D) if scale is None else float(scale)
+    m, w = _mask_args(mask, window)
+    need = workspace_bytes(B, Hq, L, D, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    st = load().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                         _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, group, L, D, DTYPE[q.dtype],
+                         m, w, scale, _stream(q.device))
+    _check("sdpa_bwd", st)
+    return dq, dk, dv

@@ -1,0 +1,84 @@
+"""Build libsdpa.so (gfx950) in-tree with hipcc.
+
+    python -m sdpa_backward_amd.build          # compile every source, link
+    python -m sdpa_backward_amd.build --asm    # also keep gfx950 assembly under _build/asm
+
+Every HIP source is compiled with the packed-fp32 instructions disabled
+(-Xclang -target-feature -Xclang -packed-fp32-ops): the compiler would
+otherwise form v_pk_* fp32 ops on its own. Float atomics are emitted as
+hardware atomics (-munsafe-fp-atomics), used for the fp32 dQ accumulator.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsdpa.so")
+SOURCES = ["sdpa_api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "f32_valu.hip"]
+ARCH = "gfx950"
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def common_flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-result",
+        f"-I{os.path.join(ROOT, 'include')}",
+    ]
+
+
+def _compile(src, asm):
+    odir = os.path.join(BUILD, "asm") if asm else BUILD
+    os.makedirs(odir, exist_ok=True)
+    obj = os.path.join(odir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    if asm:
+        cmd.append("-save-temps=obj")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; that is harmless
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+    return obj, msgs
+
+
+def build(asm: bool = False, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        results = list(ex.map(lambda s: _compile(s, asm), SOURCES))
+    objs = [o for o, _ in results]
+    if verbose:
+        for _, msgs in results:
+            for m in msgs:
+                print(m)
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", action="store_true")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(asm=a.asm, verbose=a.verbose))
+    sys.exit(0)

@@ -1,0 +1,192 @@
+// float32 attention forward (+lse) and backward on the vector ALUs.
+//
+// This path exists for float32 inputs, where the result must be computed in
+// true fp32 (no reduced-precision matrix mode: page "Lab 028 lab detail: Off
+// NVIDIA, you fix the platform yourself", section "Gradient parity", reports
+// fp32 gradients that are noisy only when TF32-style math is on). It targets
+// small problems: one thread per query row (forward, dQ) or per key (dK, dV),
+// two passes over the allowed keys, fp32 FMA throughout. D <= 128.
+#include <math.h>
+
+#include "common.h"
+
+namespace sdpa {
+
+template <int D>
+__global__ void __launch_bounds__(128)
+fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+               float* __restrict__ O, float* __restrict__ LSE, int Hq, int group, int L, int w_eff,
+               float scale) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (i >= L) return;
+  const int Hkv = Hq / group, g = h / group;
+  const float* q = Q + ((size_t)b * Hq + h) * L * D + (size_t)i * D;
+  const float* Kg = K + ((size_t)b * Hkv + g) * L * D;
+  const float* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  float qr[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) qr[d] = q[d];
+  const int jlo = max(0, i - w_eff + 1);
+  float m = -INFINITY;
+  for (int j = jlo; j <= i; j++) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    m = fmaxf(m, s * scale);
+  }
+  float l = 0.f;
+  for (int j = jlo; j <= i; j++) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    l += expf(s * scale - m);
+  }
+  const float lse = m + logf(l);
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) acc[d] = 0.f;
+  for (int j = jlo; j <= i; j++) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    const float p = expf(s * scale - lse);
+#pragma unroll
+    for (int d = 0; d < D; d++) acc[d] = fmaf(p, Vg[(size_t)j * D + d], acc[d]);
+  }
+  float* o = O + ((size_t)b * Hq + h) * L * D + (size_t)i * D;
+#pragma unroll
+  for (int d = 0; d < D; d++) o[d] = acc[d];
+  LSE[((size_t)b * Hq + h) * L + i] = lse;
+}
+
+// dQ rows (and Delta_i = <dO_i, O_i>, kept for the key pass)
+template <int D>
+__global__ void __launch_bounds__(128)
+bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+                  const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
+                  float* __restrict__ dQ, float* __restrict__ Delta, int Hq, int group, int L, int w_eff,
+                  float scale) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (i >= L) return;
+  const int Hkv = Hq / group, g = h / group;
+  const size_t row = ((size_t)b * Hq + h) * L + i;
+  const float* q = Q + row * D;
+  const float* o = O + row * D;
+  const float* dor = dO + row * D;
+  const float* Kg = K + ((size_t)b * Hkv + g) * L * D;
+  const float* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  float qr[D], dr[D], acc[D];
+  float delta = 0.f;
+#pragma unroll
+  for (int d = 0; d < D; d++) {
+    qr[d] = q[d];
+    dr[d] = dor[d];
+    delta = fmaf(dr[d], o[d], delta);
+    acc[d] = 0.f;
+  }
+  const float lse = LSE[row];
+  for (int j = max(0, i - w_eff + 1); j <= i; j++) {
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+      dp = fmaf(dr[d], Vg[(size_t)j * D + d], dp);
+    }
+    const float p = expf(s * scale - lse);
+    const float ds = p * (dp - delta);
+#pragma unroll
+    for (int d = 0; d < D; d++) acc[d] = fmaf(ds, Kg[(size_t)j * D + d], acc[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < D; d++) dQ[row * D + d] = acc[d] * scale;
+  Delta[row] = delta;
+}
+
+// dK, dV of one key, summed over the q-heads of its kv group
+template <int D>
+__global__ void __launch_bounds__(128)
+bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+                   const float* __restrict__ dO, const float* __restrict__ LSE,
+                   const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV, int Hq,
+                   int group, int L, int w_eff, float scale) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (j >= L) return;
+  const int Hkv = Hq / group;
+  const size_t krow = ((size_t)b * Hkv + g) * L + j;
+  float kr[D], vr[D], dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) {
+    kr[d] = K[krow * D + d];
+    vr[d] = V[krow * D + d];
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  const int ihi = min(L - 1, j + w_eff - 1);
+  for (int h = g * group; h < (g + 1) * group; h++) {
+    const size_t hrow = ((size_t)b * Hq + h) * L;
+    for (int i = j; i <= ihi; i++) {
+      const float* q = Q + (hrow + i) * D;
+      const float* dor = dO + (hrow + i) * D;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d++) {
+        s = fmaf(q[d], kr[d], s);
+        dp = fmaf(dor[d], vr[d], dp);
+      }
+      const float p = expf(s * scale - LSE[hrow + i]);
+      const float ds = p * (dp - Delta[hrow + i]);
+#pragma unroll
+      for (int d = 0; d < D; d++) {
+        dk[d] = fmaf(ds, q[d], dk[d]);
+        dv[d] = fmaf(p, dor[d], dv[d]);
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; d++) {
+    dK[krow * D + d] = dk[d] * scale;
+    dV[krow * D + d] = dv[d];
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int group, int L, int w_eff, float scale, hipStream_t stream) {
+  dim3 grid((L + 127) / 128, Hq, B);
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
+                     (const float*)v, (float*)o, lse, Hq, group, L, w_eff, scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
+                          int group, int L, int w_eff, float scale, hipStream_t stream) {
+  dim3 grid((L + 127) / 128, Hq, B);
+  hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
+                     (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
+                     L, w_eff, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid2((L + 127) / 128, Hq / group, B);
+  hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
+                     (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
+                     group, L, w_eff, scale);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd_f32<64>(const void*, const void*, const void*, void*, float*, int, int, int,
+                                       int, int, float, hipStream_t);
+template hipError_t launch_fwd_f32<128>(const void*, const void*, const void*, void*, float*, int, int, int,
+                                        int, int, float, hipStream_t);
+template hipError_t launch_bwd_f32<64>(const void*, const void*, const void*, const void*, const void*,
+                                       const float*, void*, void*, void*, float*, int, int, int, int, int,
+                                       float, hipStream_t);
+template hipError_t launch_bwd_f32<128>(const void*, const void*, const void*, const void*, const void*,
+                                        const float*, void*, void*, void*, float*, int, int, int, int, int,
+                                        float, hipStream_t);
+
+}  // namespace sdpa

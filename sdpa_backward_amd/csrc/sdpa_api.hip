@@ -1,0 +1,170 @@
+// C ABI of the attention library: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels. Nothing here allocates device memory.
+//
+// Unsupported combinations are refused with a status code rather than run on
+// another algorithm; the silent fall back to a materialised score matrix is
+// the failure the pages measure (page "Lab 028 lab detail: Off NVIDIA, you fix
+// the platform yourself", section "2026-10-21", starting point and upstream
+// state, where an unsupported window is refused with "NYI").
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/sdpa.h"
+#include "common.h"
+
+namespace sdpa {
+template <int D>
+hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
+                           float, hipStream_t);
+template <int D>
+hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const void*, const float*,
+                           void*, void*, void*, float*, float*, int, int, int, int, int, float, hipStream_t);
+template <int D>
+hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
+                          float, hipStream_t);
+template <int D>
+hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
+                          void*, void*, void*, float*, int, int, int, int, int, float, hipStream_t);
+}  // namespace sdpa
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+  int B, Hq, group, L, D, dtype, mask, window;
+  float scale;
+  bool empty() const { return B == 0 || Hq == 0 || L == 0; }
+  int w_eff() const { return mask == SDPA_MASK_CAUSAL ? L : std::min(window, L); }
+};
+
+bool d_supported(int dtype, int D) {
+  if (dtype == SDPA_BF16) return D == 64 || D == 128 || D == 256 || D == 512;
+  return D == 64 || D == 128;
+}
+
+// Shape checks shared by both entry points (pointers are checked by the caller).
+int check_shape(const Shape& s) {
+  if (s.dtype != SDPA_BF16 && s.dtype != SDPA_F32) return SDPA_ERR_INVALID_ARG;
+  if (s.mask != SDPA_MASK_NONE && s.mask != SDPA_MASK_CAUSAL && s.mask != SDPA_MASK_CAUSAL_WINDOW)
+    return SDPA_ERR_INVALID_ARG;
+  if (s.B < 0 || s.Hq < 0 || s.L < 0 || s.D <= 0 || s.group <= 0) return SDPA_ERR_INVALID_ARG;
+  if (s.Hq % s.group != 0) return SDPA_ERR_INVALID_ARG;
+  if (s.mask == SDPA_MASK_CAUSAL_WINDOW && s.window < 1) return SDPA_ERR_INVALID_ARG;
+  if (!isfinite(s.scale) || !(s.scale > 0.f)) return SDPA_ERR_INVALID_ARG;
+  if (s.mask == SDPA_MASK_NONE) return SDPA_ERR_UNSUPPORTED;
+  if (!d_supported(s.dtype, s.D)) return SDPA_ERR_UNSUPPORTED;
+  // launch-grid and index limits: heads and batch ride on grid y/z
+  if (s.Hq > 65535 || s.B > 65535) return SDPA_ERR_UNSUPPORTED;
+  if ((int64_t)s.B * s.Hq * s.L > (int64_t(1) << 40)) return SDPA_ERR_UNSUPPORTED;
+  return SDPA_OK;
+}
+
+size_t workspace_for(const Shape& s) {
+  if (s.empty()) return 0;
+  const size_t rows = (size_t)s.B * s.Hq * s.L;
+  size_t bytes = align_up(rows * sizeof(float));                        // Delta
+  if (s.dtype == SDPA_BF16) bytes += align_up(rows * s.D * sizeof(float));  // fp32 dQ accumulator
+  return bytes;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_abi_version(void) { return 100; }
+
+const char* sdpa_status_string(int status) {
+  switch (status) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_INVALID_ARG: return "invalid argument";
+    case SDPA_ERR_UNSUPPORTED: return "unsupported combination (not built; no fallback)";
+    case SDPA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDPA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t L, int32_t D, int32_t dtype) {
+  Shape s{B, Hq, 1, L, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
+  if (check_shape(s) != SDPA_OK) return 0;
+  return workspace_for(s);
+}
+
+int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                 int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                 float scale, hipStream_t stream) {
+  const Shape s{B, Hq, group, L, D, dtype, mask, window, scale};
+  int st = check_shape(s);
+  if (st != SDPA_OK) return st;
+  if (s.empty()) return SDPA_OK;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return SDPA_ERR_INVALID_ARG;
+  const int w = s.w_eff();
+  if (dtype == SDPA_BF16) {
+    switch (D) {
+      case 64: return to_status(sdpa::launch_fwd_bf16<64>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 128: return to_status(sdpa::launch_fwd_bf16<128>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 256: return to_status(sdpa::launch_fwd_bf16<256>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 512: return to_status(sdpa::launch_fwd_bf16<512>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+    }
+  } else {
+    switch (D) {
+      case 64: return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 128: return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+    }
+  }
+  return SDPA_ERR_UNSUPPORTED;
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+             int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window, float scale,
+             hipStream_t stream) {
+  const Shape s{B, Hq, group, L, D, dtype, mask, window, scale};
+  int st = check_shape(s);
+  if (st != SDPA_OK) return st;
+  if (s.empty()) return SDPA_OK;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return SDPA_ERR_INVALID_ARG;
+  const size_t need = workspace_for(s);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SDPA_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * Hq * L;
+  float* delta = static_cast<float*>(workspace);
+  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
+  const int w = s.w_eff();
+  if (dtype == SDPA_BF16) {
+    switch (D) {
+#define SDPA_BWD_CASE(DD)                                                                             \
+  case DD:                                                                                            \
+    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, B, Hq, \
+                                               group, L, w, scale, stream));
+      SDPA_BWD_CASE(64)
+      SDPA_BWD_CASE(128)
+      SDPA_BWD_CASE(256)
+      SDPA_BWD_CASE(512)
+#undef SDPA_BWD_CASE
+    }
+  } else {
+    switch (D) {
+      case 64:
+        return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
+                                                  scale, stream));
+      case 128:
+        return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
+                                                   scale, stream));
+    }
+  }
+  return SDPA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/sdpa.h declares, and every argument error is reported by status code
+before anything is launched (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sdpa_backward_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+BF16, F32 = 0, 1
+NONE, CAUSAL, WINDOW = 0, 1, 2
+FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sdpa_backward_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sdpa_abi_version() == 100
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
+        assert isinstance(lib.sdpa_status_string(code), bytes)
+    assert lib.sdpa_status_string(OK) == b"ok"
+
+
+def test_workspace_is_linear_in_L(lib):
+    ws = [lib.sdpa_bwd_workspace_bytes(1, 32, L, 256, BF16) for L in (4096, 8192, 16384, 32768)]
+    assert ws[0] > 0
+    for a, b in zip(ws, ws[1:]):
+        assert abs(b - 2 * a) <= 512   # alignment slack only
+    # fp32 dQ accumulator + Delta for bf16, Delta only for fp32
+    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, BF16) == 32 * 16384 * 256 * 4 + 32 * 16384 * 4
+    assert lib.sdpa_bwd_workspace_bytes(1, 2, 128, 64, F32) == 1024
+    assert lib.sdpa_bwd_workspace_bytes(0, 32, 16384, 256, BF16) == 0
+    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 100, BF16) == 0   # unsupported D
+    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, 7) == 0       # unknown dtype
+
+
+def fwd(lib, B=1, Hq=4, group=2, L=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
+        ptrs=(FAKE,) * 5):
+    return lib.sdpa_fwd_lse(*[ctypes.c_void_p(p) for p in ptrs], B, Hq, group, L, D, dtype, mask, window,
+                            scale, None)
+
+
+def bwd(lib, B=1, Hq=4, group=2, L=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
+        ptrs=(FAKE,) * 9, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sdpa_bwd(*[ctypes.c_void_p(p) for p in ptrs], ctypes.c_void_p(ws), ws_bytes, B, Hq, group, L,
+                        D, dtype, mask, window, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"dtype": 2}, INVALID),
+    ({"mask": 3}, INVALID),
+    ({"B": -1}, INVALID),
+    ({"L": -5}, INVALID),
+    ({"Hq": -4}, INVALID),
+    ({"D": 0}, INVALID),
+    ({"group": 0}, INVALID),
+    ({"Hq": 6, "group": 4}, INVALID),
+    ({"mask": WINDOW, "window": 0}, INVALID),
+    ({"scale": 0.0}, INVALID),
+    ({"scale": -1.0}, INVALID),
+    ({"scale": float("inf")}, INVALID),
+    ({"scale": float("nan")}, INVALID),
+    ({"mask": NONE}, UNSUPPORTED),
+    ({"D": 96}, UNSUPPORTED),
+    ({"D": 1024}, UNSUPPORTED),
+    ({"dtype": F32, "D": 256}, UNSUPPORTED),
+    ({"Hq": 70000, "group": 1}, UNSUPPORTED),
+])
+def test_argument_errors(lib, kw, expect):
+    assert fwd(lib, **kw) == expect
+    assert bwd(lib, **kw) == expect
+
+
+def test_null_and_misaligned_pointers(lib):
+    for n in range(5):
+        p = [FAKE] * 5
+        p[n] = 0
+        assert fwd(lib, ptrs=p) == INVALID
+        p[n] = FAKE + 2
+        assert fwd(lib, ptrs=p) == INVALID
+    for n in range(9):
+        p = [FAKE] * 9
+        p[n] = 0
+        assert bwd(lib, ptrs=p) == INVALID
+
+
+def test_workspace_errors(lib):
+    need = lib.sdpa_bwd_workspace_bytes(1, 4, 64, 64, BF16)
+    assert bwd(lib, ws=0) == WORKSPACE
+    assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert bwd(lib, ws=FAKE + 8) == WORKSPACE
+
+
+def test_empty_problems_launch_nothing(lib):
+    for kw in ({"B": 0}, {"L": 0}, {"Hq": 0}):
+        assert fwd(lib, ptrs=(0,) * 5, **kw) == OK
+        assert bwd(lib, ptrs=(0,) * 9, ws=0, ws_bytes=0, **kw) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.sdpa_fwd_lse(q, q[:, :1].contiguous(), q[:, :1].contiguous())
