@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward (+lse) and backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole hot path on one batch: sdpa_fwd_lse, then sdpa_bwd
+(Delta pre-pass, main backward kernel, dQ conversion), with inputs resident in
+device memory before the timed region starts. Default workload: the causal +
+sliding-window (1024) layer at L = 16384, D = 256, 32 query / 16 kv heads.
+Prints one JSON line on stdout; diagnostics go to stderr.
+
+Throughput is mask-aware useful FLOP: N = number of allowed (query, key)
+pairs over all heads; forward 4*D*N (QK^T, PV), backward 10*D*N (QK^T,
+dO V^T, dS K, dS^T Q, P^T dO). Masked edge-tile work, exp, and the side
+passes cost time but add no FLOP.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd mask-aware TFLOP/s and % of bf16 MFMA peak; peak mem GB"
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public figure (no sparsity)
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "bf16_window1024_L16384_D256_h32kv16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/bwd_bf16.hip", "sdpa_backward_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def allowed_pairs(w) -> int:
+    """Allowed (i, j) pairs over all heads: causal L(L+1)/2, window W*L - W(W-1)/2 (L >= W)."""
+    L = w.L
+    if w.mask == "causal_window" and w.window < L:
+        W = w.window
+        per_head = W * L - W * (W - 1) // 2
+    else:
+        per_head = L * (L + 1) // 2
+    return w.B * w.Hq * per_head
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same process, same streams)."""
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.hip = ctypes.CDLL(path or "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return out.value
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in MAIN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per main-kernel launch from the committed counter runs, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_sha256() or t.get("workload") != workload_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample: one q-head, blocks of 1024 query rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import head_rows
+
+    h, g = 0, 0
+    qh = inp["q"][0, h].double().numpy()
+    kg = inp["k"][0, g].double().numpy()
+    vg = inp["v"][0, g].double().numpy()
+    doh = inp["do"][0, h].double().numpy()
+    block = min(1024, w.L)
+    start = min(max(0, w.L // 2 - block), w.L - block)
+    r = start
+    pairs = 0
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = np.arange(r, min(w.L, r + block))
+        head_rows(qh, kg, vg, doh, w.scale, w.mask, w.window, rows)
+        if w.mask == "causal_window":
+            pairs += int(np.minimum(rows + 1, w.window).sum())
+        else:
+            pairs += int((rows + 1).sum())
+        n += 1
+        r += block
+        if r + block > w.L:
+            r = 0
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("internal_api") == "openblas"]
+    cores = max(threads) if threads else 1
+    return {
+        "value": 14 * w.D * pairs / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"q-head {h}: {n} blocks of {block} query rows x all {w.L} keys (full-width fp64 rows), "
+                  f"fwd+bwd, {pairs} allowed pairs, {dt:.1f} s wall; useful-FLOP rate",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one 1 GiB device copy (reference kernel for HBM counter scaling)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sdpa_backward_amd as sdpa
+    from workloads import BY_NAME, make_inputs
+
+    w = BY_NAME[a.workload]
+    dev = torch.device("cuda:0")
+    sdpa.load()
+    log(f"device: {torch.cuda.get_device_name(dev)}  torch {torch.__version__}  workload {w.name}")
+    t = time.perf_counter()
+    cpu_inp = make_inputs(w)
+    inp = {n: x.to(dev) for n, x in cpu_inp.items()}
+    torch.cuda.synchronize()
+    log(f"inputs ready ({time.perf_counter() - t:.1f} s)")
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    in_bytes = sum(x.numel() * x.element_size() for x in inp.values())
+
+    # peak device memory of one fwd+bwd, outputs and workspace allocated inside
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    o, lse = sdpa.sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale)
+    dq, dk, dv = sdpa.sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    del o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, sdpa.workspace_bytes(w.B, w.Hq, w.L, w.D, q.dtype)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = HipEvents()
+    evs = [[ev.create() for _ in range(5)] for _ in range(a.steps)]
+
+    def step(e=None):
+        if e:
+            ev.record(e[0], stream)
+        sdpa.sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale, out=o, lse=lse)
+        if e:
+            ev.record(e[1], stream)
+        sdpa.sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale, workspace=ws, out=(dq, dk, dv),
+                      main_events=(e[2], e[3]) if e else None)
+        if e:
+            ev.record(e[4], stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log(f"timed {a.steps} steps in {t1 - t0:.3f} s")
+
+    if a.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    fwd_ms = [ev.ms(e[0], e[1]) for e in evs]
+    bwd_ms = [ev.ms(e[1], e[4]) for e in evs]
+    main_ms = [ev.ms(e[2], e[3]) for e in evs]
+    ms_per_step = (t1 - t0) * 1e3 / a.steps
+    N = allowed_pairs(w)
+    fwd_flop, bwd_flop = 4 * w.D * N, 10 * w.D * N
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+    achieved = bwd_flop / (statistics.mean(main_ms) * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    med = statistics.median
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "D": w.D,
+                   "mask": w.mask, "window": w.window, "scale": w.scale, "allowed_pairs": N},
+        "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "peak_mem_gb": round(peak / 1e9, 3),
+        "peak_mem_above_inputs_gb": round((peak - in_bytes) / 1e9, 3),
+        "phases": {
+            "fwd": {"ms_median": round(med(fwd_ms), 4), "tflops": round(fwd_flop / med(fwd_ms) / 1e9, 1)},
+            "bwd": {"ms_median": round(med(bwd_ms), 4), "tflops": round(bwd_flop / med(bwd_ms) / 1e9, 1)},
+            "bwd_main_kernel": {"ms_median": round(med(main_ms), 4),
+                                "tflops": round(bwd_flop / med(main_ms) / 1e9, 1)},
+            "fwd_plus_bwd_wall": {"ms": round(ms_per_step, 4)},
+        },
+        "roofline": {
+            "kernel": f"bwd_main_kernel<{w.D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": bwd_flop,
+            "avg_launch_ms": round(statistics.mean(main_ms), 4),
+        },
+    }
+    if not a.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, cpu_inp, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -106,6 +106,19 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t dtype, int32_t mask, int32_t window, float scale,
              hipStream_t stream);
 
+/* Measurement variant of sdpa_bwd: identical arguments and results, plus two
+ * caller-created HIP events. When both are non-null, `main_begin` and
+ * `main_end` are recorded on `stream` immediately before and after the main
+ * backward kernel (the pre-pass and the dQ conversion fall outside them), so
+ * hipEventElapsedTime gives that kernel's duration. Null events: same as
+ * sdpa_bwd. The events stay owned by the caller. */
+int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+                   int32_t dtype, int32_t mask, int32_t window, float scale,
+                   hipStream_t stream, hipEvent_t main_begin, hipEvent_t main_end);
+
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 

@@ -22,7 +22,8 @@ STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", 
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 MASK = {"none": 0, "causal": 1, "causal_window": 2}
 
-EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_status_string", "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_timed", "sdpa_bwd_workspace_bytes", "sdpa_status_string",
+           "sdpa_abi_version")
 
 _lib = None
 
@@ -47,6 +48,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_fwd_lse.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape
     lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape + [p, p]
+    lib.sdpa_bwd_timed.restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
@@ -123,8 +126,12 @@ def workspace_bytes(B, Hq, L, D, dtype):
     return int(load().sdpa_bwd_workspace_bytes(B, Hq, L, D, DTYPE[dtype]))
 
 
-def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None):
-    """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse)."""
+def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None,
+             main_events=None):
+    """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse).
+
+    ``main_events``: optional pair of raw hipEvent_t handles recorded around the
+    main backward kernel (sdpa_bwd_timed)."""
     B, Hq, group, L, D = _validate(q, k, v, (("o", o), ("do", do)))
     if o.shape != q.shape or do.shape != q.shape:
         raise ValueError("o and do must match q")
@@ -139,8 +146,12 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    st = load().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                         _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, group, L, D, DTYPE[q.dtype],
-                         m, w, scale, _stream(q.device))
-    _check("sdpa_bwd", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(workspace), workspace.numel(), B, Hq, group, L, D, DTYPE[q.dtype], m, w, scale,
+            _stream(q.device))
+    if main_events is None:
+        _check("sdpa_bwd", load().sdpa_bwd(*args))
+    else:
+        ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
+        _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, ev0, ev1))
     return dq, dk, dv

@@ -281,8 +281,10 @@ bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 template <int D>
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* dq_acc, float* delta,
-                           int B, int Hq, int group, int L, int w_eff, float scale, hipStream_t stream) {
+                           int B, int Hq, int group, int L, int w_eff, float scale, hipStream_t stream,
+                           hipEvent_t main_begin, hipEvent_t main_end) {
   using C = BwdCfg<D>;
+  const bool timed = main_begin != nullptr && main_end != nullptr;
   const long rows = (long)B * Hq * L;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
@@ -294,11 +296,13 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   const int Hkv = Hq / group;
   dim3 grid((L + C::BKT - 1) / C::BKT, Hkv, B);
+  if (timed && (e = hipEventRecord(main_begin, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(256), C::LDS_BYTES, stream, (const bf16*)q, (const bf16*)k,
                      (const bf16*)v, (const bf16*)dO, lse, delta, dq_acc, (bf16*)dk, (bf16*)dv, Hq, group,
                      L, w_eff, scale, scale * kLog2e);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (timed && (e = hipEventRecord(main_end, stream)) != hipSuccess) return e;
   const long n8 = rows * D / 8;
   const long nblk = std::min<long>((n8 + 255) / 256, 256L * 64);
   hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, dq_acc, (bf16*)dq,
@@ -309,7 +313,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 #define SDPA_INST_BWD(D)                                                                              \
   template hipError_t launch_bwd_bf16<D>(const void*, const void*, const void*, const void*,         \
                                          const void*, const float*, void*, void*, void*, float*,     \
-                                         float*, int, int, int, int, int, float, hipStream_t);
+                                         float*, int, int, int, int, int, float, hipStream_t,      \
+                                         hipEvent_t, hipEvent_t);
 SDPA_INST_BWD(64)
 SDPA_INST_BWD(128)
 SDPA_INST_BWD(256)

@@ -164,18 +164,25 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
 template <int D>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                          int group, int L, int w_eff, float scale, hipStream_t stream) {
+                          int group, int L, int w_eff, float scale, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+  const bool timed = ev0 != nullptr && ev1 != nullptr;
+  hipError_t e;
+  if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   dim3 grid((L + 127) / 128, Hq, B);
   hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
                      (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
                      L, w_eff, scale);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2((L + 127) / 128, Hq / group, B);
   hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
                      (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
                      group, L, w_eff, scale);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 template hipError_t launch_fwd_f32<64>(const void*, const void*, const void*, void*, float*, int, int, int,
@@ -184,9 +191,9 @@ template hipError_t launch_fwd_f32<128>(const void*, const void*, const void*, v
                                         int, int, float, hipStream_t);
 template hipError_t launch_bwd_f32<64>(const void*, const void*, const void*, const void*, const void*,
                                        const float*, void*, void*, void*, float*, int, int, int, int, int,
-                                       float, hipStream_t);
+                                       float, hipStream_t, hipEvent_t, hipEvent_t);
 template hipError_t launch_bwd_f32<128>(const void*, const void*, const void*, const void*, const void*,
                                         const float*, void*, void*, void*, float*, int, int, int, int, int,
-                                        float, hipStream_t);
+                                        float, hipStream_t, hipEvent_t, hipEvent_t);
 
 }  // namespace sdpa

@@ -20,13 +20,15 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*,
                            float, hipStream_t);
 template <int D>
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const void*, const float*,
-                           void*, void*, void*, float*, float*, int, int, int, int, int, float, hipStream_t);
+                           void*, void*, void*, float*, float*, int, int, int, int, int, float, hipStream_t,
+                           hipEvent_t, hipEvent_t);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
                           float, hipStream_t);
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
-                          void*, void*, void*, float*, int, int, int, int, int, float, hipStream_t);
+                          void*, void*, void*, float*, int, int, int, int, int, float, hipStream_t,
+                          hipEvent_t, hipEvent_t);
 }  // namespace sdpa
 
 namespace {
@@ -125,10 +127,11 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
   return SDPA_ERR_UNSUPPORTED;
 }
 
-int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
-             int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window, float scale,
-             hipStream_t stream) {
+int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                   int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask,
+                   int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
+                   hipEvent_t main_end) {
   const Shape s{B, Hq, group, L, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -147,7 +150,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
 #define SDPA_BWD_CASE(DD)                                                                             \
   case DD:                                                                                            \
     return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, B, Hq, \
-                                               group, L, w, scale, stream));
+                                               group, L, w, scale, stream, main_begin, main_end));
       SDPA_BWD_CASE(64)
       SDPA_BWD_CASE(128)
       SDPA_BWD_CASE(256)
@@ -158,13 +161,21 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
     switch (D) {
       case 64:
         return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
-                                                  scale, stream));
+                                                  scale, stream, main_begin, main_end));
       case 128:
         return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
-                                                   scale, stream));
+                                                   scale, stream, main_begin, main_end));
     }
   }
   return SDPA_ERR_UNSUPPORTED;
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+             int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window, float scale,
+             hipStream_t stream) {
+  return sdpa_bwd_timed(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, L, D, dtype,
+                        mask, window, scale, stream, nullptr, nullptr);
 }
 
 }  // extern "C"
