@@ -87,10 +87,10 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t dtype, int32_t mask, int32_t window, float scale,
                  hipStream_t stream);
 
-/* Bytes of caller-provided workspace sdpa_bwd needs for this shape: a float32
- * dQ accumulator [B, Hq, L, D] (bf16 only) and the row terms
- * Delta_i = <dO_i, O_i> [B, Hq, L]. Linear in L. Returns 0 for empty shapes
- * and for invalid arguments. */
+/* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
+ * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, L]), rounded
+ * up to 256 bytes. Linear in L. Returns 0 for empty shapes and for invalid
+ * arguments. */
 size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t L, int32_t D, int32_t dtype);
 
 /* Backward. Reads q, k, v, o, dO and lse as written by sdpa_fwd_lse for the
@@ -109,7 +109,8 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
 /* Measurement variant of sdpa_bwd: identical arguments and results, plus two
  * caller-created HIP events. When both are non-null, `main_begin` and
  * `main_end` are recorded on `stream` immediately before and after the main
- * backward kernel (the pre-pass and the dQ conversion fall outside them), so
+ * backward kernel, the key-stationary dK/dV pass (bf16; the dQ pass runs
+ * before it, outside the events; for float32 they bracket both passes), so
  * hipEventElapsedTime gives that kernel's duration. Null events: same as
  * sdpa_bwd. The events stay owned by the caller. */
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -18,6 +18,19 @@
 // by lane 4*s + j/4 of the same group. If lane i addresses row r0 + i/4,
 // column c0 + 4*(i%4) of a row-major tile, lane j receives column c0 + j,
 // rows r0..r0+3: a 4x16 block arrives transposed.
+//
+// LDS tiles are row-major bf16 [rows][D] with no padding; the 16-byte chunk c
+// of row r sits at chunk slot c ^ swz(r). swz maps 16 consecutive rows to 16
+// distinct slots (conflict-free 16-byte reads of one column chunk across rows)
+// and 4 consecutive rows to 4 distinct chunk pairs (transposed reads).
+//
+// Tiles arrive by global_load_lds_dwordx4 (checked on the hardware: the 16
+// bytes a lane fetches land at LDS base + 16 * lane, one 1 KB block per wave
+// instruction), so loads of the next tile run while the current one is used.
+// The two buffers of a double-buffered tile are distinct __shared__ objects
+// and the loop body is instantiated once per buffer parity: the compiler can
+// then prove the prefetch target never aliases the tile being read and does
+// not insert a wait on the prefetch before every LDS read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,29 +69,8 @@ SDPA_DEV bf16x8 zero_bf16x8() {
   return z;
 }
 
-// 4 consecutive bf16 of one row-major LDS tile, delivered transposed across
-// each 16-lane group (see header comment).
-SDPA_DEV bf16x4 lds_tr4(const bf16* p) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-// Operand from a row-major LDS tile T[k][mn] (rows are the contraction index):
-// lane l gets column mn0 + l%32 with "paired" k-slots over rows [k0, k0+16).
-SDPA_DEV bf16x8 ld_op_tr(const bf16* T, int ld, int k0, int mn0, int lane) {
-  const int G = lane >> 4, i = lane & 15;
-  const int row = k0 + 4 * (G >> 1) + (i >> 2);
-  const int col = mn0 + 16 * (G & 1) + 4 * (i & 3);
-  bf16x4 lo = lds_tr4(T + row * ld + col);
-  bf16x4 hi = lds_tr4(T + (row + 8) * ld + col);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Operand from a row-major LDS tile T[mn][k] (columns are the contraction
-// index): lane l gets row mn0 + l%32 with "direct" k-slots k0 + 8*(l/32) + j.
-SDPA_DEV bf16x8 ld_op(const bf16* T, int ld, int k0, int mn0, int lane) {
-  return *(const bf16x8*)(T + (mn0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
-}
+// Row of the C tile held in accumulator slot i by a lane in half h.
+SDPA_DEV int c_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
 // fp32 C-tile values [8*op, 8*op+8) as a bf16 "paired" operand (rows of the
 // C tile become k: op 0 covers C rows 0..15, op 1 rows 16..31).
@@ -89,28 +81,99 @@ SDPA_DEV bf16x8 c_to_op(const f32x16& c, int op) {
   return r;
 }
 
-// Row of the C tile held in accumulator slot i by a lane in half h.
-SDPA_DEV int c_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+// Allowed (query i, key j) pair: causal diagonal and window (w_eff = min(window, L),
+// or L for plain causal); rows i >= L do not exist (j <= i < L then implies j < L).
+SDPA_DEV bool allowed(int i, int j, int w_eff, int L) { return j <= i && j > i - w_eff && i < L; }
 
-// Allowed (query i, key j) pair: causal diagonal, window (w_eff = min(window, L)
-// or L for plain causal), both indices inside the sequence.
-SDPA_DEV bool allowed(int i, int j, int w_eff, int L) {
-  return j <= i && j > i - w_eff && i < L;  // j <= i < L implies j < L
+// ---------------------------------------------------------------- swizzled tiles
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int MASK = CPR >= 16 ? 15 : CPR - 1;
+  SDPA_DEV static int swz(int r) {
+    const int x = r & 15;
+    return (((x & 3) << 1) | ((x >> 2) & 1) | ((x >> 3) << 3)) & MASK;
+  }
+  // element offset of (row r, column k)
+  SDPA_DEV static int off(int r, int k) { return r * D + ((((k >> 3) ^ swz(r))) << 3) + (k & 7); }
+};
+
+// 4 consecutive bf16 of a row-major LDS tile, delivered transposed across
+// each 16-lane group (see header comment).
+SDPA_DEV bf16x4 lds_tr4(const bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
 }
 
-// Copy a [rows x D] bf16 tile from global (row-major, stride D) into LDS with
-// row stride ld, zero-filling rows >= valid_rows. 16-byte chunks, block-strided.
-template <int D, int NTHREADS>
-SDPA_DEV void load_tile(bf16* dst, int ld, const bf16* __restrict__ src, int rows, int valid_rows,
-                        int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  const int total = rows * CPR;
-  for (int c = tid; c < total; c += NTHREADS) {
-    const int r = c / CPR, k = (c % CPR) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < valid_rows) v = *(const uint4*)(src + (size_t)r * D + k);
-    *(uint4*)(dst + r * ld + k) = v;
+// Operand from a swizzled tile T[k][mn] (rows are the contraction index):
+// lane l gets column mn0 + l%32 with "paired" k-slots over rows [k0, k0+16).
+template <int D>
+SDPA_DEV bf16x8 op_tr(const bf16* T, int k0, int mn0, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int row = k0 + 4 * (G >> 1) + (i >> 2);
+  const int col = mn0 + 16 * (G & 1) + 4 * (i & 3);
+  bf16x4 lo = lds_tr4(T + Tile<D>::off(row, col));
+  bf16x4 hi = lds_tr4(T + Tile<D>::off(row + 8, col));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Operand from a swizzled tile T[mn][k] (columns are the contraction index):
+// lane l gets row mn0 + l%32 with "direct" k-slots k0 + 8*(l/32) + j.
+template <int D>
+SDPA_DEV bf16x8 op_direct(const bf16* T, int k0, int mn0, int lane) {
+  return *(const bf16x8*)(T + Tile<D>::off(mn0 + (lane & 31), k0 + 8 * (lane >> 5)));
+}
+
+// Issue asynchronous global->LDS loads of rows [0, R) of a [R][D] tile whose
+// global rows start at src (row stride D). Rows >= valid re-read row valid-1:
+// finite data that the masks zero out downstream. valid >= 1.
+template <int D, int R, int NW>
+SDPA_DEV void issue_tile(bf16* lds, const bf16* __restrict__ src, int valid, int w, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int PER = R * CPR / 64;  // wave instructions (1 KB each) per tile
+  static_assert((R * CPR) % 64 == 0, "tile must be a whole number of 1 KB blocks");
+#pragma unroll
+  for (int jj = 0; jj < (PER + NW - 1) / NW; jj++) {
+    const int j = jj * NW + w;
+    if (PER % NW != 0 && j >= PER) break;
+    const int p = j * 64 + lane;
+    const int r = p / CPR;
+    const int c = (p % CPR) ^ Tile<D>::swz(r);
+    const int rr = r < valid ? r : valid - 1;
+    const bf16* g = src + (size_t)rr * D + c * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)(lds + j * 512), 16, 0, 0);
   }
+}
+
+// Wait for this wave's outstanding vector-memory loads and LDS operations,
+// then a workgroup barrier with no cache fence: LDS tiles written by every
+// wave are complete and every wave is done reading the previous buffer.
+SDPA_DEV void wait_all_and_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Barrier for LDS-only hand-offs (no outstanding global loads are waited for).
+SDPA_DEV void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Map dispatch order to a logical tile order in which each XCD receives a
+// contiguous range, so neighbouring tiles (which share K/V or Q/dO bands)
+// run on the same XCD. Bijection on [0, n).
+SDPA_DEV int xcd_remap(int pid, int n) {
+  constexpr int NX = 8;
+  const int per = (n + NX - 1) / NX;
+  const int tall = n % NX == 0 ? NX : n % NX;  // XCDs that get `per` tiles; the rest get per - 1
+  const int x = pid % NX, local = pid / NX;
+  return x < tall ? x * per + local : tall * per + (x - tall) * (per - 1) + local;
 }
 
 }  // namespace sdpa

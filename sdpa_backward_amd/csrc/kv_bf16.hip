@@ -1,0 +1,247 @@
+// Key-stationary dK/dV kernel for gfx950 (bf16 in, fp32 accumulate).
+//
+// One workgroup = 4 waves = one (b, kv head g) and a block of BKT keys. It
+// walks every query tile of every q-head of the GQA group whose rows can see
+// one of its keys (tiles above the diagonal or entirely past the window are
+// never visited), so dK and dV of the group are summed in registers without
+// atomics, and every key gets its dK/dV written, attended or not (page "Lab
+// 028 lab detail: Off NVIDIA, you fix the platform yourself", section "What I
+// changed, in plain terms", items 3-5). P is recomputed from S and the stored
+// lse and dS is formed per element (section "2026-10-21", "What the code
+// says"); S and dP stay in fp32 registers, only P and dS are rounded to bf16
+// as MFMA operands (section "fp32 score tiles").
+//
+// Per query tile of 32 rows, per wave (owning 32 keys; for D = 512 two waves
+// share a key block and split the head dimension, adding their partial S and
+// dP tiles through LDS):
+//   S  (32q x 32k) = Q_tile . K_w^T   A: Q (LDS, direct)   B: K_w (LDS, direct)
+//   dP (32q x 32k) = dO_tile . V_w^T  A: dO (LDS, direct)  B: V_w (registers)
+//   P = exp2(S c - lse2), dS = P * (dP - Delta)      (Delta from the dQ pass)
+//   dV_w += P^T . dO                  A: P^T (C tile reused)  B: dO (LDS, transposed reads)
+//   dK_w += dS^T . Q                  A: dS^T (C tile)        B: Q  (LDS, transposed reads)
+// Q/dO tiles stream into LDS with asynchronous global->LDS loads, double
+// buffered when they fit (D <= 256).
+#include "common.h"
+
+namespace sdpa {
+
+template <int D>
+struct KvCfg {
+  static constexpr int NW = 4;
+  static constexpr int DS = D > 256 ? 2 : 1;   // waves sharing one key block (head-dim split)
+  static constexpr int NWK = NW / DS;          // key blocks per workgroup
+  static constexpr int BKT = 32 * NWK;         // keys per workgroup
+  static constexpr int DW = D / DS;            // head-dim slice of one wave
+  static constexpr int BQ = 32;                // query rows per step
+  static constexpr int NBUF = D > 256 ? 1 : 2; // Q/dO buffers
+};
+
+// Add the partner wave's partial C tile (head-dim split): both waves of the
+// pair end with identical sums. One 16 KB buffer, so S and dP go one at a time.
+SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) xbuf[(w * 16 + i) * 64 + lane] = c[i];
+  lds_barrier();
+  const int p = w ^ 1;
+#pragma unroll
+  for (int i = 0; i < 16; i++) c[i] += xbuf[(p * 16 + i) * 64 + lane];
+  lds_barrier();
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1)
+kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+          const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+          bf16* __restrict__ dK, bf16* __restrict__ dV, int Hq, int group, int L, int w_eff, float scale,
+          float scale_log2) {
+  using C = KvCfg<D>;
+  constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
+  __shared__ __attribute__((aligned(16))) bf16 ks[C::BKT * D];
+  __shared__ __attribute__((aligned(16))) bf16 qb0[QT];
+  __shared__ __attribute__((aligned(16))) bf16 db0[QT];
+  __shared__ __attribute__((aligned(16))) bf16 qb1[C::NBUF == 2 ? QT : 8];
+  __shared__ __attribute__((aligned(16))) bf16 db1[C::NBUF == 2 ? QT : 8];
+  __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * 1024 : 4];
+  __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
+  __shared__ __attribute__((aligned(16))) float rv1[C::NBUF == 2 ? 64 : 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lane_id = lane;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
+  const int Hkv = Hq / group;
+  const int nkt = (L + C::BKT - 1) / C::BKT;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
+  const int k0 = kt * C::BKT;
+  const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
+  const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
+  const bf16* Kg = K + ((size_t)b * Hkv + g) * L * D;
+  const bf16* Vg = V + ((size_t)b * Hkv + g) * L * D;
+
+  issue_tile<D, C::BKT, C::NW>(ks, Kg + (size_t)k0 * D, L - k0, w, lane);
+  // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
+  bf16x8 vreg[NKS];
+  const bf16* vrow = Vg + (size_t)(kj < L ? kj : 0) * D;
+#pragma unroll
+  for (int s = 0; s < NKS; s++) vreg[s] = kj < L ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; d++) {
+    dkacc[d] = zero16();
+    dvacc[d] = zero16();
+  }
+
+  // query tiles that can see a key of this workgroup, for each q-head of the group
+  const int klast = min(k0 + C::BKT - 1, L - 1);
+  const int qt_lo = k0 / C::BQ;
+  const int qt_hi = min(L - 1, klast + w_eff - 1) / C::BQ;
+  const int nq = qt_hi - qt_lo + 1;
+  const int total = group * nq;
+
+  auto tile_src = [&](int it, const bf16*& qs, const bf16*& ds, int& q0) {
+    const int hq = g * group + it / nq;
+    q0 = (qt_lo + it % nq) * C::BQ;
+    const size_t off = (((size_t)b * Hq + hq) * L + q0) * D;
+    qs = Q + off;
+    ds = dO + off;
+  };
+  auto issue = [&](int it, bf16* qd, bf16* dd, float* rv) {
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const bf16 *qs, *ds;
+    int q0;
+    tile_src(it, qs, ds, q0);
+    issue_tile<D, C::BQ, C::NW>(qd, qs, L - q0, w, lane);
+    issue_tile<D, C::BQ, C::NW>(dd, ds, L - q0, w, lane);
+    if (w == 0) {  // lanes 0..31: lse of rows q0.., lanes 32..63: Delta of rows q0.. (clamped to L-1)
+      const int hq = g * group + it / nq;
+      const int row = min(q0 + (lane & 31), L - 1);
+      const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * L + row;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
+    }
+  };
+
+  auto compute = [&](int it, const bf16* Qc, const bf16* dOc, const float* rv) {
+    // Operand addresses depend only on the lane; recomputing them each step
+    // (a few VALU ops) is cheaper than keeping dozens of them live in VGPRs.
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
+    const int q0 = (qt_lo + it % nq) * C::BQ;
+    const int r1 = min(q0 + 31, L - 1);
+    const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
+    const bool full = kb0 + 31 <= q0 && kb0 > q0 + 31 - w_eff && q0 + 31 < L;
+
+    f32x16 s_acc = zero16(), dp_acc = zero16();
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < NKS; s++) {
+        const int d0 = dw0 + 16 * s;
+        s_acc = mfma(op_direct<D>(Qc, d0, 0, lane), op_direct<D>(ks, d0, 32 * kwi, lane), s_acc);
+        dp_acc = mfma(op_direct<D>(dOc, d0, 0, lane), vreg[s], dp_acc);
+      }
+      // schedule: three 16-byte LDS reads, then the two MFMAs they feed (reads run one step ahead)
+#pragma unroll
+      for (int s = 0; s < NKS; s++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    }
+    if constexpr (C::DS == 2) {
+      kv_exchange_add(s_acc, xbuf, w, lane);
+      kv_exchange_add(dp_acc, xbuf, w, lane);
+    }
+    if (!active) return;
+#pragma unroll
+    for (int blk = 0; blk < 4; blk++) {
+      const float4 l4 = *(const float4*)(rv + 8 * blk + 4 * hh);
+      const float4 d4 = *(const float4*)(rv + 32 + 8 * blk + 4 * hh);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int i = 4 * blk + r;
+        const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
+        float p = __builtin_amdgcn_exp2f(s_acc[i] * scale_log2 - lv);
+        if (!full && !allowed(q0 + c_row(i, hh), kj, w_eff, L)) p = 0.f;
+        s_acc[i] = p;
+        dp_acc[i] = p * (dp_acc[i] - dv);
+      }
+    }
+    const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
+    const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
+#pragma unroll
+    for (int d = 0; d < NDB; d++) {
+      const int c0 = dw0 + 32 * d;
+      dvacc[d] = mfma(pa0, op_tr<D>(dOc, 0, c0, lane), dvacc[d]);
+      dvacc[d] = mfma(pa1, op_tr<D>(dOc, 16, c0, lane), dvacc[d]);
+      dkacc[d] = mfma(da0, op_tr<D>(Qc, 0, c0, lane), dkacc[d]);
+      dkacc[d] = mfma(da1, op_tr<D>(Qc, 16, c0, lane), dkacc[d]);
+    }
+    // schedule: two transposed 8-byte reads (one operand), then one MFMA
+#pragma unroll
+    for (int d = 0; d < 4 * NDB; d++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+  };
+
+  if constexpr (C::NBUF == 2) {
+    issue(0, qb0, db0, rv0);
+    wait_all_and_barrier();
+    for (int it = 0; it < total; it += 2) {
+      if (it + 1 < total) issue(it + 1, qb1, db1, rv1);
+      compute(it, qb0, db0, rv0);
+      wait_all_and_barrier();
+      if (it + 1 >= total) break;
+      if (it + 2 < total) issue(it + 2, qb0, db0, rv0);
+      compute(it + 1, qb1, db1, rv1);
+      wait_all_and_barrier();
+    }
+  } else {
+    for (int it = 0; it < total; it++) {
+      issue(it, qb0, db0, rv0);
+      wait_all_and_barrier();
+      compute(it, qb0, db0, rv0);
+      wait_all_and_barrier();
+    }
+  }
+
+  // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
+  bf16* dKg = dK + ((size_t)b * Hkv + g) * L * D;
+  bf16* dVg = dV + ((size_t)b * Hkv + g) * L * D;
+#pragma unroll
+  for (int d = 0; d < NDB; d++) {
+    const int col = dw0 + 32 * d + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int key = kb0 + c_row(i, hh);
+      if (key < L) {
+        dKg[(size_t)key * D + col] = (bf16)(dkacc[d][i] * scale);
+        dVg[(size_t)key * D + col] = (bf16)dvacc[d][i];
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int L, int w_eff,
+                     float scale, hipStream_t stream) {
+  using C = KvCfg<D>;
+  const long nwg = (long)((L + C::BKT - 1) / C::BKT) * (Hq / group) * B;
+  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_kernel<D>, dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+                     (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq, group, L, w_eff,
+                     scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+#define SDPA_INST_KV(D)                                                                                  \
+  template hipError_t launch_kv<D>(const void*, const void*, const void*, const void*, const float*,    \
+                                   const float*, void*, void*, int, int, int, int, int, float, hipStream_t);
+SDPA_INST_KV(64)
+SDPA_INST_KV(128)
+SDPA_INST_KV(256)
+SDPA_INST_KV(512)
+
+}  // namespace sdpa

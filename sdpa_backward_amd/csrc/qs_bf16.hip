@@ -1,0 +1,286 @@
+// Query-stationary attention kernels for gfx950 (bf16 in, fp32 accumulate):
+//
+//   QS_FWD  forward: O and the per-row logsumexp (lse) that the backward reuses
+//           (page "Lab 028 lab detail: Off NVIDIA, you fix the platform
+//           yourself", section "What I changed, in plain terms", item 1)
+//   QS_DQ   backward for dQ: recompute P = exp(S - lse) per key tile, form
+//           dS = P * (dP - Delta) per element (same page, section "2026-10-21",
+//           "What the code says") and accumulate dQ = scale * dS K; also
+//           computes Delta_i = <dO_i, O_i> for its rows and stores it for the
+//           key-stationary dK/dV kernel.
+//
+// One workgroup = 4 waves = BQ query rows of one (b, h). Each wave owns 32 rows
+// (for D = 512 two waves share 32 rows and split the head dimension, adding
+// their partial score tiles through LDS). The loop walks key tiles of BK keys
+// in the causal/window band only (tiles above the diagonal or entirely behind
+// the window are never visited; a wave skips tiles outside its own rows' band,
+// and applies the element mask only on edge tiles). K and V tiles stream into
+// double-buffered LDS with asynchronous global->LDS loads.
+//
+// Per key tile, per wave (C tiles are 32x32 fp32, one query per lane column):
+//   S^T  = K_tile . Q_w^T                  A: K (LDS, direct)  B: Q_w (registers)
+//   FWD: online softmax in the log2 domain, fp32 state; the running max is only
+//        raised when a tile exceeds it by more than 8 (2^8 headroom), so the
+//        O rescale runs rarely; P^T feeds  O^T += V^T . P^T  (A: V, transposed reads)
+//   DQ:  dP^T = V_tile . dO_w^T             A: V (LDS, direct)  B: dO_w (registers)
+//        P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - Delta)
+//        dQ^T += K^T . dS^T                 A: K (transposed reads) B: dS^T (C tile reused)
+// S, P, dP stay fp32; only P and dS are rounded to bf16 as MFMA operands
+// (section "fp32 score tiles" of the Lab 028 page).
+#include "common.h"
+
+namespace sdpa {
+
+enum { QS_FWD = 0, QS_DQ = 1 };
+
+template <int D>
+struct QsCfg {
+  static constexpr int NW = 4;
+  static constexpr int DS = D > 256 ? 2 : 1;    // waves sharing one 32-row block (head-dim split)
+  static constexpr int NQW = NW / DS;           // 32-row blocks per workgroup
+  static constexpr int BQ = 32 * NQW;           // query rows per workgroup
+  static constexpr int DW = D / DS;             // head-dim slice of one wave
+  static constexpr int BK = D > 256 ? 32 : 64;  // keys per tile
+  static constexpr int NMB = BK / 32;           // 32-key blocks per tile
+  static constexpr int TILE = BK * D;           // elements of one K (or V) tile
+};
+
+// Partial C tiles of the two waves that split the head dimension: each adds
+// the partner's tiles (same lane layout), so both end with identical sums.
+template <int N>
+SDPA_DEV void exchange_add(f32x16 (&c)[N], float* xbuf, int w, int lane) {
+#pragma unroll
+  for (int t = 0; t < N; t++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) xbuf[((w * N + t) * 16 + i) * 64 + lane] = c[t][i];
+  lds_barrier();
+  const int p = w ^ 1;
+#pragma unroll
+  for (int t = 0; t < N; t++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) c[t][i] += xbuf[((p * N + t) * 16 + i) * 64 + lane];
+}
+
+template <int D, int MODE>
+__global__ void __launch_bounds__(256, 1)
+qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+          const bf16* __restrict__ O, const bf16* __restrict__ dO, float* __restrict__ LSE,
+          float* __restrict__ Delta, bf16* __restrict__ Out, int Hq, int group, int L, int w_eff,
+          float scale, float scale_log2) {
+  using C = QsCfg<D>;
+  constexpr int BK = C::BK, NMB = C::NMB, DW = C::DW, NKS = DW / 16, NDB = DW / 32;
+  constexpr int NX = MODE == QS_DQ ? 2 * NMB : NMB;  // C tiles exchanged when the head dim is split
+  __shared__ __attribute__((aligned(16))) bf16 kb0[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 kb1[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 vb0[C::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 vb1[C::TILE];
+  __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * NX * 1024 : 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
+  const int nqt = (L + C::BQ - 1) / C::BQ;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - logical % nqt;  // longest causal rows first within a head
+  const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
+  const int Hkv = Hq / group, g = h / group;
+  const size_t hrow = (size_t)b * Hq + h;
+  const bf16* Kg = K + ((size_t)b * Hkv + g) * L * D;
+  const bf16* Vg = V + ((size_t)b * Hkv + g) * L * D;
+
+  const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
+  const int qi = iw0 + (lane & 31);  // this lane's query row
+  const bool qok = qi < L;
+
+  // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
+  bf16x8 qreg[NKS];
+  const bf16* qrow = Q + (hrow * L + (qok ? qi : 0)) * D;
+#pragma unroll
+  for (int s = 0; s < NKS; s++) qreg[s] = qok ? *(const bf16x8*)(qrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+
+  bf16x8 dreg[MODE == QS_DQ ? NKS : 1];
+  float lse2 = 0.f, dlt = 0.f;
+  if constexpr (MODE == QS_DQ) {
+    const bf16* drow = dO + (hrow * L + (qok ? qi : 0)) * D;
+    const bf16* orow = O + (hrow * L + (qok ? qi : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NKS; s++) dreg[s] = qok ? *(const bf16x8*)(drow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+    // Delta_i = <dO_i, O_i> over the whole head dimension, fp32
+    float dot = 0.f;
+    if (qok) {
+#pragma unroll 4
+      for (int s = 0; s < D / 16; s++) {
+        const bf16x8 a = *(const bf16x8*)(drow + 16 * s + 8 * hh);
+        const bf16x8 o = *(const bf16x8*)(orow + 16 * s + 8 * hh);
+#pragma unroll
+        for (int j = 0; j < 8; j++) dot += (float)a[j] * (float)o[j];
+      }
+    }
+    dlt = dot + __shfl_xor(dot, 32);
+    lse2 = qok ? LSE[hrow * L + qi] * kLog2e : 0.f;
+    if (qok && dsi == 0 && hh == 0) Delta[hrow * L + qi] = dlt;
+  }
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; d++) acc[d] = zero16();
+  float m = -INFINITY, lsum = 0.f;  // forward: running (used) max in log2 units and row sum
+
+  const int i1 = min(i0 + C::BQ - 1, L - 1);
+  const int kt_lo = max(0, i0 - w_eff + 1) / BK, kt_hi = i1 / BK;
+  const int wr0 = iw0, wr1 = min(iw0 + 31, L - 1);  // this wave's rows (wr1 < wr0: none)
+
+  auto step = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
+    if (kt + 1 <= kt_hi) {  // prefetch the next tile into the other buffers
+      const int jn = (kt + 1) * BK;
+      issue_tile<D, BK, C::NW>(Kn, Kg + (size_t)jn * D, L - jn, w, lane);
+      issue_tile<D, BK, C::NW>(Vn, Vg + (size_t)jn * D, L - jn, w, lane);
+    }
+    const int j0 = kt * BK;
+    const bool active = wr0 <= wr1 && j0 <= wr1 && j0 + BK - 1 > wr0 - w_eff;
+    const bool full = j0 + BK - 1 <= wr0 && j0 > wr1 - w_eff && wr1 == wr0 + 31;
+
+    f32x16 st[NX];  // [0, NMB): S^T blocks; [NMB, 2 NMB): dP^T blocks (DQ)
+#pragma unroll
+    for (int t = 0; t < NX; t++) st[t] = zero16();
+    if (active) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; mb++)
+#pragma unroll
+        for (int s = 0; s < NKS; s++) {
+          st[mb] = mfma(op_direct<D>(Kc, dw0 + 16 * s, 32 * mb, lane), qreg[s], st[mb]);
+          if constexpr (MODE == QS_DQ)
+            st[NMB + mb] = mfma(op_direct<D>(Vc, dw0 + 16 * s, 32 * mb, lane), dreg[s], st[NMB + mb]);
+        }
+    }
+    if constexpr (C::DS == 2) exchange_add<NX>(st, xbuf, w, lane);
+    if (!active) return;
+
+    if constexpr (MODE == QS_FWD) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < NMB; mb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          float x = st[mb][i] * scale_log2;
+          if (!full && !allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L)) x = -INFINITY;
+          st[mb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m + 8.f;  // raise the used max only beyond 2^8 headroom
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+        if (need) m = mx;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; d++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) acc[d][i] *= alpha;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float rs = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < NMB; mb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const float p = __builtin_amdgcn_exp2f(st[mb][i] - m_use);
+          st[mb][i] = p;
+          rs += p;
+        }
+      lsum += rs + __shfl_xor(rs, 32);
+#pragma unroll
+      for (int mb = 0; mb < NMB; mb++) {
+        const bf16x8 p0 = c_to_op(st[mb], 0), p1 = c_to_op(st[mb], 1);
+#pragma unroll
+        for (int d = 0; d < NDB; d++) {
+          acc[d] = mfma(op_tr<D>(Vc, 32 * mb, dw0 + 32 * d, lane), p0, acc[d]);
+          acc[d] = mfma(op_tr<D>(Vc, 32 * mb + 16, dw0 + 32 * d, lane), p1, acc[d]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < NMB; mb++) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          float p = __builtin_amdgcn_exp2f(st[mb][i] * scale_log2 - lse2);
+          if (!full && !allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L)) p = 0.f;
+          st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
+        }
+        const bf16x8 d0 = c_to_op(st[NMB + mb], 0), d1 = c_to_op(st[NMB + mb], 1);
+#pragma unroll
+        for (int d = 0; d < NDB; d++) {
+          acc[d] = mfma(op_tr<D>(Kc, 32 * mb, dw0 + 32 * d, lane), d0, acc[d]);
+          acc[d] = mfma(op_tr<D>(Kc, 32 * mb + 16, dw0 + 32 * d, lane), d1, acc[d]);
+        }
+      }
+    }
+  };
+
+  {  // first tile
+    const int j0 = kt_lo * BK;
+    issue_tile<D, BK, C::NW>(kb0, Kg + (size_t)j0 * D, L - j0, w, lane);
+    issue_tile<D, BK, C::NW>(vb0, Vg + (size_t)j0 * D, L - j0, w, lane);
+    wait_all_and_barrier();
+  }
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    step(kt, kb0, vb0, kb1, vb1);
+    wait_all_and_barrier();
+    if (kt + 1 > kt_hi) break;
+    step(kt + 1, kb1, vb1, kb0, vb0);
+    wait_all_and_barrier();
+  }
+
+  if (!qok) return;
+  bf16* orow = Out + (hrow * L + qi) * D;
+  if constexpr (MODE == QS_FWD) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int d = 0; d < NDB; d++)
+#pragma unroll
+      for (int blk = 0; blk < 4; blk++) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; r++) v[r] = (bf16)(acc[d][4 * blk + r] * inv);
+        *(bf16x4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+      }
+    if (dsi == 0 && hh == 0) LSE[hrow * L + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int d = 0; d < NDB; d++)
+#pragma unroll
+      for (int blk = 0; blk < 4; blk++) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; r++) v[r] = (bf16)(acc[d][4 * blk + r] * scale);
+        *(bf16x4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+      }
+  }
+}
+
+template <int D, int MODE>
+hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
+                     float* delta, void* out, int B, int Hq, int group, int L, int w_eff, float scale,
+                     hipStream_t stream) {
+  using C = QsCfg<D>;
+  const long nwg = (long)((L + C::BQ - 1) / C::BQ) * Hq * B;
+  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qs_kernel<D, MODE>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, (const bf16*)o, (const bf16*)dO, lse, delta, (bf16*)out,
+                     Hq, group, L, w_eff, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+#define SDPA_INST_QS(D)                                                                                 \
+  template hipError_t launch_qs<D, QS_FWD>(const void*, const void*, const void*, const void*,          \
+                                           const void*, float*, float*, void*, int, int, int, int, int, \
+                                           float, hipStream_t);                                         \
+  template hipError_t launch_qs<D, QS_DQ>(const void*, const void*, const void*, const void*,           \
+                                          const void*, float*, float*, void*, int, int, int, int, int,  \
+                                          float, hipStream_t);
+SDPA_INST_QS(64)
+SDPA_INST_QS(128)
+SDPA_INST_QS(256)
+SDPA_INST_QS(512)
+
+}  // namespace sdpa

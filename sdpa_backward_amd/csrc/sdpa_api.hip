@@ -11,17 +11,19 @@
 
 #include <algorithm>
 
-#include "../../include/sdpa.h"
+#include "sdpa.h"
 #include "common.h"
 
 namespace sdpa {
+enum { QS_FWD = 0, QS_DQ = 1 };
+template <int D, int MODE>
+hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
+                     float* delta, void* out, int B, int Hq, int group, int L, int w_eff, float scale,
+                     hipStream_t stream);
 template <int D>
-hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
-                           float, hipStream_t);
-template <int D>
-hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const void*, const float*,
-                           void*, void*, void*, float*, float*, int, int, int, int, int, float, hipStream_t,
-                           hipEvent_t, hipEvent_t);
+hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int L, int w_eff,
+                     float scale, hipStream_t stream);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
                           float, hipStream_t);
@@ -29,6 +31,24 @@ template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
                           void*, void*, void*, float*, int, int, int, int, int, float, hipStream_t,
                           hipEvent_t, hipEvent_t);
+
+// bf16 backward: dQ pass (also writes Delta), then the dK/dV pass; the
+// optional events bracket the dK/dV kernel.
+template <int D>
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
+                           int group, int L, int w_eff, float scale, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+  hipError_t e = launch_qs<D, QS_DQ>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, L,
+                                     w_eff, scale, stream);
+  if (e != hipSuccess) return e;
+  const bool timed = ev0 != nullptr && ev1 != nullptr;
+  if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = launch_kv<D>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, L, w_eff, scale, stream);
+  if (e != hipSuccess) return e;
+  if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
 }  // namespace sdpa
 
 namespace {
@@ -70,9 +90,7 @@ int check_shape(const Shape& s) {
 size_t workspace_for(const Shape& s) {
   if (s.empty()) return 0;
   const size_t rows = (size_t)s.B * s.Hq * s.L;
-  size_t bytes = align_up(rows * sizeof(float));                        // Delta
-  if (s.dtype == SDPA_BF16) bytes += align_up(rows * s.D * sizeof(float));  // fp32 dQ accumulator
-  return bytes;
+  return align_up(rows * sizeof(float));  // Delta_i = <dO_i, O_i>, one float per query row
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
@@ -113,10 +131,10 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
   const int w = s.w_eff();
   if (dtype == SDPA_BF16) {
     switch (D) {
-      case 64: return to_status(sdpa::launch_fwd_bf16<64>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
-      case 128: return to_status(sdpa::launch_fwd_bf16<128>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
-      case 256: return to_status(sdpa::launch_fwd_bf16<256>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
-      case 512: return to_status(sdpa::launch_fwd_bf16<512>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 64: return to_status(sdpa::launch_qs<64, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
+      case 128: return to_status(sdpa::launch_qs<128, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
+      case 256: return to_status(sdpa::launch_qs<256, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
+      case 512: return to_status(sdpa::launch_qs<512, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
     }
   } else {
     switch (D) {
@@ -141,16 +159,14 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
     if (p == nullptr || !aligned16(p)) return SDPA_ERR_INVALID_ARG;
   const size_t need = workspace_for(s);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SDPA_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * Hq * L;
   float* delta = static_cast<float*>(workspace);
-  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
   const int w = s.w_eff();
   if (dtype == SDPA_BF16) {
     switch (D) {
 #define SDPA_BWD_CASE(DD)                                                                             \
   case DD:                                                                                            \
-    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, B, Hq, \
-                                               group, L, w, scale, stream, main_begin, main_end));
+    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w, \
+                                               scale, stream, main_begin, main_end));
       SDPA_BWD_CASE(64)
       SDPA_BWD_CASE(128)
       SDPA_BWD_CASE(256)

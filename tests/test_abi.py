@@ -51,8 +51,8 @@ def test_workspace_is_linear_in_L(lib):
     assert ws[0] > 0
     for a, b in zip(ws, ws[1:]):
         assert abs(b - 2 * a) <= 512   # alignment slack only
-    # fp32 dQ accumulator + Delta for bf16, Delta only for fp32
-    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, BF16) == 32 * 16384 * 256 * 4 + 32 * 16384 * 4
+    # Delta only: one float per query row
+    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, BF16) == 32 * 16384 * 4
     assert lib.sdpa_bwd_workspace_bytes(1, 2, 128, 64, F32) == 1024
     assert lib.sdpa_bwd_workspace_bytes(0, 32, 16384, 256, BF16) == 0
     assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 100, BF16) == 0   # unsupported D
