@@ -86,42 +86,76 @@ SDPA_DEV bf16x8 c_to_op(const f32x16& c, int op) {
 SDPA_DEV bool allowed(int i, int j, int w_eff, int L) { return j <= i && j > i - w_eff && i < L; }
 
 // ---------------------------------------------------------------- swizzled tiles
+// Chunk c (16 bytes) of row r sits at chunk slot c ^ swz(r), swz(r) < 16:
+//   bits 2-3 = r & 3, bits 0-1 = (r >> 2) & 3.
+// 16 consecutive rows get 16 distinct slots (16-byte reads of one chunk
+// across rows, serviced 16 lanes per cycle, hit 16 distinct 16-byte bank
+// groups), and rows r..r+3 (r a multiple of 4) get distinct 64-byte quarters
+// (transposed reads, serviced 32 lanes = 4 rows x 64 bytes per cycle). Both
+// patterns measured conflict-free on the hardware bank-conflict counter for
+// the row strides used here. Only the low 4 chunk bits are permuted, so higher
+// chunk offsets stay additive and every read is a per-lane base plus an
+// immediate offset.
 template <int D>
 struct Tile {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int MASK = CPR >= 16 ? 15 : CPR - 1;
-  SDPA_DEV static int swz(int r) {
-    const int x = r & 15;
-    return (((x & 3) << 1) | ((x >> 2) & 1) | ((x >> 3) << 3)) & MASK;
+  static constexpr int CPR = D / 8;                         // 16-byte chunks per row
+  static constexpr int SMASK = CPR >= 16 ? 15 : CPR - 1;   // swizzle bits available
+  SDPA_DEV static int swz(int r) { return (((r & 3) << 2) | ((r >> 2) & 3)) & SMASK; }
+  SDPA_DEV static int slot(int r, int c) { return c ^ swz(r); }
+};
+
+// Per-lane LDS byte offsets for the two operand read patterns of a [rows][D]
+// swizzled tile. 16 registers serve every tile with row length D.
+//   dir[j]:  "direct" read, lane row l%32, chunk 2j + l/32 (j = 0..7)
+//   trn[2q + h]: transposed read, chunk block q (columns 32q..), rows +0 (h=0) / +8 (h=1)
+template <int D>
+struct LaneAddr {
+  uint32_t dir[8];
+  uint32_t trn[8];
+  SDPA_DEV void init(int lane) {
+    const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 8; j++) dir[j] = r * D * 2 + (Tile<D>::slot(r, 2 * j + hh) & 15) * 16;
+    const int G = lane >> 4, i = lane & 15;
+    const int row = 4 * (G >> 1) + (i >> 2);
+    const int cl = 2 * (G & 1) + ((i & 3) >> 1), within = (i & 1) * 8;  // bytes inside the chunk
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int rr = row + 8 * h;
+        trn[2 * q + h] = rr * D * 2 + (Tile<D>::slot(rr, 4 * q + cl) & 15) * 16 + within;
+      }
   }
-  // element offset of (row r, column k)
-  SDPA_DEV static int off(int r, int k) { return r * D + ((((k >> 3) ^ swz(r))) << 3) + (k & 7); }
 };
 
 // 4 consecutive bf16 of a row-major LDS tile, delivered transposed across
 // each 16-lane group (see header comment).
-SDPA_DEV bf16x4 lds_tr4(const bf16* p) {
+SDPA_DEV bf16x4 lds_tr4(const char* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
 
 // Operand from a swizzled tile T[k][mn] (rows are the contraction index):
 // lane l gets column mn0 + l%32 with "paired" k-slots over rows [k0, k0+16).
+// k0: multiple of 16; mn0: multiple of 32.
 template <int D>
-SDPA_DEV bf16x8 op_tr(const bf16* T, int k0, int mn0, int lane) {
-  const int G = lane >> 4, i = lane & 15;
-  const int row = k0 + 4 * (G >> 1) + (i >> 2);
-  const int col = mn0 + 16 * (G & 1) + 4 * (i & 3);
-  bf16x4 lo = lds_tr4(T + Tile<D>::off(row, col));
-  bf16x4 hi = lds_tr4(T + Tile<D>::off(row + 8, col));
+SDPA_DEV bf16x8 op_tr(const bf16* T, const LaneAddr<D>& a, int k0, int mn0) {
+  const int q = mn0 / 32;  // 4 chunks per 32-column block
+  const char* base = reinterpret_cast<const char*>(T) + k0 * D * 2 + (q >> 2) * 256;
+  bf16x4 lo = lds_tr4(base + a.trn[2 * (q & 3)]);
+  bf16x4 hi = lds_tr4(base + a.trn[2 * (q & 3) + 1]);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Operand from a swizzled tile T[mn][k] (columns are the contraction index):
 // lane l gets row mn0 + l%32 with "direct" k-slots k0 + 8*(l/32) + j.
+// k0: multiple of 16; mn0: multiple of 32.
 template <int D>
-SDPA_DEV bf16x8 op_direct(const bf16* T, int k0, int mn0, int lane) {
-  return *(const bf16x8*)(T + Tile<D>::off(mn0 + (lane & 31), k0 + 8 * (lane >> 5)));
+SDPA_DEV bf16x8 op_direct(const bf16* T, const LaneAddr<D>& a, int k0, int mn0) {
+  const int c = k0 / 8;  // even
+  const char* p = reinterpret_cast<const char*>(T) + a.dir[(c & 15) >> 1] + (c >> 4) * 256 + mn0 * D * 2;
+  return *(const bf16x8*)p;
 }
 
 // Issue asynchronous global->LDS loads of rows [0, R) of a [R][D] tile whose
@@ -138,7 +172,7 @@ SDPA_DEV void issue_tile(bf16* lds, const bf16* __restrict__ src, int valid, int
     if (PER % NW != 0 && j >= PER) break;
     const int p = j * 64 + lane;
     const int r = p / CPR;
-    const int c = (p % CPR) ^ Tile<D>::swz(r);
+    const int c = Tile<D>::slot(r, p % CPR);  // the slot map is an involution
     const int rr = r < valid ? r : valid - 1;
     const bf16* g = src + (size_t)rr * D + c * 8;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,

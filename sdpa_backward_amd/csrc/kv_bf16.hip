@@ -25,6 +25,11 @@
 
 namespace sdpa {
 
+// Which gradients one launch produces. D = 512 splits them into two launches
+// (dV, then dK) so each wave's accumulators fit the register file; smaller D
+// produce both in one pass.
+enum { KV_BOTH = 0, KV_DV = 1, KV_DK = 2 };
+
 template <int D>
 struct KvCfg {
   static constexpr int NW = 4;
@@ -48,7 +53,7 @@ SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
   lds_barrier();
 }
 
-template <int D>
+template <int D, int PASS>
 __global__ void __launch_bounds__(256, 1)
 kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
           const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
@@ -65,8 +70,10 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
   __shared__ __attribute__((aligned(16))) float rv1[C::NBUF == 2 ? 64 : 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, lane_id = lane;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
+  la.init(lane);
   const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
   const int nkt = (L + C::BKT - 1) / C::BKT;
@@ -80,16 +87,19 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
   issue_tile<D, C::BKT, C::NW>(ks, Kg + (size_t)k0 * D, L - k0, w, lane);
   // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
-  bf16x8 vreg[NKS];
-  const bf16* vrow = Vg + (size_t)(kj < L ? kj : 0) * D;
+  constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
+  bf16x8 vreg[WANT_DK ? NKS : 1];
+  if constexpr (WANT_DK) {
+    const bf16* vrow = Vg + (size_t)(kj < L ? kj : 0) * D;
 #pragma unroll
-  for (int s = 0; s < NKS; s++) vreg[s] = kj < L ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+    for (int s = 0; s < NKS; s++) vreg[s] = kj < L ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+  }
 
-  f32x16 dkacc[NDB], dvacc[NDB];
+  f32x16 dkacc[WANT_DK ? NDB : 1], dvacc[WANT_DV ? NDB : 1];
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
-    dkacc[d] = zero16();
-    dvacc[d] = zero16();
+    if constexpr (WANT_DK) dkacc[d] = zero16();
+    if constexpr (WANT_DV) dvacc[d] = zero16();
   }
 
   // query tiles that can see a key of this workgroup, for each q-head of the group
@@ -107,8 +117,6 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     ds = dO + off;
   };
   auto issue = [&](int it, bf16* qd, bf16* dd, float* rv) {
-    int lane = lane_id;
-    asm volatile("" : "+v"(lane));
     const bf16 *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
@@ -124,10 +132,6 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   };
 
   auto compute = [&](int it, const bf16* Qc, const bf16* dOc, const float* rv) {
-    // Operand addresses depend only on the lane; recomputing them each step
-    // (a few VALU ops) is cheaper than keeping dozens of them live in VGPRs.
-    int lane = lane_id;
-    asm volatile("" : "+v"(lane));
     const int q0 = (qt_lo + it % nq) * C::BQ;
     const int r1 = min(q0 + 31, L - 1);
     const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
@@ -138,19 +142,20 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
         const int d0 = dw0 + 16 * s;
-        s_acc = mfma(op_direct<D>(Qc, d0, 0, lane), op_direct<D>(ks, d0, 32 * kwi, lane), s_acc);
-        dp_acc = mfma(op_direct<D>(dOc, d0, 0, lane), vreg[s], dp_acc);
+        s_acc = mfma(op_direct<D>(Qc, la, d0, 0), op_direct<D>(ks, la, d0, 32 * kwi), s_acc);
+        if constexpr (WANT_DK) dp_acc = mfma(op_direct<D>(dOc, la, d0, 0), vreg[s], dp_acc);
       }
-      // schedule: three 16-byte LDS reads, then the two MFMAs they feed (reads run one step ahead)
+      // schedule: LDS reads run two steps (6 reads) ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
       }
     }
     if constexpr (C::DS == 2) {
       kv_exchange_add(s_acc, xbuf, w, lane);
-      kv_exchange_add(dp_acc, xbuf, w, lane);
+      if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
     }
     if (!active) return;
 #pragma unroll
@@ -164,24 +169,31 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         float p = __builtin_amdgcn_exp2f(s_acc[i] * scale_log2 - lv);
         if (!full && !allowed(q0 + c_row(i, hh), kj, w_eff, L)) p = 0.f;
         s_acc[i] = p;
-        dp_acc[i] = p * (dp_acc[i] - dv);
+        if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
       }
     }
     const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
     const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
+    (void)pa0; (void)pa1; (void)da0; (void)da1;
+    constexpr int MPB = (WANT_DV ? 2 : 0) + (WANT_DK ? 2 : 0);  // MFMAs per head-dim block
 #pragma unroll
     for (int d = 0; d < NDB; d++) {
       const int c0 = dw0 + 32 * d;
-      dvacc[d] = mfma(pa0, op_tr<D>(dOc, 0, c0, lane), dvacc[d]);
-      dvacc[d] = mfma(pa1, op_tr<D>(dOc, 16, c0, lane), dvacc[d]);
-      dkacc[d] = mfma(da0, op_tr<D>(Qc, 0, c0, lane), dkacc[d]);
-      dkacc[d] = mfma(da1, op_tr<D>(Qc, 16, c0, lane), dkacc[d]);
+      if constexpr (WANT_DV) {
+        dvacc[d] = mfma(pa0, op_tr<D>(dOc, la, 0, c0), dvacc[d]);
+        dvacc[d] = mfma(pa1, op_tr<D>(dOc, la, 16, c0), dvacc[d]);
+      }
+      if constexpr (WANT_DK) {
+        dkacc[d] = mfma(da0, op_tr<D>(Qc, la, 0, c0), dkacc[d]);
+        dkacc[d] = mfma(da1, op_tr<D>(Qc, la, 16, c0), dkacc[d]);
+      }
     }
-    // schedule: two transposed 8-byte reads (one operand), then one MFMA
+    // schedule: transposed reads run one head-dim block ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
 #pragma unroll
-    for (int d = 0; d < 4 * NDB; d++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    for (int d = 0; d < NDB; d++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MPB, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
     }
   };
 
@@ -216,8 +228,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     for (int i = 0; i < 16; i++) {
       const int key = kb0 + c_row(i, hh);
       if (key < L) {
-        dKg[(size_t)key * D + col] = (bf16)(dkacc[d][i] * scale);
-        dVg[(size_t)key * D + col] = (bf16)dvacc[d][i];
+        if constexpr (WANT_DK) dKg[(size_t)key * D + col] = (bf16)(dkacc[d][i] * scale);
+        if constexpr (WANT_DV) dVg[(size_t)key * D + col] = (bf16)dvacc[d][i];
       }
     }
   }
@@ -230,9 +242,20 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
   using C = KvCfg<D>;
   const long nwg = (long)((L + C::BKT - 1) / C::BKT) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_kernel<D>, dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq, group, L, w_eff,
-                     scale, scale * kLog2e);
+  if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
+    hipLaunchKernelGGL((kv_kernel<D, KV_DV>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
+                       group, L, w_eff, scale, scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kv_kernel<D, KV_DK>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
+                       group, L, w_eff, scale, scale * kLog2e);
+  } else {
+    hipLaunchKernelGGL((kv_kernel<D, KV_BOTH>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
+                       group, L, w_eff, scale, scale * kLog2e);
+  }
   return hipGetLastError();
 }
 

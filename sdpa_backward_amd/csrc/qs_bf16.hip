@@ -78,6 +78,8 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
+  la.init(lane);
   const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int nqt = (L + C::BQ - 1) / C::BQ;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -148,10 +150,18 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       for (int mb = 0; mb < NMB; mb++)
 #pragma unroll
         for (int s = 0; s < NKS; s++) {
-          st[mb] = mfma(op_direct<D>(Kc, dw0 + 16 * s, 32 * mb, lane), qreg[s], st[mb]);
+          st[mb] = mfma(op_direct<D>(Kc, la, dw0 + 16 * s, 32 * mb), qreg[s], st[mb]);
           if constexpr (MODE == QS_DQ)
-            st[NMB + mb] = mfma(op_direct<D>(Vc, dw0 + 16 * s, 32 * mb, lane), dreg[s], st[NMB + mb]);
+            st[NMB + mb] = mfma(op_direct<D>(Vc, la, dw0 + 16 * s, 32 * mb), dreg[s], st[NMB + mb]);
         }
+      // schedule: LDS reads run two steps ahead of their MFMAs
+      constexpr int RPS = MODE == QS_DQ ? 2 : 1;  // reads (and MFMAs) per step
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
+#pragma unroll
+      for (int t = 0; t < NMB * NKS; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, RPS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+      }
     }
     if constexpr (C::DS == 2) exchange_add<NX>(st, xbuf, w, lane);
     if (!active) return;
@@ -194,9 +204,16 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         const bf16x8 p0 = c_to_op(st[mb], 0), p1 = c_to_op(st[mb], 1);
 #pragma unroll
         for (int d = 0; d < NDB; d++) {
-          acc[d] = mfma(op_tr<D>(Vc, 32 * mb, dw0 + 32 * d, lane), p0, acc[d]);
-          acc[d] = mfma(op_tr<D>(Vc, 32 * mb + 16, dw0 + 32 * d, lane), p1, acc[d]);
+          acc[d] = mfma(op_tr<D>(Vc, la, 32 * mb, dw0 + 32 * d), p0, acc[d]);
+          acc[d] = mfma(op_tr<D>(Vc, la, 32 * mb + 16, dw0 + 32 * d), p1, acc[d]);
         }
+      }
+      // schedule: transposed reads run two MFMAs (4 reads) ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int t = 0; t < NMB * NDB; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
       }
     } else {
 #pragma unroll
@@ -210,9 +227,15 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         const bf16x8 d0 = c_to_op(st[NMB + mb], 0), d1 = c_to_op(st[NMB + mb], 1);
 #pragma unroll
         for (int d = 0; d < NDB; d++) {
-          acc[d] = mfma(op_tr<D>(Kc, 32 * mb, dw0 + 32 * d, lane), d0, acc[d]);
-          acc[d] = mfma(op_tr<D>(Kc, 32 * mb + 16, dw0 + 32 * d, lane), d1, acc[d]);
+          acc[d] = mfma(op_tr<D>(Kc, la, 32 * mb, dw0 + 32 * d), d0, acc[d]);
+          acc[d] = mfma(op_tr<D>(Kc, la, 32 * mb + 16, dw0 + 32 * d), d1, acc[d]);
         }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int t = 0; t < NMB * NDB; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
       }
     }
   };
