@@ -21,6 +21,8 @@
 //   dK_w += dS^T . Q                  A: dS^T (C tile)        B: Q  (LDS, transposed reads)
 // Q/dO tiles stream into LDS with asynchronous global->LDS loads, double
 // buffered when they fit (D <= 256).
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdpa {
@@ -158,20 +160,26 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
     }
     if (!active) return;
+    // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
+    // tiles, as a select (the wave-uniform test stays outside the element loop)
+    auto form = [&](auto masked) {
 #pragma unroll
-    for (int blk = 0; blk < 4; blk++) {
-      const float4 l4 = *(const float4*)(rv + 8 * blk + 4 * hh);
-      const float4 d4 = *(const float4*)(rv + 32 + 8 * blk + 4 * hh);
+      for (int blk = 0; blk < 4; blk++) {
+        const float4 l4 = *(const float4*)(rv + 8 * blk + 4 * hh);
+        const float4 d4 = *(const float4*)(rv + 32 + 8 * blk + 4 * hh);
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int i = 4 * blk + r;
-        const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
-        float p = __builtin_amdgcn_exp2f(s_acc[i] * scale_log2 - lv);
-        if (!full && !allowed(q0 + c_row(i, hh), kj, w_eff, L)) p = 0.f;
-        s_acc[i] = p;
-        if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
+        for (int r = 0; r < 4; r++) {
+          const int i = 4 * blk + r;
+          const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
+          float p = __builtin_amdgcn_exp2f(s_acc[i] * scale_log2 - lv);
+          if constexpr (decltype(masked)::value) p = allowed(q0 + c_row(i, hh), kj, w_eff, L) ? p : 0.f;
+          s_acc[i] = p;
+          if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
+        }
       }
-    }
+    };
+    if (full) form(std::false_type{});
+    else form(std::true_type{});
     const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
     const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
     (void)pa0; (void)pa1; (void)da0; (void)da1;

@@ -27,6 +27,8 @@
 //        dQ^T += K^T . dS^T                 A: K (transposed reads) B: dS^T (C tile reused)
 // S, P, dP stay fp32; only P and dS are rounded to bf16 as MFMA operands
 // (section "fp32 score tiles" of the Lab 028 page).
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdpa {
@@ -168,15 +170,20 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
     if constexpr (MODE == QS_FWD) {
       float mx = -INFINITY;
+      auto scores = [&](auto masked) {  // log2-domain scores, -inf outside the band (edge tiles)
 #pragma unroll
-      for (int mb = 0; mb < NMB; mb++)
+        for (int mb = 0; mb < NMB; mb++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          float x = st[mb][i] * scale_log2;
-          if (!full && !allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L)) x = -INFINITY;
-          st[mb][i] = x;
-          mx = fmaxf(mx, x);
-        }
+          for (int i = 0; i < 16; i++) {
+            float x = st[mb][i] * scale_log2;
+            if constexpr (decltype(masked)::value)
+              x = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? x : -INFINITY;
+            st[mb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+      };
+      if (full) scores(std::false_type{});
+      else scores(std::true_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool need = mx > m + 8.f;  // raise the used max only beyond 2^8 headroom
       if (__any(need)) {
@@ -218,12 +225,17 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
+        auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          float p = __builtin_amdgcn_exp2f(st[mb][i] * scale_log2 - lse2);
-          if (!full && !allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L)) p = 0.f;
-          st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
-        }
+          for (int i = 0; i < 16; i++) {
+            float p = __builtin_amdgcn_exp2f(st[mb][i] * scale_log2 - lse2);
+            if constexpr (decltype(masked)::value)
+              p = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? p : 0.f;
+            st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
+          }
+        };
+        if (full) form(std::false_type{});
+        else form(std::true_type{});
         const bf16x8 d0 = c_to_op(st[NMB + mb], 0), d1 = c_to_op(st[NMB + mb], 1);
 #pragma unroll
         for (int d = 0; d < NDB; d++) {
