@@ -33,7 +33,7 @@ METRIC = "attention fwd+bwd mask-aware TFLOP/s and % of bf16 MFMA peak; peak mem
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public figure (no sparsity)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_window1024_L16384_D256_h32kv16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv_kernel_window1024_L16384_D256.json")
 MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_bf16.hip", "sdpa_backward_amd/csrc/common.h"]
 
 
