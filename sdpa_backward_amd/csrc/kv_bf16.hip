@@ -141,18 +141,30 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
     f32x16 s_acc = zero16(), dp_acc = zero16();
     if (active) {
+      // all of S first, then dP: exp(S) can start while the dP MFMAs run
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
         const int d0 = dw0 + 16 * s;
         s_acc = mfma(op_direct<D>(Qc, la, d0, 0), op_direct<D>(ks, la, d0, 32 * kwi), s_acc);
-        if constexpr (WANT_DK) dp_acc = mfma(op_direct<D>(dOc, la, d0, 0), vreg[s], dp_acc);
       }
-      // schedule: LDS reads run two steps (6 reads) ahead of the MFMAs that use them
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      if constexpr (WANT_DK) {
+#pragma unroll
+        for (int s = 0; s < NKS; s++)
+          dp_acc = mfma(op_direct<D>(dOc, la, dw0 + 16 * s, 0), vreg[s], dp_acc);
+      }
+      // schedule: LDS reads run ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int s = 0; s < NKS; s++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      if constexpr (WANT_DK) {
+#pragma unroll
+        for (int s = 0; s < NKS; s++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
     if constexpr (C::DS == 2) {
