@@ -81,6 +81,49 @@ SDPA_DEV bf16x8 c_to_op(const f32x16& c, int op) {
   return r;
 }
 
+// Max / sum of a value over the two 32-lane halves of the wave (lanes l and
+// l ^ 32 hold the two halves of one C-tile column). v_permlane32_swap keeps the
+// exchange in the VALU: no LDS round trip, no wait on outstanding LDS reads.
+SDPA_DEV float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SDPA_DEV float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Ask the register allocator to hold a value in AGPRs at this point (MFMAs read
+// and write AGPRs directly; only VALU arithmetic needs VGPRs).
+SDPA_DEV void keep_in_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+SDPA_DEV void keep_in_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
+
+// x[t] *= a for accumulator tiles that stay in AGPRs: each element is read
+// into a VGPR, multiplied and written back inside one asm statement, so the
+// register allocator never moves the tiles into VGPRs for this rare rescale
+// (plain C++ makes it copy every tile out of and back into AGPRs on every
+// iteration). The leading wait states cover an MFMA still writing a tile (a VALU
+// read of an MFMA result needs them), the trailing ones a following MFMA that
+// reads a tile as its accumulator input.
+template <int N>
+SDPA_DEV void scale_in_agpr(f32x16 (&x)[N], float a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+#pragma unroll
+  for (int t = 0; t < N; t++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      float e = x[t][i], tmp;
+      asm volatile(
+          "v_accvgpr_read_b32 %1, %0\n\t"
+          "v_mul_f32_e32 %1, %2, %1\n\t"
+          "v_accvgpr_write_b32 %0, %1"
+          : "+a"(e), "=&v"(tmp)
+          : "v"(a));
+      x[t][i] = e;
+    }
+  asm volatile("s_nop 7");
+}
+
 // Allowed (query i, key j) pair: causal diagonal and window (w_eff = min(window, L),
 // or L for plain causal); rows i >= L do not exist (j <= i < L then implies j < L).
 SDPA_DEV bool allowed(int i, int j, int w_eff, int L) { return j <= i && j > i - w_eff && i < L; }
@@ -158,26 +201,49 @@ SDPA_DEV bf16x8 op_direct(const bf16* T, const LaneAddr<D>& a, int k0, int mn0) 
   return *(const bf16x8*)p;
 }
 
-// Issue asynchronous global->LDS loads of rows [0, R) of a [R][D] tile whose
-// global rows start at src (row stride D). Rows >= valid re-read row valid-1:
-// finite data that the masks zero out downstream. valid >= 1.
+// Asynchronous global->LDS tile loads through a buffer resource. A wave
+// issues whole 1 KB blocks (buffer_load_dwordx4 ... lds: lane l's 16 bytes land
+// at the block's LDS base + 16 l); the lane's source offset inside the tile is
+// fixed, so it is computed once (voff) and every load needs no address
+// arithmetic. The resource of each tile covers only its valid rows: lanes whose
+// offset falls beyond them are range-checked by the hardware and read nothing
+// from memory (rows past the end of the sequence are masked downstream; the
+// buffers are zeroed once at kernel start, so such rows only ever hold zeros
+// or finite data of an earlier tile).
 template <int D, int R, int NW>
-SDPA_DEV void issue_tile(bf16* lds, const bf16* __restrict__ src, int valid, int w, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int PER = R * CPR / 64;  // wave instructions (1 KB each) per tile
+struct TileLoader {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int PER = R * CPR / 64;         // 1 KB blocks per tile
+  static constexpr int NJ = (PER + NW - 1) / NW;   // blocks issued by one wave
   static_assert((R * CPR) % 64 == 0, "tile must be a whole number of 1 KB blocks");
+  uint32_t voff[NJ];
+  SDPA_DEV void init(int w, int lane) {
 #pragma unroll
-  for (int jj = 0; jj < (PER + NW - 1) / NW; jj++) {
-    const int j = jj * NW + w;
-    if (PER % NW != 0 && j >= PER) break;
-    const int p = j * 64 + lane;
-    const int r = p / CPR;
-    const int c = Tile<D>::slot(r, p % CPR);  // the slot map is an involution
-    const int rr = r < valid ? r : valid - 1;
-    const bf16* g = src + (size_t)rr * D + c * 8;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)(lds + j * 512), 16, 0, 0);
+    for (int jj = 0; jj < NJ; jj++) {
+      const int p = (jj * NW + w) * 64 + lane;
+      const int r = p / CPR;
+      voff[jj] = (uint32_t)(r * D + Tile<D>::slot(r, p % CPR) * 8) * 2;  // the slot map is an involution
+    }
   }
+  // Rows [0, min(valid, R)) of the [R][D] tile starting at src (row stride D).
+  SDPA_DEV void issue(bf16* lds, const bf16* src, int valid, int w) const {
+    const int rows = valid < R ? valid : R;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
+#pragma unroll
+    for (int jj = 0; jj < NJ; jj++) {
+      const int j = jj * NW + w;
+      if (PER % NW != 0 && j >= PER) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + j * 512), 16,
+                                               (int)voff[jj], 0, 0, 0);
+    }
+  }
+};
+
+// Zero n bf16 elements of an LDS buffer with the workgroup's 256 threads
+// (n a multiple of 8 * 256).
+SDPA_DEV void zero_lds(bf16* p, int n, int tid) {
+  for (int i = tid * 8; i < n; i += 256 * 8) *(bf16x8*)(p + i) = zero_bf16x8();
 }
 
 // Wait for this wave's outstanding vector-memory loads and LDS operations,

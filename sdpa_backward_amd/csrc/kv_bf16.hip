@@ -87,7 +87,21 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const bf16* Kg = K + ((size_t)b * Hkv + g) * L * D;
   const bf16* Vg = V + ((size_t)b * Hkv + g) * L * D;
 
-  issue_tile<D, C::BKT, C::NW>(ks, Kg + (size_t)k0 * D, L - k0, w, lane);
+  zero_lds(ks, C::BKT * D, tid);
+  zero_lds(qb0, QT, tid);
+  zero_lds(db0, QT, tid);
+  if constexpr (C::NBUF == 2) {
+    zero_lds(qb1, QT, tid);
+    zero_lds(db1, QT, tid);
+  }
+  lds_barrier();
+  {
+    TileLoader<D, C::BKT, C::NW> kld;
+    kld.init(w, lane);
+    kld.issue(ks, Kg + (size_t)k0 * D, L - k0, w);
+  }
+  TileLoader<D, C::BQ, C::NW> ld;  // per-lane source offsets of the Q/dO tile loads
+  ld.init(w, lane);
   // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
   constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
   bf16x8 vreg[WANT_DK ? NKS : 1];
@@ -122,8 +136,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     const bf16 *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
-    issue_tile<D, C::BQ, C::NW>(qd, qs, L - q0, w, lane);
-    issue_tile<D, C::BQ, C::NW>(dd, ds, L - q0, w, lane);
+    ld.issue(qd, qs, L - q0, w);
+    ld.issue(dd, ds, L - q0, w);
     if (w == 0) {  // lanes 0..31: lse of rows q0.., lanes 32..63: Delta of rows q0.. (clamped to L-1)
       const int hq = g * group + it / nq;
       const int row = min(q0 + (lane & 31), L - 1);

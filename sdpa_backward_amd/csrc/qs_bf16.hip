@@ -35,6 +35,16 @@ namespace sdpa {
 
 enum { QS_FWD = 0, QS_DQ = 1 };
 
+// How many MFMAs ahead the LDS operand reads are issued (S / dP products, and
+// the O / dQ products). Deeper look-ahead hides LDS latency at the cost of
+// operand registers.
+#ifndef QS_AHEAD_S
+#define QS_AHEAD_S 4
+#endif
+#ifndef QS_AHEAD_O
+#define QS_AHEAD_O 4
+#endif
+
 template <int D>
 struct QsCfg {
   static constexpr int NW = 4;
@@ -82,6 +92,8 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
   la.init(lane);
+  TileLoader<D, C::BK, C::NW> ld;  // per-lane source offsets of the K/V tile loads
+  ld.init(w, lane);
   const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int nqt = (L + C::BQ - 1) / C::BQ;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -137,9 +149,13 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   auto step = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
     if (kt + 1 <= kt_hi) {  // prefetch the next tile into the other buffers
       const int jn = (kt + 1) * BK;
-      issue_tile<D, BK, C::NW>(Kn, Kg + (size_t)jn * D, L - jn, w, lane);
-      issue_tile<D, BK, C::NW>(Vn, Vg + (size_t)jn * D, L - jn, w, lane);
+      ld.issue(Kn, Kg + (size_t)jn * D, L - jn, w);
+      ld.issue(Vn, Vg + (size_t)jn * D, L - jn, w);
     }
+#pragma unroll
+    for (int s = 0; s < NKS; s++) keep_in_agpr(qreg[s]);
+#pragma unroll
+    for (int d = 0; d < NDB; d++) keep_in_agpr(acc[d]);
     const int j0 = kt * BK;
     const bool active = wr0 <= wr1 && j0 <= wr1 && j0 + BK - 1 > wr0 - w_eff;
     const bool full = j0 + BK - 1 <= wr0 && j0 > wr1 - w_eff && wr1 == wr0 + 31;
@@ -156,9 +172,9 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
           if constexpr (MODE == QS_DQ)
             st[NMB + mb] = mfma(op_direct<D>(Vc, la, dw0 + 16 * s, 32 * mb), dreg[s], st[NMB + mb]);
         }
-      // schedule: LDS reads run two steps ahead of their MFMAs
+      // schedule: LDS reads run QS_AHEAD_S MFMAs ahead
       constexpr int RPS = MODE == QS_DQ ? 2 : 1;  // reads (and MFMAs) per step
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, QS_AHEAD_S * RPS, 0);
 #pragma unroll
       for (int t = 0; t < NMB * NKS; t++) {
         __builtin_amdgcn_sched_group_barrier(0x008, RPS, 0);
@@ -169,43 +185,40 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     if (!active) return;
 
     if constexpr (MODE == QS_FWD) {
+      // The max is taken over raw scores (scale > 0 commutes with it); masked
+      // entries become -inf first (edge tiles only).
       float mx = -INFINITY;
-      auto scores = [&](auto masked) {  // log2-domain scores, -inf outside the band (edge tiles)
+      auto scores = [&](auto masked) {
 #pragma unroll
         for (int mb = 0; mb < NMB; mb++)
 #pragma unroll
           for (int i = 0; i < 16; i++) {
-            float x = st[mb][i] * scale_log2;
             if constexpr (decltype(masked)::value)
-              x = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? x : -INFINITY;
-            st[mb][i] = x;
-            mx = fmaxf(mx, x);
+              st[mb][i] = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? st[mb][i] : -INFINITY;
+            mx = fmaxf(mx, st[mb][i]);
           }
       };
       if (full) scores(std::false_type{});
       else scores(std::true_type{});
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_max(mx) * scale_log2;
       const bool need = mx > m + 8.f;  // raise the used max only beyond 2^8 headroom
-      if (__any(need)) {
+      if (__any(need && m != -INFINITY)) {  // (the first tile of a row has nothing to rescale)
         const float alpha = need ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
-        if (need) m = mx;
         lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; d++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) acc[d][i] *= alpha;
+        scale_in_agpr(acc, alpha);
       }
-      const float m_use = m == -INFINITY ? 0.f : m;
+      if (need) m = mx;
+      const float neg_m = m == -INFINITY ? 0.f : -m;
       float rs = 0.f;
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          const float p = __builtin_amdgcn_exp2f(st[mb][i] - m_use);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, neg_m));
           st[mb][i] = p;
           rs += p;
         }
-      lsum += rs + __shfl_xor(rs, 32);
+      lsum += half_sum(rs);
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
         const bf16x8 p0 = c_to_op(st[mb], 0), p1 = c_to_op(st[mb], 1);
@@ -215,12 +228,12 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
           acc[d] = mfma(op_tr<D>(Vc, la, 32 * mb + 16, dw0 + 32 * d), p1, acc[d]);
         }
       }
-      // schedule: transposed reads run two MFMAs (4 reads) ahead
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      // schedule: transposed reads run QS_AHEAD_O MFMAs ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS_AHEAD_O, 1);
 #pragma unroll
       for (int t = 0; t < NMB * NDB; t++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS_AHEAD_O, 1);
       }
     } else {
 #pragma unroll
@@ -228,7 +241,7 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
           for (int i = 0; i < 16; i++) {
-            float p = __builtin_amdgcn_exp2f(st[mb][i] * scale_log2 - lse2);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, -lse2));
             if constexpr (decltype(masked)::value)
               p = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? p : 0.f;
             st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
@@ -243,19 +256,24 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
           acc[d] = mfma(op_tr<D>(Kc, la, 32 * mb + 16, dw0 + 32 * d), d1, acc[d]);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS_AHEAD_O, 1);
 #pragma unroll
       for (int t = 0; t < NMB * NDB; t++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS_AHEAD_O, 1);
       }
     }
   };
 
   {  // first tile
     const int j0 = kt_lo * BK;
-    issue_tile<D, BK, C::NW>(kb0, Kg + (size_t)j0 * D, L - j0, w, lane);
-    issue_tile<D, BK, C::NW>(vb0, Vg + (size_t)j0 * D, L - j0, w, lane);
+    zero_lds(kb0, C::TILE, tid);
+    zero_lds(kb1, C::TILE, tid);
+    zero_lds(vb0, C::TILE, tid);
+    zero_lds(vb1, C::TILE, tid);
+    lds_barrier();
+    ld.issue(kb0, Kg + (size_t)j0 * D, L - j0, w);
+    ld.issue(vb0, Vg + (size_t)j0 * D, L - j0, w);
     wait_all_and_barrier();
   }
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {

@@ -42,11 +42,12 @@ def run(w, inp, window=None, out=None, scale=None):
 
 def check_full(w, gpu, ref, tol=None):
     tol = TOL[w.dtype] if tol is None else tol
+    tol = tol if isinstance(tol, dict) else {n: tol for n in ("O", "dQ", "dK", "dV")}
     errs = {n: rel_fro(_np(gpu[n]), ref[n]) for n in ("O", "dQ", "dK", "dV")}
     errs["lse"] = float(np.max(np.abs(_np(gpu["lse"]) - ref["lse"]))) if ref["lse"].size else 0.0
     print(w.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     for n in ("O", "dQ", "dK", "dV"):
-        assert errs[n] <= tol, (n, errs[n])
+        assert errs[n] <= tol[n], (n, errs[n])
     assert errs["lse"] <= LSE_TOL, errs["lse"]
     return errs
 
@@ -107,6 +108,43 @@ def test_second_seed_draw():
         w = CONFIGS[which]
         inp = make_inputs(w, seed=w.seed + 1000)
         check_full(w, run(w, inp), oracle_full(w, inp))
+
+
+RISING = [
+    # name, Hq, Hkv, L, D, mask, window
+    ("rising_causal_D256", 2, 1, 1024, 256, MASK_CAUSAL, 0),
+    ("rising_w300_D128", 2, 2, 1000, 128, MASK_WINDOW, 300),
+    ("rising_causal_D512", 2, 1, 700, 512, MASK_CAUSAL, 0),
+    ("rising_w100_D64", 2, 1, 900, 64, MASK_WINDOW, 100),
+]
+
+
+@pytest.mark.parametrize("case", RISING, ids=[c[0] for c in RISING])
+def test_rising_scores_force_rescales(case):
+    """Scores that grow along the key axis by about 8 (natural log units) per
+    64 keys: the running row max of the forward pass rises past its headroom on
+    almost every key tile, so the accumulator rescale runs again and again.
+    Every query shares a direction u; key j carries (j / L) * alpha * u.
+
+    O and lse (what the rescale touches) keep the usual gates. dQ gets 6e-2:
+    with u in every key, dQ_i = sum_j dS_ij k_j cancels heavily, and rounding
+    dS and O (through Delta) to bf16, as every bf16 MFMA path must, already
+    leaves 2.3e-2 against the fp64 oracle in the D=256 case (oracle arithmetic
+    with only those two roundings added)."""
+    name, Hq, Hkv, L, D, mask, window = case
+    w = Workload(name, 1, Hq, Hkv, L, D, "bf16", mask, window, seed=7300 + D)
+    g = torch.Generator().manual_seed(w.seed)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm() * math.sqrt(D)
+    alpha = 8.0 * (L / 64) / math.sqrt(D)   # score rise over the whole sequence: about 8 L / 64
+    ramp = (torch.arange(L, dtype=torch.float32) / L)[:, None] * alpha
+    inp = {
+        "q": (torch.randn(1, Hq, L, D, generator=g) * 0.5 + u).to(torch.bfloat16),
+        "k": (torch.randn(1, Hkv, L, D, generator=g) * 0.5 + ramp * u).to(torch.bfloat16),
+        "v": torch.randn(1, Hkv, L, D, generator=g).to(torch.bfloat16),
+        "do": torch.randn(1, Hq, L, D, generator=g).to(torch.bfloat16),
+    }
+    check_full(w, run(w, inp), oracle_full(w, inp), tol={"O": 1e-2, "dQ": 6e-2, "dK": 1e-2, "dV": 1e-2})
 
 
 def _sample_rows(L, rng, n=24):
