@@ -128,6 +128,12 @@ SDPA_DEV void scale_in_agpr(f32x16 (&x)[N], float a) {
 // or L for plain causal); rows i >= L do not exist (j <= i < L then implies j < L).
 SDPA_DEV bool allowed(int i, int j, int w_eff, int L) { return j <= i && j > i - w_eff && i < L; }
 
+// The same test in two steps for a run of keys j = j0 + r: base = i - j0 (or a
+// value that fails every test when row i does not exist), then key j0 + r is
+// allowed iff 0 <= base - r < w_eff, one unsigned compare per key.
+SDPA_DEV int band_base(int i, int j0, int L) { return i < L ? i - j0 : INT32_MIN; }
+SDPA_DEV bool in_band(int base, int r, int w_eff) { return (uint32_t)base - (uint32_t)r < (uint32_t)w_eff; }
+
 // ---------------------------------------------------------------- swizzled tiles
 // Chunk c (16 bytes) of row r sits at chunk slot c ^ swz(r), swz(r) < 16:
 //   bits 2-3 = r & 3, bits 0-1 = (r >> 2) & 3.

@@ -188,6 +188,9 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     if (!active) return;
     // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
     // tiles, as a select (the wave-uniform test stays outside the element loop)
+    // rows q0 + c_row(i, hh) vs this lane's key kj: in the band iff
+    // 0 <= q0 + c_row - kj < w_eff, and the row must exist (< L)
+    const int base = q0 + 4 * hh - kj, rowlim = L - q0 - 4 * hh;
     auto form = [&](auto masked) {
 #pragma unroll
       for (int blk = 0; blk < 4; blk++) {
@@ -197,8 +200,11 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         for (int r = 0; r < 4; r++) {
           const int i = 4 * blk + r;
           const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
-          float p = __builtin_amdgcn_exp2f(s_acc[i] * scale_log2 - lv);
-          if constexpr (decltype(masked)::value) p = allowed(q0 + c_row(i, hh), kj, w_eff, L) ? p : 0.f;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], scale_log2, -lv));
+          if constexpr (decltype(masked)::value) {
+            const int rr = 8 * blk + r;  // c_row(i, hh) - 4 hh
+            p = (uint32_t)(base + rr) < (uint32_t)w_eff && rr < rowlim ? p : 0.f;
+          }
           s_acc[i] = p;
           if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
         }

@@ -190,13 +190,15 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       float mx = -INFINITY;
       auto scores = [&](auto masked) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; mb++)
+        for (int mb = 0; mb < NMB; mb++) {
+          const int base = band_base(qi, j0 + 32 * mb + 4 * hh, L);
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             if constexpr (decltype(masked)::value)
-              st[mb][i] = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? st[mb][i] : -INFINITY;
+              st[mb][i] = in_band(base, 8 * (i >> 2) + (i & 3), w_eff) ? st[mb][i] : -INFINITY;
             mx = fmaxf(mx, st[mb][i]);
           }
+        }
       };
       if (full) scores(std::false_type{});
       else scores(std::true_type{});
@@ -238,12 +240,13 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
+        const int base = band_base(qi, j0 + 32 * mb + 4 * hh, L);
         auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, -lse2));
             if constexpr (decltype(masked)::value)
-              p = allowed(qi, j0 + 32 * mb + c_row(i, hh), w_eff, L) ? p : 0.f;
+              p = in_band(base, 8 * (i >> 2) + (i & 3), w_eff) ? p : 0.f;
             st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
           }
         };
