@@ -3,9 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = the whole hot path on one batch: sdpa_fwd_lse, then sdpa_bwd
-(Delta pre-pass, main backward kernel, dQ conversion), with inputs resident in
-device memory before the timed region starts. Default workload: the causal +
+One step = the whole hot path on one batch: sdpa_fwd_lse (forward kernel),
+then sdpa_bwd (query-stationary dQ kernel, which also writes Delta, then the
+key-stationary dK/dV kernel), with inputs resident in device memory before the
+timed region starts. Default workload: the causal +
 sliding-window (1024) layer at L = 16384, D = 256, 32 query / 16 kv heads.
 Prints one JSON line on stdout; diagnostics go to stderr.
 

@@ -1,0 +1,207 @@
+"""Summaries of rocprofv3 output for the attention kernels (kernel time,
+hardware counters, HBM traffic of the dK/dV kernel).
+
+    python -m sdpa_backward_amd.profsum OUTDIR [--workload NAME] [--cmd-prefix TEXT]
+
+OUTDIR is what collect_profiles.sh wrote: trace/ (kernel trace), p1..p4/
+(counter passes), trace.log (the bench JSON line of the traced run). Writes
+kernel_stats_<tag>.md, counters_<tag>.md and traffic_kv_kernel_<tag>.json into
+OUTDIR; <tag> names the workload by its mask and sizes.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_bf16.hip", "sdpa_backward_amd/csrc/common.h"]
+COPY_KERNEL = "copyBuffer"   # the 1 GiB device copy bench.py --copy-probe runs
+COPY_BYTES = 1 << 30
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in MAIN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def tag(w) -> str:
+    mask = f"window{w.window}" if w.mask == "causal_window" else "causal"
+    return f"{mask}_L{w.L}_D{w.D}"
+
+
+def short(name: str) -> str:
+    name = name.replace("void ", "")
+    name = re.sub(r"\(.*", "", name)
+    return name
+
+
+def roles(w):
+    """kernel-name prefix -> (role, useful FLOP per call, algorithmic bytes read, written)."""
+    from bench import allowed_pairs
+    N = allowed_pairs(w)
+    e = 2  # bf16
+    q = w.B * w.Hq * w.L * w.D * e
+    kv = w.B * w.Hkv * w.L * w.D * e
+    row = w.B * w.Hq * w.L * 4
+    D = w.D
+    return {
+        f"sdpa::qs_kernel<{D}, 0>": ("forward (O, lse)", 4 * D * N, q + 2 * kv, q + row),
+        f"sdpa::qs_kernel<{D}, 1>": ("dQ pass (+Delta)", 6 * D * N, 3 * q + 2 * kv + row, q + row),
+        f"sdpa::kv_kernel<{D}, 0>": ("dK/dV pass", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
+        f"sdpa::kv_kernel<{D}, 1>": ("dV pass (D=512)", 4 * D * N, q + 2 * kv + 2 * row, kv),
+        f"sdpa::kv_kernel<{D}, 2>": ("dK pass (D=512)", 6 * D * N, 2 * q + 2 * kv + 2 * row, kv),
+    }
+
+
+def read_trace(d):
+    f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+    per = collections.defaultdict(list)
+    for r in rows:
+        per[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return per
+
+
+def read_counters(d):
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    agg = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(f)):
+        k = (r["Dispatch_Id"], r["Counter_Name"])
+        agg[k] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = short(r["Kernel_Name"])
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (disp, counter), v in agg.items():
+        per[names[disp]][counter].append(v)
+    return per
+
+
+def bench_line(path):
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{") and '"metric"' in line:
+            return json.loads(line)
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("outdir")
+    ap.add_argument("--workload", default="bf16_window1024_L16384_D256_h32kv16")
+    ap.add_argument("--steps", type=int, default=10, help="timed steps of the traced bench run")
+    a = ap.parse_args()
+    from workloads import BY_NAME
+    w = BY_NAME[a.workload]
+    t = tag(w)
+    R = roles(w)
+    out = a.outdir
+    script = "bash sdpa_backward_amd/collect_profiles.sh OUTDIR " + w.name
+    wl = f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, L={w.L}, D={w.D}, mask={w.mask}" + \
+         (f", window={w.window}" if w.mask == "causal_window" else "")
+
+    # ---------------------------------------------------------------- kernel time
+    tr = read_trace(os.path.join(out, "trace"))
+    bl = bench_line(os.path.join(out, "trace.log"))
+    lines = [f"# Kernel time: {wl}", "",
+             "Collected on one MI355X by (repository root):", "", "```", script, "```", "",
+             "whose trace step is:", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/trace -o run -- "
+             f"python -u bench.py --no-cpu-baseline --workload {w.name} --steps {a.steps} --warmup 2", "```", "",
+             f"'timed avg' is the mean over the last {a.steps} calls (the timed steps of bench.py).", "",
+             "| kernel | role | calls | all avg (us) | timed avg (us) | min (us) | useful FLOP per call | TFLOP/s at timed avg |",
+             "|---|---|---|---|---|---|---|---|"]
+    timed = {}
+    for k, v in tr.items():
+        if k not in R:
+            continue
+        role, flop, _, _ = R[k]
+        ta = statistics.mean(v[-a.steps:])
+        timed[k] = ta
+        lines.append(f"| `{k}` | {role} | {len(v)} | {statistics.mean(v):.1f} | {ta:.1f} | {min(v):.1f} | "
+                     f"{flop:.4e} | {flop / ta / 1e6:.1f} |")
+    main_k = f"sdpa::kv_kernel<{w.D}, 0>"
+    if bl and main_k in timed:
+        ev = bl["roofline"]["avg_launch_ms"] * 1e3
+        lines += ["", f"In-bench HIP events around `{main_k}` in the same run (mean over the timed steps): "
+                  f"{ev:.1f} us; rocprofv3 timed average: {timed[main_k]:.1f} us "
+                  f"({abs(ev - timed[main_k]) / timed[main_k] * 100:.1f} % apart)."]
+    lines += ["", "Useful FLOP per call: forward 4*D*N, dQ pass 6*D*N (S, dP, dQ), dK/dV pass 8*D*N "
+              "(S, dP, dV, dK); N = allowed (query, key) pairs over all heads. The backward's useful work "
+              "is 10*D*N; the two-pass backward computes 14*D*N (S and dP in both passes)."]
+    open(os.path.join(out, f"kernel_stats_{t}.md"), "w").write("\n".join(lines) + "\n")
+
+    # ---------------------------------------------------------------- counters
+    p = {i: read_counters(os.path.join(out, f"p{i}")) for i in (1, 2, 3, 4)}
+
+    def mean_of(i, k, c):
+        v = p[i].get(k, {}).get(c)
+        return statistics.mean(v) if v else float("nan")
+
+    copy_k = next((k for k in p[3] if COPY_KERNEL in k), None)
+    fetch_scale = COPY_BYTES / 1024 / mean_of(3, copy_k, "FETCH_SIZE") if copy_k else float("nan")
+    copy_k4 = next((k for k in p[4] if COPY_KERNEL in k), None)
+    write_scale = COPY_BYTES / 1024 / mean_of(4, copy_k4, "WRITE_SIZE") if copy_k4 else float("nan")
+    lines = [f"# Hardware counters: {wl}", "", "Collected on one MI355X by (repository root):", "", "```", script,
+             "```", "", "whose counter passes are (one rocprofv3 run each):", "", "```"]
+    for i, cs in enumerate(PASSES, 1):
+        lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {cs} --output-format csv -d OUTDIR/p{i} -o run -- "
+                     f"python -u bench.py --no-cpu-baseline --workload {w.name} --steps 2 --warmup 1 --copy-probe")
+    lines += ["```", "",
+              f"HBM byte scaling from the 1 GiB device copy in the same runs: FETCH_SIZE KiB x {fetch_scale:.3f} "
+              f"= bytes read / 1024, WRITE_SIZE KiB x {write_scale:.3f} = bytes written / 1024.", "",
+              "| kernel | MFMA busy | VALU instr / MFMA instr | LDS bank-conflict cycles / LDS active cycles "
+              "| HBM read | algorithmic read | HBM write | algorithmic write |",
+              "|---|---|---|---|---|---|---|---|"]
+    traffic = None
+    for k in R:
+        if k not in timed:
+            continue
+        role, flop, ar, aw = R[k]
+        busy = mean_of(1, k, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * timed[k] * 1e-6 * 2.4e9)
+        valu = mean_of(1, k, "SQ_INSTS_VALU") / mean_of(1, k, "SQ_INSTS_MFMA")
+        bank = mean_of(2, k, "SQ_LDS_BANK_CONFLICT") / mean_of(2, k, "SQ_ACTIVE_INST_LDS")
+        rd = mean_of(3, k, "FETCH_SIZE") * 1024 * fetch_scale
+        wr = mean_of(4, k, "WRITE_SIZE") * 1024 * write_scale
+        lines.append(f"| `{k}` | {100 * busy:.1f} % | {valu:.2f} | {bank:.3f} | {rd / 1e9:.3f} GB | {ar / 1e9:.3f} GB "
+                     f"| {wr / 1e9:.3f} GB | {aw / 1e9:.3f} GB |")
+        if k == main_k:
+            traffic = {"kernel": f"kv_kernel<{w.D}, 0> (dK/dV pass)", "workload": w.name,
+                       "sources_sha256": sources_sha256(),
+                       "fetch_kib_per_launch": mean_of(3, k, "FETCH_SIZE"),
+                       "write_kib_per_launch": mean_of(4, k, "WRITE_SIZE"),
+                       "fetch_scale": fetch_scale, "write_scale": write_scale,
+                       "hbm_bytes_per_launch": int(rd + wr),
+                       "source": f"profiles/counters_{t}.md"}
+    lines += ["", "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x timed avg kernel time x 2.4 GHz). "
+              "SQ_INSTS_VALU counts the MFMA instructions too. Algorithmic bytes: every input read once, every "
+              "output written once (bf16 tensors, fp32 lse / Delta rows)."]
+    open(os.path.join(out, f"counters_{t}.md"), "w").write("\n".join(lines) + "\n")
+    if traffic:
+        json.dump(traffic, open(os.path.join(out, f"traffic_kv_kernel_{t}.json"), "w"), indent=1)
+    print(f"wrote summaries for {t} into {out}")
+
+
+PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU",
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_ADDR_CONFLICT SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_WAIT_INST_ANY SQ_LDS_IDX_ACTIVE",
+    "FETCH_SIZE",
+    "WRITE_SIZE",
+]
+
+if __name__ == "__main__":
+    main()
