@@ -81,7 +81,8 @@ int check_shape(const Shape& s) {
   if (!isfinite(s.scale) || !(s.scale > 0.f)) return SDPA_ERR_INVALID_ARG;
   if (s.mask == SDPA_MASK_NONE) return SDPA_ERR_UNSUPPORTED;
   if (!d_supported(s.dtype, s.D)) return SDPA_ERR_UNSUPPORTED;
-  // launch-grid and index limits: heads and batch ride on grid y/z
+  // size limits: the kernels' 1-D grids hold at most 2^31 - 1 workgroups (checked
+  // again at launch), head and batch counts stay far below that
   if (s.Hq > 65535 || s.B > 65535) return SDPA_ERR_UNSUPPORTED;
   if ((int64_t)s.B * s.Hq * s.L > (int64_t(1) << 40)) return SDPA_ERR_UNSUPPORTED;
   return SDPA_OK;
