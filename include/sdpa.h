@@ -13,14 +13,15 @@
  * and the backward is the gradient of sum(dO * O) with respect to Q, K, V,
  * summed over the q-heads of each kv group for dK and dV.
  *
- * The forward "writes the logsumexp (the per-row softmax normalizer the
- * backward reuses)" and the backward "recomputes the softmax probability P"
- * tile by tile, skipping tiles above the causal diagonal and tiles entirely
- * outside the window: page "Lab 028 lab detail: Off NVIDIA, you fix the
- * platform yourself", sections "2026-10-21" ("What the code says") and
- * "What I changed, in plain terms" (items 1, 3, 4). GQA maps q-head h to kv
- * head h / group: page "MiniCPM5 Decode Megakernel - end-to-end build plan
- * (handoff)", section 4, stage 5.
+ * The forward also stores each row's logsumexp; the backward rebuilds P from
+ * the scores and that stored value one tile at a time, never visits tiles that
+ * lie wholly above the causal diagonal or wholly behind the window, and masks
+ * single elements only in the tiles the band's edges cross: page "Lab 028 lab
+ * detail: Off NVIDIA, you fix the platform yourself", sections "2026-10-21"
+ * ("What the code says") and "What I changed, in plain terms" (items 1, 3,
+ * 4). GQA maps q-head h to kv head h / group: page "MiniCPM5 Decode
+ * Megakernel - end-to-end build plan (handoff)", section 4.1, stage 5 of the
+ * per-layer list.
  *
  * Masks (allowed pairs; Lq == Lk == L in this version):
  *   SDPA_MASK_CAUSAL         j <= i

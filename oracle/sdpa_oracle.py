@@ -7,11 +7,11 @@ execute this module: only tests/, ``__graft_entry__.smoke()`` and the
 
 What is computed, and where the pages define it
 ------------------------------------------------
-* The forward keeps "the per-row softmax normalizer the backward reuses", the
-  logsumexp (page "Lab 028 lab detail: Off NVIDIA, you fix the platform
-  yourself", section "What I changed, in plain terms", item 1). The backward
-  recomputes the softmax probability P from the scores and that lse and forms
-  P and dS per element (same page, section "2026-10-21", "What the code says";
+* The forward keeps each row's logsumexp, the normalizer of its softmax, for
+  the backward to reuse (page "Lab 028 lab detail: Off NVIDIA, you fix the
+  platform yourself", section "What I changed, in plain terms", item 1). The
+  backward rebuilds P from the scores and that lse and forms P and dS per
+  element (same page, section "2026-10-21", "What the code says";
   page "Training - design (ORPO, flash-CCE head, prefix sharing, segmented
   backward)", section 6, which lists a fused backward that stores per-row LSE
   and recomputes P).
@@ -20,7 +20,7 @@ What is computed, and where the pages define it
   page, "Plan for the build", step 4, and "What I changed", items 3-4). With
   queries a suffix of the keys, ``diag_off = Lk - Lq``.
 * GQA: query head h reads kv head ``h // group`` (page "MiniCPM5 Decode
-  Megakernel - end-to-end build plan (handoff)", section 4, per-layer stage 5).
+  Megakernel - end-to-end build plan (handoff)", section 4.1, per-layer stage 5).
 
 The pages name these pieces but never print the gradient formulas, so the
 oracle writes out the textbook chain rule of the plain definition:

@@ -6,8 +6,7 @@
 Every HIP source is compiled with the packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops): the compiler would
 otherwise form v_pk_* fp32 ops on its own. The machine scheduler runs its
-ILP strategy (-amdgpu-sched-strategy=iterative-ilp). Float atomics are emitted as
-hardware atomics (-munsafe-fp-atomics), used for the fp32 dQ accumulator.
+ILP strategy (-amdgpu-sched-strategy=iterative-ilp). No kernel uses atomics.
 """
 from __future__ import annotations
 
@@ -36,7 +35,7 @@ def _hipcc():
 
 def common_flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # the ILP-oriented machine scheduler keeps more LDS reads in flight ahead of
         # their MFMAs in these one-wave-per-SIMD kernels (measured faster than default)

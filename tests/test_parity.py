@@ -224,6 +224,13 @@ def test_large_workloads_sampled(which):
     rel = (torch.linalg.norm(dv_sum - do_sum) / torch.linalg.norm(do_sum)).item()
     print("dV column-sum identity rel err", f"{rel:.2e}", flush=True)
     assert rel <= 1e-2
+    # and every dS row sums to zero, so sum_j dK_{g,j} = 0: measured against
+    # the size of dK (the backward's Delta comes from the bf16 O, so this only
+    # holds to bf16 rounding)
+    dk_sum = gpu["dK"].double().sum(dim=2)
+    rel_k = (torch.linalg.norm(dk_sum) / torch.linalg.norm(gpu["dK"].double())).item()
+    print("dK column-sum identity rel err", f"{rel_k:.2e}", flush=True)
+    assert rel_k <= 1e-2
 
 
 # ------------------------------------------------------------------ invariants on the GPU
@@ -247,10 +254,8 @@ def test_window_at_least_L_equals_causal_bitwise():
     a = run(w, inp)
     for W in (700, 701, 2**31 - 1):
         b = run(w.with_(mask=MASK_WINDOW, window=W), inp)
-        for n in ("O", "lse", "dK", "dV"):
+        for n in ("O", "lse", "dQ", "dK", "dV"):
             assert torch.equal(a[n], b[n]), (W, n)
-        # dQ goes through fp32 atomics whose order may vary: equal to rounding
-        assert rel_fro(_np(b["dQ"]), _np(a["dQ"])) <= 1e-5
 
 
 def test_masked_keys_do_not_change_outputs():
@@ -275,9 +280,9 @@ def test_determinism():
     inp = make_inputs(w)
     a = run(w, inp)
     b = run(w, inp)
-    for n in ("O", "lse", "dK", "dV"):
+    # no atomics anywhere: every output is bitwise reproducible
+    for n in ("O", "lse", "dQ", "dK", "dV"):
         assert torch.equal(a[n], b[n]), n
-    assert rel_fro(_np(a["dQ"]), _np(b["dQ"])) <= 1e-5
 
 
 def test_empty_sequence_is_a_no_op():
