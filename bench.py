@@ -42,6 +42,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def achievable_peak(torch, dev, ev, stream, n_wg=2048, iters=2048, reps=3):
+    """bf16 MFMA TFLOP/s this GPU sustains at its running clock (libsdpa_probe.so:
+    register-only MFMA chains, no memory traffic), median of `reps` launches."""
+    from sdpa_backward_amd import build
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    probe.sdpa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    probe.sdpa_probe_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    probe.sdpa_probe_mfma_bf16_flop.restype = ctypes.c_double
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    flop = probe.sdpa_probe_mfma_bf16_flop(n_wg, iters)
+    e = [ev.create() for _ in range(2 * reps)]
+    assert probe.sdpa_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), n_wg, iters, ctypes.c_void_p(stream)) == 0
+    for r in range(reps):
+        ev.record(e[2 * r], stream)
+        assert probe.sdpa_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), n_wg, iters, ctypes.c_void_p(stream)) == 0
+        ev.record(e[2 * r + 1], stream)
+    torch.cuda.synchronize()
+    ms = statistics.median(ev.ms(e[2 * r], e[2 * r + 1]) for r in range(reps))
+    return flop / (ms * 1e-3) / 1e12
+
+
 def allowed_pairs(w) -> int:
     """Allowed (i, j) pairs over all heads: causal L(L+1)/2, window W*L - W(W-1)/2 (L >= W)."""
     L = w.L
@@ -228,6 +249,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    peak_meas = achievable_peak(torch, dev, ev, stream)
+
     fwd_ms = [ev.ms(e[0], e[1]) for e in evs]
     bwd_ms = [ev.ms(e[1], e[4]) for e in evs]
     main_ms = [ev.ms(e[2], e[3]) for e in evs]
@@ -259,9 +282,11 @@ def main():
         "peak_mem_gb": round(peak / 1e9, 3),
         "peak_mem_above_inputs_gb": round((peak - in_bytes) / 1e9, 3),
         "phases": {
-            "fwd": {"ms_median": round(med(fwd_ms), 4), "tflops": round(fwd_flop / med(fwd_ms) / 1e9, 1)},
-            "bwd": {"ms_median": round(med(bwd_ms), 4), "tflops": round(bwd_flop / med(bwd_ms) / 1e9, 1)},
-            "bwd_dkdv_kernel": {"ms_median": round(med(main_ms), 4),
+            "fwd": {"ms_median": round(med(fwd_ms), 4), "ms_min": round(min(fwd_ms), 4),
+                    "tflops": round(fwd_flop / med(fwd_ms) / 1e9, 1)},
+            "bwd": {"ms_median": round(med(bwd_ms), 4), "ms_min": round(min(bwd_ms), 4),
+                    "tflops": round(bwd_flop / med(bwd_ms) / 1e9, 1)},
+            "bwd_dkdv_kernel": {"ms_median": round(med(main_ms), 4), "ms_min": round(min(main_ms), 4),
                                 "tflops_8DN": round(kv_flop / med(main_ms) / 1e9, 1)},
             "bwd_dq_pass": {"ms_median": round(med(bwd_ms) - med(main_ms), 4),
                             "tflops_6DN": round(6 * w.D * N / (med(bwd_ms) - med(main_ms)) / 1e9, 1)},
@@ -275,11 +300,16 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            "achievable_peak": round(peak_meas, 1),
+            "frac_of_achievable": round(achieved / peak_meas, 4),
+            "achievable_peak_note": "bf16 MFMA chains on registers at the running clock (libsdpa_probe.so)",
             "algorithmic_flop_per_launch": kv_flop,
             "algorithmic_unit": "8*D FLOP per allowed (query, key) pair (S, dP, dV, dK)",
             "avg_launch_ms": round(statistics.mean(main_ms), 4),
         },
     }
+    result["env"] = {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,
+                     "hip": getattr(torch.version, "hip", None), "arch": "gfx950"}
     if not a.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, cpu_inp, a.cpu_seconds)

@@ -23,6 +23,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
 SOURCES = ["sdpa_api.hip", "qs_bf16.hip", "kv_bf16.hip", "f32_valu.hip"]
+# measurement helper, its own library (include/sdpa_probe.h)
+PROBE_LIB = os.path.join(PKG, "libsdpa_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 ARCH = "gfx950"
 
 
@@ -60,21 +63,26 @@ def _compile(src, asm):
     return obj, msgs
 
 
-def build(asm: bool = False, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, asm), SOURCES))
-    objs = [o for o, _ in results]
-    if verbose:
-        for _, msgs in results:
-            for m in msgs:
-                print(m)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(asm: bool = False, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, asm), srcs)))
+    if verbose:
+        for _, msgs in results.values():
+            for m in msgs:
+                print(m)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

@@ -18,8 +18,8 @@ NONE, CAUSAL, WINDOW = 0, 1, 2
 FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sdpa_[a-z0-9_]+)\s*\(", text)))
 
@@ -37,6 +37,24 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_its_header():
+    from sdpa_backward_amd import build
+    path = build.PROBE_LIB
+    if not os.path.exists(path):
+        build.build()
+    probe = ctypes.CDLL(path)
+    names = header_functions(os.path.join(ROOT, "include", "sdpa_probe.h"))
+    assert names == ["sdpa_probe_mfma_bf16", "sdpa_probe_mfma_bf16_flop"], names
+    for n in names:
+        assert hasattr(probe, n), n
+    probe.sdpa_probe_mfma_bf16_flop.restype = ctypes.c_double
+    probe.sdpa_probe_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert probe.sdpa_probe_mfma_bf16_flop(10, 3) == 10 * 4 * 8 * 3 * 32768
+    probe.sdpa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert probe.sdpa_probe_mfma_bf16(None, 1, 1, None) == -1   # rejected before any launch
+    assert probe.sdpa_probe_mfma_bf16(ctypes.c_void_p(FAKE), 0, 1, None) == -1
 
 
 def test_version_and_status_strings(lib):
