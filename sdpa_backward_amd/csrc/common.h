@@ -231,6 +231,17 @@ struct TileLoader {
       voff[jj] = (uint32_t)(r * D + Tile<D>::slot(r, p % CPR) * 8) * 2;  // the slot map is an involution
     }
   }
+  // Resource covering rows [0, min(valid, R)) of the [R][D] tile starting at
+  // src (row stride D); valid <= 0 gives an empty range (loads read nothing).
+  SDPA_DEV static __amdgpu_buffer_rsrc_t rsrc_of(const bf16* src, int valid) {
+    const int rows = __builtin_amdgcn_readfirstlane(valid < 0 ? 0 : valid < R ? valid : R);  // uniform
+    return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
+  }
+  // This wave's block jj of a tile (jj < NJ, and jj * NW + w < PER).
+  SDPA_DEV void issue_one(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int jj, int w) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + (jj * NW + w) * 512),
+                                             16, (int)voff[jj], 0, 0, 0);
+  }
   // Rows [0, min(valid, R)) of the [R][D] tile starting at src (row stride D).
   SDPA_DEV void issue(bf16* lds, const bf16* src, int valid, int w) const {
     const int rows = valid < R ? valid : R;

@@ -147,11 +147,25 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int wr0 = iw0, wr1 = min(iw0 + 31, L - 1);  // this wave's rows (wr1 < wr0: none)
 
   auto step = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
-    if (kt + 1 <= kt_hi) {  // prefetch the next tile into the other buffers
-      const int jn = (kt + 1) * BK;
-      ld.issue(Kn, Kg + (size_t)jn * D, L - jn, w);
-      ld.issue(Vn, Vg + (size_t)jn * D, L - jn, w);
-    }
+    // The next tile's loads (into the other buffers) are issued one at a time
+    // between the score MFMAs below: issued back to back they stall the wave
+    // until the CU's vector-memory path has taken the workgroup's whole tile.
+    // Each load stays after the LDS reads that precede it in program order
+    // (it writes LDS), so the operand reads are software-pipelined by hand and
+    // the loads slot in between them. On the last tile the resources cover no
+    // rows and the loads read nothing.
+    const bool more = kt + 1 <= kt_hi;
+    const int jn = more ? (kt + 1) * BK : 0;
+    const auto krs = decltype(ld)::rsrc_of(Kg + (size_t)jn * D, more ? L - jn : 0);
+    const auto vrs = decltype(ld)::rsrc_of(Vg + (size_t)jn * D, more ? L - jn : 0);
+    constexpr int NJ = decltype(ld)::NJ;
+    auto load_one = [&, krs, vrs](int j) {  // j in [0, 2 NJ): K blocks, then V blocks
+      if constexpr (decltype(ld)::PER % C::NW != 0) {
+        if ((j % NJ) * C::NW + w >= decltype(ld)::PER) return;
+      }
+      if (j < NJ) ld.issue_one(Kn, krs, j, w);
+      else ld.issue_one(Vn, vrs, j - NJ, w);
+    };
 #pragma unroll
     for (int s = 0; s < NKS; s++) keep_in_agpr(qreg[s]);
 #pragma unroll
@@ -160,26 +174,33 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     const bool active = wr0 <= wr1 && j0 <= wr1 && j0 + BK - 1 > wr0 - w_eff;
     const bool full = j0 + BK - 1 <= wr0 && j0 > wr1 - w_eff && wr1 == wr0 + 31;
 
+    // Scores of every wave, also of waves whose rows miss this tile (they
+    // would only wait at the tile barrier): no branch around the MFMAs.
+    // Operand k (k < NM) is block mb = k / NKS, k-slice s = k % NKS; with
+    // dP (dQ pass) every k has two reads and two MFMAs.
     f32x16 st[NX];  // [0, NMB): S^T blocks; [NMB, 2 NMB): dP^T blocks (DQ)
 #pragma unroll
     for (int t = 0; t < NX; t++) st[t] = zero16();
-    if (active) {
+    {
+      constexpr int NM = NMB * NKS, AH = QS_AHEAD_S, NLD = 2 * NJ;
+      constexpr int EVERY = NM / NLD > 0 ? NM / NLD : 1;  // MFMA steps between loads
+      bf16x8 ka[AH], va[MODE == QS_DQ ? AH : 1];
+      auto rd = [&](int k) {
+        ka[k % AH] = op_direct<D>(Kc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
+        if constexpr (MODE == QS_DQ) va[k % AH] = op_direct<D>(Vc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
+      };
 #pragma unroll
-      for (int mb = 0; mb < NMB; mb++)
+      for (int k = 0; k < AH; k++) rd(k);
 #pragma unroll
-        for (int s = 0; s < NKS; s++) {
-          st[mb] = mfma(op_direct<D>(Kc, la, dw0 + 16 * s, 32 * mb), qreg[s], st[mb]);
-          if constexpr (MODE == QS_DQ)
-            st[NMB + mb] = mfma(op_direct<D>(Vc, la, dw0 + 16 * s, 32 * mb), dreg[s], st[NMB + mb]);
-        }
-      // schedule: LDS reads run QS_AHEAD_S MFMAs ahead
-      constexpr int RPS = MODE == QS_DQ ? 2 : 1;  // reads (and MFMAs) per step
-      __builtin_amdgcn_sched_group_barrier(0x100, QS_AHEAD_S * RPS, 0);
-#pragma unroll
-      for (int t = 0; t < NMB * NKS; t++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, RPS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+      for (int k = 0; k < NM; k++) {
+        const int mb = k / NKS, s = k % NKS;
+        st[mb] = mfma(ka[k % AH], qreg[s], st[mb]);
+        if constexpr (MODE == QS_DQ) st[NMB + mb] = mfma(va[k % AH], dreg[s], st[NMB + mb]);
+        if (k + AH < NM) rd(k + AH);
+        if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
       }
+#pragma unroll
+      for (int j = NM / EVERY; j < NLD; j++) load_one(j);  // (when there are more loads than MFMA steps)
     }
     if constexpr (C::DS == 2) exchange_add<NX>(st, xbuf, w, lane);
     if (!active) return;
