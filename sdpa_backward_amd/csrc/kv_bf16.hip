@@ -32,6 +32,10 @@ namespace sdpa {
 // produce both in one pass.
 enum { KV_BOTH = 0, KV_DV = 1, KV_DK = 2 };
 
+#ifndef KV_AHEAD
+#define KV_AHEAD 3  // S / dP operand reads issued this many MFMAs ahead
+#endif
+
 template <int D>
 struct KvCfg {
   static constexpr int NW = 4;
@@ -132,53 +136,90 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     qs = Q + off;
     ds = dO + off;
   };
+  // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta of them (rows
+  // clamped to L-1); one 4-byte global->LDS load per lane (wave 0 only)
+  auto load_rows = [&](int it, float* rv) {
+    const int hq = g * group + it / nq;
+    const int q0 = (qt_lo + it % nq) * C::BQ;
+    const int row = min(q0 + (lane & 31), L - 1);
+    const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * L + row;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
+  };
   auto issue = [&](int it, bf16* qd, bf16* dd, float* rv) {
     const bf16 *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
     ld.issue(qd, qs, L - q0, w);
     ld.issue(dd, ds, L - q0, w);
-    if (w == 0) {  // lanes 0..31: lse of rows q0.., lanes 32..63: Delta of rows q0.. (clamped to L-1)
-      const int hq = g * group + it / nq;
-      const int row = min(q0 + (lane & 31), L - 1);
-      const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * L + row;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
-    }
+    if (w == 0) load_rows(it, rv);
   };
 
-  auto compute = [&](int it, const bf16* Qc, const bf16* dOc, const float* rv) {
+  // One query tile. With PREFETCH the next tile's Q, dO (and lse, Delta) loads
+  // into (qn, dn, rvn) are issued one at a time between the S / dP MFMAs: in
+  // one burst they stall the wave until the CU's vector-memory path has taken
+  // them all. A load stays after the LDS reads that precede it in program
+  // order (it writes LDS), so the operand reads are software-pipelined by hand
+  // and the loads slot in between them. Past the last tile the resources cover
+  // no rows (nothing is read).
+  auto compute = [&](auto prefetch, int it, const bf16* Qc, const bf16* dOc, const float* rv, bf16* qn,
+                     bf16* dn, float* rvn) {
+    constexpr bool PF = decltype(prefetch)::value;
     const int q0 = (qt_lo + it % nq) * C::BQ;
     const int r1 = min(q0 + 31, L - 1);
     const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
     const bool full = kb0 + 31 <= q0 && kb0 > q0 + 31 - w_eff && q0 + 31 < L;
 
+    __amdgpu_buffer_rsrc_t qrs, drs;
+    if constexpr (PF) {
+      const bool more = it + 1 < total;
+      const bf16 *qs, *ds;
+      int q0n;
+      tile_src(more ? it + 1 : it, qs, ds, q0n);
+      qrs = decltype(ld)::rsrc_of(qs, more ? L - q0n : 0);
+      drs = decltype(ld)::rsrc_of(ds, more ? L - q0n : 0);
+      if (w == 0) load_rows(more ? it + 1 : it, rvn);
+    }
+    constexpr int NJ = decltype(ld)::NJ;
+    auto load_one = [&, qrs, drs](int j) {  // j in [0, 2 NJ): Q blocks, then dO blocks
+      if constexpr (decltype(ld)::PER % C::NW != 0) {
+        if ((j % NJ) * C::NW + w >= decltype(ld)::PER) return;
+      }
+      if (j < NJ) ld.issue_one(qn, qrs, j, w);
+      else ld.issue_one(dn, drs, j - NJ, w);
+    };
+
+    // S (all of it first, so exp(S) can start while the dP MFMAs run), then
+    // dP; computed by every wave (a wave whose keys miss this tile would only
+    // wait at the tile barrier): no branch around the MFMAs. MFMA step k < NKS
+    // is S with k-slice k, step NKS + k is dP with k-slice k.
     f32x16 s_acc = zero16(), dp_acc = zero16();
-    if (active) {
-      // all of S first, then dP: exp(S) can start while the dP MFMAs run
-#pragma unroll
-      for (int s = 0; s < NKS; s++) {
-        const int d0 = dw0 + 16 * s;
-        s_acc = mfma(op_direct<D>(Qc, la, d0, 0), op_direct<D>(ks, la, d0, 32 * kwi), s_acc);
-      }
-      if constexpr (WANT_DK) {
-#pragma unroll
-        for (int s = 0; s < NKS; s++)
-          dp_acc = mfma(op_direct<D>(dOc, la, dw0 + 16 * s, 0), vreg[s], dp_acc);
-      }
-      // schedule: LDS reads run ahead of the MFMAs that use them
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int s = 0; s < NKS; s++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      if constexpr (WANT_DK) {
-#pragma unroll
-        for (int s = 0; s < NKS; s++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    {
+      constexpr int NM = WANT_DK ? 2 * NKS : NKS, AH = KV_AHEAD, NLD = PF ? 2 * NJ : 0;
+      constexpr int EVERY = NLD > 0 && NM / NLD > 0 ? NM / NLD : 1;
+      bf16x8 ra[AH], rb[AH];
+      auto rd = [&](int k) {
+        if (k < NKS) {
+          ra[k % AH] = op_direct<D>(Qc, la, dw0 + 16 * k, 0);
+          rb[k % AH] = op_direct<D>(ks, la, dw0 + 16 * k, 32 * kwi);
+        } else {
+          ra[k % AH] = op_direct<D>(dOc, la, dw0 + 16 * (k - NKS), 0);
         }
+      };
+#pragma unroll
+      for (int k = 0; k < AH; k++) rd(k);
+#pragma unroll
+      for (int k = 0; k < NM; k++) {
+        if (k < NKS) s_acc = mfma(ra[k % AH], rb[k % AH], s_acc);
+        else if constexpr (WANT_DK) dp_acc = mfma(ra[k % AH], vreg[k - NKS], dp_acc);
+        if (k + AH < NM) rd(k + AH);
+        if constexpr (NLD > 0) {
+          if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
+        }
+      }
+      if constexpr (NLD > 0) {
+#pragma unroll
+        for (int j = NM / EVERY; j < NLD; j++) load_one(j);
       }
     }
     if constexpr (C::DS == 2) {
@@ -241,19 +282,17 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     issue(0, qb0, db0, rv0);
     wait_all_and_barrier();
     for (int it = 0; it < total; it += 2) {
-      if (it + 1 < total) issue(it + 1, qb1, db1, rv1);
-      compute(it, qb0, db0, rv0);
+      compute(std::true_type{}, it, qb0, db0, rv0, qb1, db1, rv1);
       wait_all_and_barrier();
       if (it + 1 >= total) break;
-      if (it + 2 < total) issue(it + 2, qb0, db0, rv0);
-      compute(it + 1, qb1, db1, rv1);
+      compute(std::true_type{}, it + 1, qb1, db1, rv1, qb0, db0, rv0);
       wait_all_and_barrier();
     }
   } else {
     for (int it = 0; it < total; it++) {
       issue(it, qb0, db0, rv0);
       wait_all_and_barrier();
-      compute(it, qb0, db0, rv0);
+      compute(std::false_type{}, it, qb0, db0, rv0, qb0, db0, rv0);
       wait_all_and_barrier();
     }
   }
