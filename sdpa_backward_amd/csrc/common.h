@@ -273,6 +273,18 @@ SDPA_DEV void wait_all_and_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Wait until at most VM of this wave's vector-memory loads are outstanding
+// (they complete in order, so the older ones have landed) and for its LDS
+// operations, then a workgroup barrier.
+template <int VM>
+SDPA_DEV void wait_vm_and_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));  // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Barrier for LDS-only hand-offs (no outstanding global loads are waited for).
 SDPA_DEV void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -74,7 +74,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   __shared__ __attribute__((aligned(16))) bf16 db1[C::NBUF == 2 ? QT : 8];
   __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * 1024 : 4];
   __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
-  __shared__ __attribute__((aligned(16))) float rv1[C::NBUF == 2 ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float rv1[64];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
@@ -155,6 +155,61 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     if (w == 0) load_rows(it, rv);
   };
 
+  // P = exp(S - lse), dS = P (dP - Delta) from the score tiles, then
+  // dV += P^T dO and dK += dS^T Q for the query tile whose rows start at q0.
+  auto form_and_update = [&](int q0, bool full, const float* rv, f32x16& s_acc, f32x16& dp_acc,
+                             const bf16* Qc, const bf16* dOc) {
+  // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
+  // tiles, as a select (the wave-uniform test stays outside the element loop)
+  // rows q0 + c_row(i, hh) vs this lane's key kj: in the band iff
+  // 0 <= q0 + c_row - kj < w_eff, and the row must exist (< L)
+  const int base = q0 + 4 * hh - kj, rowlim = L - q0 - 4 * hh;
+  auto form = [&](auto masked) {
+#pragma unroll
+    for (int blk = 0; blk < 4; blk++) {
+      const float4 l4 = *(const float4*)(rv + 8 * blk + 4 * hh);
+      const float4 d4 = *(const float4*)(rv + 32 + 8 * blk + 4 * hh);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int i = 4 * blk + r;
+        const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], scale_log2, -lv));
+        if constexpr (decltype(masked)::value) {
+          const int rr = 8 * blk + r;  // c_row(i, hh) - 4 hh
+          p = (uint32_t)(base + rr) < (uint32_t)w_eff && rr < rowlim ? p : 0.f;
+        }
+        s_acc[i] = p;
+        if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
+      }
+    }
+  };
+  if (full) form(std::false_type{});
+  else form(std::true_type{});
+  const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
+  const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
+  (void)pa0; (void)pa1; (void)da0; (void)da1;
+  constexpr int MPB = (WANT_DV ? 2 : 0) + (WANT_DK ? 2 : 0);  // MFMAs per head-dim block
+#pragma unroll
+  for (int d = 0; d < NDB; d++) {
+    const int c0 = dw0 + 32 * d;
+    if constexpr (WANT_DV) {
+      dvacc[d] = mfma(pa0, op_tr<D>(dOc, la, 0, c0), dvacc[d]);
+      dvacc[d] = mfma(pa1, op_tr<D>(dOc, la, 16, c0), dvacc[d]);
+    }
+    if constexpr (WANT_DK) {
+      dkacc[d] = mfma(da0, op_tr<D>(Qc, la, 0, c0), dkacc[d]);
+      dkacc[d] = mfma(da1, op_tr<D>(Qc, la, 16, c0), dkacc[d]);
+    }
+  }
+  // schedule: transposed reads run one head-dim block ahead of their MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
+#pragma unroll
+  for (int d = 0; d < NDB; d++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MPB, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
+  }
+  };
+
   // One query tile. With PREFETCH the next tile's Q, dO (and lse, Delta) loads
   // into (qn, dn, rvn) are issued one at a time between the S / dP MFMAs: in
   // one burst they stall the wave until the CU's vector-memory path has taken
@@ -227,55 +282,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
     }
     if (!active) return;
-    // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
-    // tiles, as a select (the wave-uniform test stays outside the element loop)
-    // rows q0 + c_row(i, hh) vs this lane's key kj: in the band iff
-    // 0 <= q0 + c_row - kj < w_eff, and the row must exist (< L)
-    const int base = q0 + 4 * hh - kj, rowlim = L - q0 - 4 * hh;
-    auto form = [&](auto masked) {
-#pragma unroll
-      for (int blk = 0; blk < 4; blk++) {
-        const float4 l4 = *(const float4*)(rv + 8 * blk + 4 * hh);
-        const float4 d4 = *(const float4*)(rv + 32 + 8 * blk + 4 * hh);
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int i = 4 * blk + r;
-          const float lv = (&l4.x)[r] * kLog2e, dv = (&d4.x)[r];
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], scale_log2, -lv));
-          if constexpr (decltype(masked)::value) {
-            const int rr = 8 * blk + r;  // c_row(i, hh) - 4 hh
-            p = (uint32_t)(base + rr) < (uint32_t)w_eff && rr < rowlim ? p : 0.f;
-          }
-          s_acc[i] = p;
-          if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
-        }
-      }
-    };
-    if (full) form(std::false_type{});
-    else form(std::true_type{});
-    const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
-    const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
-    (void)pa0; (void)pa1; (void)da0; (void)da1;
-    constexpr int MPB = (WANT_DV ? 2 : 0) + (WANT_DK ? 2 : 0);  // MFMAs per head-dim block
-#pragma unroll
-    for (int d = 0; d < NDB; d++) {
-      const int c0 = dw0 + 32 * d;
-      if constexpr (WANT_DV) {
-        dvacc[d] = mfma(pa0, op_tr<D>(dOc, la, 0, c0), dvacc[d]);
-        dvacc[d] = mfma(pa1, op_tr<D>(dOc, la, 16, c0), dvacc[d]);
-      }
-      if constexpr (WANT_DK) {
-        dkacc[d] = mfma(da0, op_tr<D>(Qc, la, 0, c0), dkacc[d]);
-        dkacc[d] = mfma(da1, op_tr<D>(Qc, la, 16, c0), dkacc[d]);
-      }
-    }
-    // schedule: transposed reads run one head-dim block ahead of their MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
-#pragma unroll
-    for (int d = 0; d < NDB; d++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, MPB, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
-    }
+    form_and_update(q0, full, rv, s_acc, dp_acc, Qc, dOc);
   };
 
   if constexpr (C::NBUF == 2) {
@@ -289,12 +296,89 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       wait_all_and_barrier();
     }
   } else {
-    for (int it = 0; it < total; it++) {
-      issue(it, qb0, db0, rv0);
-      wait_all_and_barrier();
-      compute(std::false_type{}, it, qb0, db0, rv0, qb0, db0, rv0);
-      wait_all_and_barrier();
+    // One Q and one dO buffer (two of each do not fit at D = 512). Each is
+    // refilled as soon as every wave is done with it, so its load has part of
+    // a tile's work to land instead of stalling the next tile:
+    //   dV pass: Q(t) feeds only the S MFMAs and dO(t) only the dV MFMAs, so
+    //     Q(t+1) loads after the S exchange and dO(t+1) after the dV MFMAs.
+    //   dK pass: Q(t) feeds S and dK, dO(t) only dP; the two buffers swap roles
+    //     every tile: Q(t+1) loads into dO(t)'s buffer after the exchanges,
+    //     dO(t+1) into Q(t)'s buffer after the dK MFMAs.
+    // A wave's loads complete in order, so "Q landed, dO may still be in
+    // flight" is vmcnt(NJ): at most one tile's worth of this wave's loads
+    // outstanding (wave 0's extra lse/Delta load rides with the Q tile).
+    constexpr int NJ = decltype(ld)::NJ;
+    auto issue_q = [&](int it, bool more, bf16* dst, float* rvd) {
+      const bf16 *qs, *ds;
+      int q0n;
+      tile_src(it, qs, ds, q0n);
+      ld.issue(dst, qs, more ? L - q0n : 0, w);
+      if (w == 0) load_rows(it, rvd);
+    };
+    auto issue_do = [&](int it, bool more, bf16* dst) {
+      const bf16 *qs, *ds;
+      int q0n;
+      tile_src(it, qs, ds, q0n);
+      ld.issue(dst, ds, more ? L - q0n : 0, w);
+    };
+    // S, then (dK pass) dP once dO has landed; operand reads pipelined by hand
+    auto sdp = [&](const bf16* Qc, const bf16* dOc, f32x16& s_acc, f32x16& dp_acc) {
+      constexpr int AH = KV_AHEAD;
+      bf16x8 ra[AH], rb[AH];
+      s_acc = zero16();
+      dp_acc = zero16();
+#pragma unroll
+      for (int k = 0; k < AH; k++) {
+        ra[k] = op_direct<D>(Qc, la, dw0 + 16 * k, 0);
+        rb[k] = op_direct<D>(ks, la, dw0 + 16 * k, 32 * kwi);
+      }
+#pragma unroll
+      for (int k = 0; k < NKS; k++) {
+        s_acc = mfma(ra[k % AH], rb[k % AH], s_acc);
+        if (k + AH < NKS) {
+          ra[k % AH] = op_direct<D>(Qc, la, dw0 + 16 * (k + AH), 0);
+          rb[k % AH] = op_direct<D>(ks, la, dw0 + 16 * (k + AH), 32 * kwi);
+        }
+      }
+      if constexpr (WANT_DK) {
+        wait_vm_and_barrier<0>();  // dO(t) in every wave's part of the buffer
+#pragma unroll
+        for (int k = 0; k < AH; k++) ra[k] = op_direct<D>(dOc, la, dw0 + 16 * k, 0);
+#pragma unroll
+        for (int k = 0; k < NKS; k++) {
+          dp_acc = mfma(ra[k % AH], vreg[k], dp_acc);
+          if (k + AH < NKS) ra[k % AH] = op_direct<D>(dOc, la, dw0 + 16 * (k + AH), 0);
+        }
+      }
+    };
+    auto tile = [&](int it, bf16* Qb, bf16* Db, float* rvc, float* rvn) {
+      const int q0 = (qt_lo + it % nq) * C::BQ;
+      const int r1 = min(q0 + 31, L - 1);
+      const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
+      const bool full = kb0 + 31 <= q0 && kb0 > q0 + 31 - w_eff && q0 + 31 < L;
+      const bool more = it + 1 < total;
+      const int itn = more ? it + 1 : it;
+      wait_vm_and_barrier<NJ>();  // Q(t) and lse/Delta(t) landed (dO(t) may not have)
+      f32x16 s_acc, dp_acc;
+      sdp(Qb, Db, s_acc, dp_acc);
+      kv_exchange_add(s_acc, xbuf, w, lane);
+      if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
+      // dV pass: Q(t)'s buffer is free; dK pass: dO(t)'s buffer is free
+      issue_q(itn, more, WANT_DK ? Db : Qb, rvn);
+      if constexpr (!WANT_DK) wait_vm_and_barrier<NJ>();  // dO(t) landed (Q(t+1) may not have)
+      if (active) form_and_update(q0, full, rvc, s_acc, dp_acc, Qb, Db);
+      lds_barrier();  // every wave is done with the buffer refilled next
+      issue_do(itn, more, WANT_DK ? Qb : Db);
+    };
+    issue_q(0, true, qb0, rv0);
+    issue_do(0, true, db0);
+    for (int it = 0; it < total; it += 2) {
+      tile(it, qb0, db0, rv0, rv1);
+      if (it + 1 >= total) break;
+      if constexpr (WANT_DK) tile(it + 1, db0, qb0, rv1, rv0);
+      else tile(it + 1, qb0, db0, rv1, rv0);
     }
+    wait_all_and_barrier();  // (the last no-op loads)
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
