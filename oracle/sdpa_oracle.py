@@ -17,8 +17,13 @@ What is computed, and where the pages define it
   and recomputes P).
 * Masks: above the causal diagonal P is zero; a window additionally zeroes P
   where the key index is below ``i + diag_off - window_size + 1`` (Lab 028
-  page, "Plan for the build", step 4, and "What I changed", items 3-4). With
-  queries a suffix of the keys, ``diag_off = Lk - Lq``.
+  page, "Plan for the build", step 4, and "What I changed", items 3-4). A
+  window without the causal mask is read as a band on both sides of the
+  query's diagonal: a key at distance ``window_size`` or more from it, ahead
+  or behind, is masked (same page, "What I changed", items 3 and 4, where the
+  non-causal window also drops the tiles wholly ahead). With queries a suffix of the keys,
+  ``diag_off = Lk - Lq`` (same page, item 5(b), and the parity cases with
+  ``qL < kL``). No mask: every key.
 * GQA: query head h reads kv head ``h // group`` (page "MiniCPM5 Decode
   Megakernel - end-to-end build plan (handoff)", section 4.1, per-layer stage 5).
 
@@ -42,54 +47,65 @@ rows x every key). Softmax rows are independent, so row blocking changes no
 value; nothing else is blocked, fused or reordered.
 
 Readings where the pages are silent: lse uses the natural log; a row with no
-allowed key (impossible for Lq == Lk) gets lse = -inf, O = 0 and zero
-gradients; ``window >= Lk`` is identical to plain causal.
+allowed key (possible only when Lq > Lk under a causal mask, or with no keys
+at all) gets lse = -inf, O = 0 and zero gradients; ``window >= Lk`` is
+identical to plain causal, and a two-sided window of at least Lq + Lk keys is
+identical to no mask.
 
 Pins: tests/test_oracle.py checks this module against central finite
-differences, an independent float64 autograd of the plain forward, the
-library SDPA routine, pure-Python brute force on tiny inputs, a hand-derived
-worked example and exact invariants.
+differences, an independent float64 autograd of the plain forward (its mask
+built from torch's tril/triu), the library SDPA routine (causal, no mask, and
+its lower-right causal bias for queries that are a suffix of the keys),
+pure-Python brute force on tiny inputs, a hand-derived worked example and
+exact invariants.
 """
 from __future__ import annotations
 
 import numpy as np
 
-MASKS = ("none", "causal", "causal_window")
+MASKS = ("none", "causal", "causal_window", "window")
 
 
-def allowed_block(rows: np.ndarray, Lk: int, mask: str, window: int, diag_off: int) -> np.ndarray:
-    """Boolean [len(rows), Lk]: True where query row i may attend key j.
+def allowed(i, j, Lq: int, Lk: int, mask: str, window: int):
+    """True where query row i may attend key j (numpy broadcasting over i, j).
 
-    causal:        j <= i + diag_off
-    causal_window: additionally j >= i + diag_off - window + 1
-    none:          every key
+    With d = i + diag_off - j, diag_off = Lk - Lq (the query's diagonal sits
+    diag_off keys to the right of its row index):
+      none:          every key
+      causal:        d >= 0
+      causal_window: 0 <= d < window
+      window:        -window < d < window   (both sides, diagonal included)
+    Keys outside [0, Lk) and rows outside [0, Lq) do not exist.
     """
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
-    j = np.arange(Lk)[None, :]
-    i = np.asarray(rows)[:, None]
-    if mask == "none":
-        return np.ones((len(rows), Lk), dtype=bool)
-    ok = j <= i + diag_off
-    if mask == "causal_window":
-        if window < 1:
-            raise ValueError("window must be >= 1")
-        ok &= j >= i + diag_off - window + 1
+    if mask in ("causal_window", "window") and window < 1:
+        raise ValueError("window must be >= 1")
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    ok = (i >= 0) & (i < Lq) & (j >= 0) & (j < Lk)
+    d = i + (Lk - Lq) - j
+    if mask == "causal":
+        ok = ok & (d >= 0)
+    elif mask == "causal_window":
+        ok = ok & (d >= 0) & (d < window)
+    elif mask == "window":
+        ok = ok & (d > -window) & (d < window)
     return ok
+
+
+def allowed_block(rows: np.ndarray, Lq: int, Lk: int, mask: str, window: int) -> np.ndarray:
+    """Boolean [len(rows), Lk]: the allowed pairs of these query rows."""
+    return allowed(np.asarray(rows)[:, None], np.arange(Lk)[None, :], Lq, Lk, mask, window)
 
 
 def rows_attending(keys, Lq: int, Lk: int, mask: str, window: int) -> np.ndarray:
     """Sorted query rows that attend at least one of ``keys`` (for sampled key gradients)."""
-    diag_off = Lk - Lq
-    keys = np.asarray(keys)
-    rows = set()
-    for j in keys:
-        if mask == "none":
-            return np.arange(Lq)
-        lo = max(0, int(j) - diag_off)
-        hi = Lq - 1 if mask == "causal" else min(Lq - 1, int(j) - diag_off + window - 1)
-        rows.update(range(lo, hi + 1))
-    return np.array(sorted(rows), dtype=np.int64)
+    rows = np.arange(Lq)
+    hit = np.zeros(Lq, dtype=bool)
+    for j in np.asarray(keys):
+        hit |= allowed(rows, int(j), Lq, Lk, mask, window)
+    return rows[hit]
 
 
 def _softmax_rows(S: np.ndarray, ok: np.ndarray):
@@ -117,7 +133,7 @@ def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True):
     """
     Lq, Lk = q_h.shape[0], k_g.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    ok = allowed_block(rows, Lk, mask, window, Lk - Lq)
+    ok = allowed_block(rows, Lq, Lk, mask, window)
     qb = q_h[rows]
     S = scale * (qb @ k_g.T)
     P, lse = _softmax_rows(S, ok)

@@ -49,17 +49,31 @@ def pin_golden(mod, tol=1e-14):
 
 
 def brute_forward(q, k, v, scale, mask, window):
-    """O and lse from the definition with Python loops and math.exp (no numpy linear algebra)."""
-    B, Hq, L, D = q.shape
-    Hkv = k.shape[1]
+    """O and lse from the definition with Python loops and math.exp (no numpy linear algebra).
+
+    Query row i sits at key position i + Lk - Lq (queries are the last Lq of
+    the Lk positions); a row with no allowed key gets O = 0, lse = -inf."""
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
     group = Hq // Hkv
-    O = np.zeros((B, Hq, L, D))
-    lse = np.zeros((B, Hq, L))
+    O = np.zeros((B, Hq, Lq, D))
+    lse = np.zeros((B, Hq, Lq))
     for b in range(B):
         for h in range(Hq):
             g = h // group
-            for i in range(L):
-                keys = [j for j in range(L) if j <= i and (mask == "causal" or j > i - window)]
+            for i in range(Lq):
+                pos = i + Lk - Lq
+                if mask == "none":
+                    keys = list(range(Lk))
+                elif mask == "causal":
+                    keys = [j for j in range(Lk) if j <= pos]
+                elif mask == "causal_window":
+                    keys = [j for j in range(Lk) if pos - window < j <= pos]
+                else:  # "window": both sides of the diagonal
+                    keys = [j for j in range(Lk) if abs(j - pos) < window]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
                 s = [scale * sum(float(q[b, h, i, d]) * float(k[b, g, j, d]) for d in range(D)) for j in keys]
                 mx = max(s)
                 z = sum(math.exp(x - mx) for x in s)
@@ -69,35 +83,54 @@ def brute_forward(q, k, v, scale, mask, window):
     return O, lse
 
 
-def tiny_inputs(Hq, Hkv, L, D, seed):
+def tiny_inputs(Hq, Hkv, L, D, seed, Lk=None):
+    """Seeded N(0, 1) fp64 inputs; L query rows and Lk (default L) keys."""
+    Lk = L if Lk is None else Lk
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((1, Hq, L, D))
-    k = rng.standard_normal((1, Hkv, L, D))
-    v = rng.standard_normal((1, Hkv, L, D))
+    k = rng.standard_normal((1, Hkv, Lk, D))
+    v = rng.standard_normal((1, Hkv, Lk, D))
     do = rng.standard_normal((1, Hq, L, D))
     return q, k, v, do
 
 
+# Hq, Hkv, Lq, Lk, D, scale, mask, window
+BRUTE_CASES = [
+    (2, 1, 7, 7, 3, 0.7, "causal", 0),
+    (4, 2, 9, 9, 4, 1.0, "causal_window", 3),
+    (2, 2, 6, 6, 2, 3.0, "causal_window", 1),
+    (3, 1, 5, 5, 5, 0.45, "causal_window", 2),
+    (2, 1, 6, 6, 3, 0.9, "none", 0),
+    (2, 2, 8, 8, 3, 0.8, "window", 3),
+    (2, 1, 4, 9, 3, 0.6, "causal", 0),          # queries the last 4 of 9 positions
+    (2, 1, 5, 11, 2, 1.1, "causal_window", 3),
+    (2, 1, 4, 10, 3, 0.5, "window", 2),
+    (2, 1, 3, 7, 2, 0.7, "none", 0),
+    (2, 1, 9, 4, 3, 0.8, "causal", 0),          # more queries than keys: the first rows see nothing
+    (2, 2, 8, 5, 2, 1.3, "window", 2),
+]
+
+
 def pin_brute(mod, cases=None):
-    """Max abs error of oracle O/lse against brute force over a few tiny cases."""
-    cases = cases or [
-        (2, 1, 7, 3, 0.7, "causal", 0),
-        (4, 2, 9, 4, 1.0, "causal_window", 3),
-        (2, 2, 6, 2, 3.0, "causal_window", 1),
-        (3, 1, 5, 5, 0.45, "causal_window", 2),
-    ]
+    """Max abs error of oracle O/lse against brute force over a few tiny cases (lse -inf must match)."""
+    cases = cases or BRUTE_CASES
     worst = 0.0
-    for n, (Hq, Hkv, L, D, s, mask, W) in enumerate(cases):
-        q, k, v, _ = tiny_inputs(Hq, Hkv, L, D, 100 + n)
+    for n, (Hq, Hkv, Lq, Lk, D, s, mask, W) in enumerate(cases):
+        q, k, v, _ = tiny_inputs(Hq, Hkv, Lq, D, 100 + n, Lk)
         O, lse = mod.sdpa_forward(q, k, v, s, mask, W)
         Ob, lb = brute_forward(q, k, v, s, mask, W)
-        worst = max(worst, float(np.max(np.abs(O - Ob))), float(np.max(np.abs(lse - lb))))
+        if not np.all(np.isfinite(O)):
+            return math.inf
+        fin = np.isfinite(lb)
+        if not np.array_equal(np.isfinite(lse), fin) or np.any(lse[~fin] != lb[~fin]):
+            return math.inf
+        worst = max(worst, float(np.max(np.abs(O - Ob))), float(np.max(np.abs(lse[fin] - lb[fin]), initial=0.0)))
     return worst
 
 
-def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0):
+def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None):
     """max|FD - analytic| / max|analytic| over every coordinate of Q, K and V."""
-    q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed)
+    q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed, Lk)
     res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
     grads = {"q": res["dQ"], "k": res["dK"], "v": res["dV"]}
 
@@ -152,20 +185,34 @@ def fd_directional_error(mod, Hq, Hkv, L, D, scale, mask, window, ndir=16, seed=
     return worst
 
 
+def torch_mask(Lq, Lk, mask, window):
+    """Allowed pairs [Lq, Lk] built from torch's own band routines: tril keeps
+    j <= i + diagonal and triu keeps j >= i + diagonal, with the diagonal moved
+    Lk - Lq to the right (queries are the last Lq key positions)."""
+    ones = torch.ones(Lq, Lk, dtype=torch.bool)
+    off = Lk - Lq
+    if mask == "none":
+        return ones
+    if mask == "causal":
+        return torch.tril(ones, diagonal=off)
+    if mask == "causal_window":
+        return torch.tril(ones, diagonal=off) & torch.triu(ones, diagonal=off - window + 1)
+    if mask == "window":
+        return torch.tril(ones, diagonal=off + window - 1) & torch.triu(ones, diagonal=off - window + 1)
+    raise ValueError(mask)
+
+
 def torch_plain(q, k, v, do, scale, mask, window):
-    """float64 autograd of the plain forward: matmul -> -inf mask -> softmax -> matmul."""
+    """float64 autograd of the plain forward: matmul -> -inf mask -> softmax -> matmul
+    (every row must have an allowed key)."""
     q = torch.tensor(q, dtype=torch.float64, requires_grad=True)
     k = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     v = torch.tensor(v, dtype=torch.float64, requires_grad=True)
     group = q.shape[1] // k.shape[1]
     kk = k.repeat_interleave(group, dim=1)
     vv = v.repeat_interleave(group, dim=1)
-    L, Lk = q.shape[2], k.shape[2]
-    i = torch.arange(L)[:, None]
-    j = torch.arange(Lk)[None, :]
-    ok = j <= i + (Lk - L)
-    if mask == "causal_window":
-        ok = ok & (j > i + (Lk - L) - window)
+    ok = torch_mask(q.shape[2], k.shape[2], mask, window)
+    assert bool(ok.any(dim=1).all()), "a row with no allowed key"
     S = scale * torch.matmul(q, kk.transpose(-1, -2).contiguous())
     S = S.masked_fill(~ok, float("-inf"))
     lse = torch.logsumexp(S, dim=-1)

@@ -46,6 +46,20 @@ FD_CASES = [
     (4, 1, 16, 4, 0.5, "causal_window", 16),
     (1, 1, 7, 8, 1.0, "causal_window", 14),
     (4, 2, 16, 8, 1.0, "causal_window", 5),
+    (2, 1, 7, 4, 0.5, "none", 0),
+    (2, 2, 13, 4, 1.0, "window", 1),
+    (4, 2, 13, 4, 0.8, "window", 3),
+    (2, 1, 16, 8, 3.0, "window", 16),
+]
+# queries the last Lq of Lk positions, and more queries than keys
+FD_CASES_QK = [
+    # Hq, Hkv, Lq, Lk, D, scale, mask, window
+    (2, 1, 5, 13, 4, 0.7, "causal", 0),
+    (2, 2, 7, 16, 4, 1.0, "causal_window", 3),
+    (2, 1, 4, 13, 4, 0.9, "window", 3),
+    (2, 1, 6, 9, 4, 0.6, "none", 0),
+    (2, 1, 13, 7, 4, 0.8, "causal", 0),
+    (2, 1, 13, 7, 4, 1.1, "window", 2),
 ]
 
 
@@ -53,6 +67,12 @@ FD_CASES = [
 def test_finite_differences_exhaustive(case):
     Hq, Hkv, L, D, s, mask, W = case
     assert pins.fd_error(sdpa_oracle, Hq, Hkv, L, D, s, mask, W) <= 1e-7
+
+
+@pytest.mark.parametrize("case", FD_CASES_QK, ids=[str(c) for c in FD_CASES_QK])
+def test_finite_differences_exhaustive_lq_ne_lk(case):
+    Hq, Hkv, Lq, Lk, D, s, mask, W = case
+    assert pins.fd_error(sdpa_oracle, Hq, Hkv, Lq, D, s, mask, W, Lk=Lk) <= 1e-7
 
 
 @pytest.mark.parametrize("mask,window", [("causal", 0), ("causal_window", 40)])
@@ -81,6 +101,22 @@ def test_autograd_independent(which, shrink):
     assert err <= 1e-12, err
 
 
+@pytest.mark.parametrize("Lq,Lk,mask,window", [
+    (300, 300, "none", 0),
+    (300, 300, "window", 64),
+    (200, 700, "causal", 0),
+    (200, 700, "causal_window", 96),
+    (200, 700, "window", 96),
+    (150, 400, "none", 0),
+    (700, 200, "none", 0),
+    (500, 260, "window", 300),
+])
+def test_autograd_independent_more_masks(Lq, Lk, mask, window):
+    q, k, v, do = pins.tiny_inputs(4, 2, Lq, 32, 77, Lk)
+    err = pins.autograd_error(sdpa_oracle, q, k, v, do, 32 ** -0.5, mask, window)
+    assert err <= 1e-12, err
+
+
 def test_library_sdpa_forward():
     import torch.nn.functional as F
     for which, shrink in ((0, {}), (1, {"L": 1024}), (3, {"Hq": 4, "Hkv": 2, "L": 700, "window": 100})):
@@ -101,9 +137,97 @@ def test_library_sdpa_forward():
             assert pins.rel_fro(O, ref2.numpy()) <= 1e-12
 
 
+def test_library_sdpa_no_mask_and_lower_right_causal():
+    # no mask: the library routine with no attention mask at all; queries as a
+    # suffix of the keys: the library's lower-right causal bias
+    import warnings
+
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    for Lq, Lk in ((100, 100), (60, 250), (250, 60)):
+        q, k, v, _ = pins.tiny_inputs(4, 2, Lq, 16, 78, Lk)
+        tq, tk, tv = torch.tensor(q), torch.tensor(k), torch.tensor(v)
+        O, _ = oracle.sdpa_forward(q, k, v, 0.3, "none", 0)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, scale=0.3, enable_gqa=True)
+        assert pins.rel_fro(O, ref.numpy()) <= 1e-12
+        if Lq <= Lk:
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                bias = causal_lower_right(Lq, Lk)._materialize("cpu")
+            O, _ = oracle.sdpa_forward(q, k, v, 0.3, "causal", 0)
+            rep = lambda x: x.repeat_interleave(2, dim=1)
+            ref = F.scaled_dot_product_attention(tq, rep(tk), rep(tv), attn_mask=bias, scale=0.3)
+            assert pins.rel_fro(O, ref.numpy()) <= 1e-12
+
+
 # ---------------------------------------------------------------- invariants
-def _rand(Hq=4, Hkv=2, L=37, D=8, seed=5):
-    return pins.tiny_inputs(Hq, Hkv, L, D, seed)
+def _rand(Hq=4, Hkv=2, L=37, D=8, seed=5, Lk=None):
+    return pins.tiny_inputs(Hq, Hkv, L, D, seed, Lk)
+
+
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("causal_window", 7), ("window", 5), ("none", 0)])
+def test_queries_as_suffix_of_keys(mask, window):
+    # Lq < Lk: query row i is row i + Lk - Lq of the square problem over all Lk
+    # positions; its outputs are that row's, and dK/dV are the square problem's
+    # with dO zero on the rows that are not queries.
+    Lq, Lk = 11, 30
+    q, k, v, do = _rand(L=Lk, seed=21)
+    do_sq = do.copy()
+    do_sq[:, :, : Lk - Lq] = 0.0
+    sq = oracle.sdpa_fwd_bwd(q, k, v, do_sq, 0.7, mask, window)
+    sub = oracle.sdpa_fwd_bwd(q[:, :, Lk - Lq:], k, v, do[:, :, Lk - Lq:], 0.7, mask, window)
+    for n in ("O", "lse", "dQ"):
+        assert np.max(np.abs(sub[n] - sq[n][:, :, Lk - Lq:])) <= 1e-13, n
+    for n in ("dK", "dV"):
+        assert np.max(np.abs(sub[n] - sq[n])) <= 1e-13, n
+
+
+def test_more_queries_than_keys_leaves_rows_empty():
+    # Lq > Lk under a causal mask: the first Lq - Lk rows have no key at or
+    # before their position; they get O = 0, lse = -inf and contribute nothing
+    Lq, Lk = 20, 8
+    q, k, v, do = _rand(L=Lq, Lk=Lk, seed=22)
+    res = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, "causal", 0)
+    e = Lq - Lk
+    assert np.all(res["lse"][:, :, :e] == -np.inf) and np.all(np.isfinite(res["lse"][:, :, e:]))
+    assert np.all(res["O"][:, :, :e] == 0) and np.all(res["dQ"][:, :, :e] == 0)
+    tail = oracle.sdpa_fwd_bwd(q[:, :, e:], k, v, do[:, :, e:], 0.7, "causal", 0)
+    for n in ("dK", "dV"):
+        assert np.array_equal(res[n], tail[n]), n
+
+
+def test_two_sided_window_is_time_reversal_symmetric():
+    # reversing the order of the positions maps the band |i - j| < W onto itself
+    q, k, v, do = _rand(L=29, seed=23)
+    f = lambda x: x[:, :, ::-1].copy()
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, "window", 6)
+    b = oracle.sdpa_fwd_bwd(f(q), f(k), f(v), f(do), 0.8, "window", 6)
+    for n in ("O", "lse", "dQ", "dK", "dV"):
+        assert np.max(np.abs(f(b[n]) - a[n])) <= 1e-13, n   # axis 2 is the position axis of every tensor
+    # the causal window is not symmetric: its reversal looks ahead instead
+    c = oracle.sdpa_fwd_bwd(f(q), f(k), f(v), f(do), 0.8, "causal_window", 6)
+    d = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, "causal_window", 6)
+    assert np.max(np.abs(f(c["O"]) - d["O"])) > 1e-3
+
+
+@pytest.mark.parametrize("Lq,Lk", [(37, 37), (20, 37), (37, 20)])
+def test_wide_two_sided_window_is_no_mask_bitwise(Lq, Lk):
+    q, k, v, do = _rand(L=Lq, Lk=Lk, seed=24)
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, "none", 0)
+    for W in (Lq + Lk, 2**31 - 1):
+        b = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, "window", W)
+        for n in a:
+            assert np.array_equal(a[n], b[n]), (W, n)
+
+
+def test_window_one_is_self_for_both_window_kinds():
+    q, k, v, do = _rand(L=15, Lk=24, seed=25)
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 1.2, "causal_window", 1)
+    b = oracle.sdpa_fwd_bwd(q, k, v, do, 1.2, "window", 1)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+    g = np.repeat(np.arange(2), 2)
+    assert np.array_equal(a["O"][0], v[0, g, 24 - 15:])
 
 
 def test_softmax_rows_sum_to_one():
@@ -216,15 +340,18 @@ def test_row_blocking_changes_nothing():
         assert np.max(np.abs(a[n] - b[n])) <= 1e-13
 
 
-def test_sampled_rows_and_keys_match_full():
-    q, k, v, do = _rand(Hq=4, Hkv=2, L=60)
-    for mask, W in (("causal", 0), ("causal_window", 11)):
+@pytest.mark.parametrize("Lq,Lk", [(60, 60), (45, 80), (80, 45)])
+def test_sampled_rows_and_keys_match_full(Lq, Lk):
+    q, k, v, do = _rand(Hq=4, Hkv=2, L=Lq, Lk=Lk)
+    for mask, W in (("causal", 0), ("causal_window", 11), ("window", 9), ("none", 0)):
         full = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, mask, W)
-        rows = np.array([0, 13, 59])
+        rows = np.array([0, 13, Lq - 1])
         r = oracle.sampled_rows(q, k, v, do, 0.7, mask, W, 0, 3, rows)
         for n in ("O", "lse", "dQ"):
-            assert np.max(np.abs(r[n] - full[n][0, 3, rows])) <= 1e-13
-        keys = np.array([0, 30, 59])
+            assert np.array_equal(np.isfinite(r[n]), np.isfinite(full[n][0, 3, rows]))
+            fin = np.isfinite(r[n])
+            assert np.max(np.abs(r[n][fin] - full[n][0, 3, rows][fin])) <= 1e-13
+        keys = np.array([0, 30, Lk - 1])
         kk = oracle.sampled_keys(q, k, v, do, 0.7, mask, W, 0, 1, keys, row_block=17)
         for n in ("dK", "dV"):
             assert np.max(np.abs(kk[n] - full[n][0, 1, keys])) <= 1e-12
@@ -239,8 +366,13 @@ MUTATIONS = [
     ('out["dQ"] = scale * (dS @ k_g)', 'out["dQ"] = scale * (dS @ v_g)'),           # wrong operand
     ('out["dV"] = P.T @ dob', 'out["dV"] = dS.T @ dob'),                             # P vs dS
     ("dP = dob @ v_g.T", "dP = dob @ k_g.T"),                                        # wrong operand
-    ("ok &= j >= i + diag_off - window + 1", "ok &= j > i + diag_off - window + 1"),  # window off by one
-    ("ok = j <= i + diag_off", "ok = j < i + diag_off"),                             # diagonal excluded
+    ("ok = ok & (d >= 0) & (d < window)", "ok = ok & (d >= 0) & (d <= window)"),     # window off by one
+    ("ok = ok & (d >= 0)\n", "ok = ok & (d > 0)\n"),                                # diagonal excluded
+    ("ok = ok & (d > -window) & (d < window)", "ok = ok & (d >= -window) & (d < window)"),  # two-sided, one too many
+    ("ok = ok & (d > -window) & (d < window)", "ok = ok & (d >= 0) & (d < window)"),  # two-sided read as causal
+    ("d = i + (Lk - Lq) - j", "d = i + (Lq - Lk) - j"),                              # diagonal offset sign
+    ("d = i + (Lk - Lq) - j", "d = i - j"),                                          # top-left alignment
+    ("nonempty = tot > 0", "nonempty = tot >= 0"),                                   # empty rows -> NaN
     ("g = h // group\n            for r0 in range(0, Lq, row_block):\n                rows = np.arange(r0, min(Lq, r0 + row_block))\n                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h]",
      "g = h % Hkv\n            for r0 in range(0, Lq, row_block):\n                rows = np.arange(r0, min(Lq, r0 + row_block))\n                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h]"),  # GQA map
     ("lse = m_safe + np.log(tot)", "lse = m_safe + np.log(tot + 1e-3)"),          # wrong normaliser
@@ -259,18 +391,19 @@ def _mutant(old, new):
 def _pins_catch(mod):
     failures = []
     try:
-        if pins.pin_golden(mod) > 1e-14:
+        if not pins.pin_golden(mod) <= 1e-14:
             failures.append("golden")
     except Exception:
         failures.append("golden-raised")
     try:
-        if pins.pin_brute(mod) > 1e-12:
+        if not pins.pin_brute(mod) <= 1e-12:
             failures.append("brute")
     except Exception:
         failures.append("brute-raised")
-    for case in [(4, 2, 9, 4, 0.8, "causal_window", 3), (2, 1, 7, 4, 0.5, "causal", 0)]:
+    for case in [(4, 2, 9, 4, 0.8, "causal_window", 3), (2, 1, 7, 4, 0.5, "causal", 0),
+                 (2, 1, 5, 3, 0.8, "window", 2, 0, 9)]:
         try:
-            if pins.fd_error(mod, *case) > 1e-7:
+            if not pins.fd_error(mod, *case) <= 1e-7:
                 failures.append(f"fd{case}")
         except Exception:
             failures.append("fd-raised")
