@@ -63,15 +63,25 @@ def achievable_peak(torch, dev, ev, stream, n_wg=2048, iters=2048, reps=3):
     return flop / (ms * 1e-3) / 1e12
 
 
+def row_key_counts(w, rows):
+    """Allowed keys of each query row in ``rows`` (the queries are the last L of Lk positions)."""
+    import numpy as np
+
+    Lq, Lk, W = w.L, w.Lkv, w.window
+    pos = np.asarray(rows, dtype=np.int64) + (Lk - Lq)   # the row's diagonal key
+    lo, hi = np.zeros_like(pos), np.full_like(pos, Lk - 1)
+    if w.mask in ("causal", "causal_window", "window"):
+        hi = np.minimum(hi, pos + (W - 1 if w.mask == "window" else 0))
+    if w.mask in ("causal_window", "window"):
+        lo = np.maximum(lo, pos - W + 1)
+    return np.maximum(hi - lo + 1, 0)
+
+
 def allowed_pairs(w) -> int:
-    """Allowed (i, j) pairs over all heads: causal L(L+1)/2, window W*L - W(W-1)/2 (L >= W)."""
-    L = w.L
-    if w.mask == "causal_window" and w.window < L:
-        W = w.window
-        per_head = W * L - W * (W - 1) // 2
-    else:
-        per_head = L * (L + 1) // 2
-    return w.B * w.Hq * per_head
+    """Allowed (i, j) pairs over all heads."""
+    import numpy as np
+
+    return w.B * w.Hq * int(row_key_counts(w, np.arange(w.L)).sum())
 
 
 class HipEvents:
@@ -145,10 +155,7 @@ def cpu_baseline(w, inp, seconds):
     while True:
         rows = np.arange(r, min(w.L, r + block))
         head_rows(qh, kg, vg, doh, w.scale, w.mask, w.window, rows)
-        if w.mask == "causal_window":
-            pairs += int(np.minimum(rows + 1, w.window).sum())
-        else:
-            pairs += int((rows + 1).sum())
+        pairs += int(row_key_counts(w, rows).sum())
         n += 1
         r += block
         if r + block > w.L:
@@ -163,7 +170,7 @@ def cpu_baseline(w, inp, seconds):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"q-head {h}: {n} blocks of {block} query rows x all {w.L} keys (full-width fp64 rows), "
+        "sample": f"q-head {h}: {n} blocks of {block} query rows x all {w.Lkv} keys (full-width fp64 rows), "
                   f"fwd+bwd, {pairs} allowed pairs, {dt:.1f} s wall; useful-FLOP rate",
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
@@ -276,7 +283,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "D": w.D,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "Lk": w.Lkv, "D": w.D,
                    "mask": w.mask, "window": w.window, "scale": w.scale, "allowed_pairs": N},
         "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "peak_mem_gb": round(peak / 1e9, 3),

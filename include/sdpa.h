@@ -15,7 +15,8 @@
  *
  * The forward also stores each row's logsumexp; the backward rebuilds P from
  * the scores and that stored value one tile at a time, never visits tiles that
- * lie wholly above the causal diagonal or wholly behind the window, and masks
+ * lie wholly outside the mask's band (above the causal diagonal, behind or,
+ * for a two-sided window, ahead of the window), and masks
  * single elements only in the tiles the band's edges cross: page "Lab 028 lab
  * detail: Off NVIDIA, you fix the platform yourself", sections "2026-10-21"
  * ("What the code says") and "What I changed, in plain terms" (items 1, 3,
@@ -23,31 +24,46 @@
  * Megakernel - end-to-end build plan (handoff)", section 4.1, stage 5 of the
  * per-layer list.
  *
- * Masks (allowed pairs; Lq == Lk == L in this version):
- *   SDPA_MASK_CAUSAL         j <= i
- *   SDPA_MASK_CAUSAL_WINDOW  j <= i and j > i - window   (window counts the
- *                            diagonal: window 1 = self only; window >= L is
- *                            identical to causal)
- * Keys j >= L and rows i >= L do not exist.
+ * Rows and keys
+ * -------------
+ * There are Lq query rows and Lk keys; the queries are the LAST Lq of the Lk
+ * key positions, so row i's diagonal is key i + off, off = Lk - Lq (the
+ * pages' diag_off; Lq == Lk gives off = 0). Masks (allowed pairs (i, j),
+ * 0 <= i < Lq, 0 <= j < Lk; d = i + off - j):
+ *   SDPA_MASK_NONE           every pair
+ *   SDPA_MASK_CAUSAL         d >= 0
+ *   SDPA_MASK_CAUSAL_WINDOW  0 <= d < window   (window counts the diagonal:
+ *                            window 1 = the diagonal key only; window >= Lk
+ *                            is identical to causal)
+ *   SDPA_MASK_WINDOW         -window < d < window   (both sides of the
+ *                            diagonal, no causal mask: 2 window - 1 keys;
+ *                            window >= Lq + Lk is identical to no mask)
+ * The non-causal window and queries that are a suffix of the keys are the
+ * variants of the same page, "What I changed, in plain terms", items 3-5.
+ * A row with no allowed key (Lq > Lk under a causal mask, or Lk == 0) gets
+ * O = 0, lse = -inf and dQ = 0, and adds nothing to dK/dV.
  *
  * Layout and ownership
  * --------------------
  * Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
- * contiguous row-major: Q, O, dO, dQ [B, Hq, L, D]; K, V, dK, dV
- * [B, Hq/group, L, D]; lse [B, Hq, L] float32. Element type: bfloat16
+ * contiguous row-major: Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
+ * [B, Hq/group, Lk, D]; lse [B, Hq, Lq] float32. Element type: bfloat16
  * (SDPA_BF16) or float32 (SDPA_F32) for Q, K, V, O, dO, dQ, dK, dV; lse is
- * always float32. Pointers must be 16-byte aligned. Outputs must not alias
- * inputs. The library never allocates device memory: the backward's scratch
- * space is the caller's `workspace` buffer.
+ * always float32. Pointers of non-empty tensors must be non-null and 16-byte
+ * aligned (pointers of tensors with no elements are not read). Outputs must
+ * not alias inputs. The library never allocates device memory: the
+ * backward's scratch space is the caller's `workspace` buffer.
  *
  * Execution and errors
  * --------------------
  * Work is enqueued on `stream` (0 = the null stream) and the call returns
  * after the enqueue. There is no global state; calls are thread-safe. All
  * argument checks happen before any launch: on error nothing is launched and
- * no output is touched. A problem with B == 0 or L == 0 (or Hq == 0) is valid
- * and launches nothing. There is no silent fallback to another algorithm:
- * unsupported combinations return SDPA_ERR_UNSUPPORTED.
+ * no output is touched. Empty problems are valid: B, Hq, Lq or Lk may be 0
+ * (the forward then launches nothing when there are no rows; the backward
+ * writes zero dK/dV when there are keys but no rows). There is no silent
+ * fallback to another algorithm: unsupported combinations return
+ * SDPA_ERR_UNSUPPORTED.
  */
 #ifndef SDPA_H
 #define SDPA_H
@@ -64,10 +80,11 @@ extern "C" {
 enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % group != 0,
-                                window < 1 with CAUSAL_WINDOW, scale not
+                                window < 1 with a window mask, scale not
                                 finite or <= 0, unknown enum, misaligned ptr */
-  SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: MASK_NONE, D not in
-                                {64,128,256,512} (bf16) / {64,128} (f32) */
+  SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64,128,256,512}
+                                (bf16) / {64,128} (f32); Lq + Lk > 2^30; B or
+                                Hq > 65535 */
   SDPA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
   SDPA_ERR_LAUNCH = -4       /* the HIP runtime reported a launch error */
 };
@@ -75,35 +92,38 @@ enum sdpa_status {
 enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F32 = 1 };
 
 enum sdpa_mask {
-  SDPA_MASK_NONE = 0, /* reserved; returns SDPA_ERR_UNSUPPORTED */
+  SDPA_MASK_NONE = 0,
   SDPA_MASK_CAUSAL = 1,
-  SDPA_MASK_CAUSAL_WINDOW = 2
+  SDPA_MASK_CAUSAL_WINDOW = 2,
+  SDPA_MASK_WINDOW = 3 /* two-sided, not causal */
 };
 
 /* Forward. Reads q, k, v; writes o (input dtype, fully overwritten for every
- * row i < L) and lse (float32, natural log, one value per query row).
- * `window` is ignored unless mask == SDPA_MASK_CAUSAL_WINDOW. */
+ * row i < Lq) and lse (float32, natural log, one value per query row).
+ * `window` is ignored unless mask is SDPA_MASK_CAUSAL_WINDOW or
+ * SDPA_MASK_WINDOW. */
 int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+                 int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                  int32_t dtype, int32_t mask, int32_t window, float scale,
                  hipStream_t stream);
 
 /* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
- * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, L]), rounded
- * up to 256 bytes. Linear in L. Returns 0 for empty shapes and for invalid
- * arguments. */
-size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t L, int32_t D, int32_t dtype);
+ * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, Lq]),
+ * rounded up to 256 bytes. Linear in Lq. Returns 0 for empty shapes and for
+ * invalid arguments. */
+size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, int32_t dtype);
 
 /* Backward. Reads q, k, v, o, dO and lse as written by sdpa_fwd_lse for the
- * same arguments; writes dq [B, Hq, L, D] and dk, dv [B, Hq/group, L, D] in
+ * same arguments; writes dq [B, Hq, Lq, D] and dk, dv [B, Hq/group, Lk, D] in
  * the input dtype, every element fully overwritten (keys no query attends get
  * exact zeros). `workspace` is device memory of at least
- * sdpa_bwd_workspace_bytes(...) bytes; its contents on entry do not matter
- * and are clobbered. Calls that share a workspace must be stream-ordered. */
+ * sdpa_bwd_workspace_bytes(...) bytes (it may be null when that is 0); its
+ * contents on entry do not matter and are clobbered. Calls that share a
+ * workspace must be stream-ordered. */
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
              const float* lse, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
-             int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+             int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
              int32_t dtype, int32_t mask, int32_t window, float scale,
              hipStream_t stream);
 
@@ -117,14 +137,14 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                    const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
-                   int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D,
+                   int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                    int32_t dtype, int32_t mask, int32_t window, float scale,
                    hipStream_t stream, hipEvent_t main_begin, hipEvent_t main_end);
 
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 200. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,6 +1,7 @@
 """MI355X (gfx950) memory-efficient scaled-dot-product attention: forward with
-per-row logsumexp and tiled dQ/dK/dV backward under causal and causal+window
-masks with GQA. The compute lives in the HIP library libsdpa.so (C ABI in
+per-row logsumexp and tiled dQ/dK/dV backward with GQA, under causal, causal
+sliding-window, two-sided window or no mask, with the queries optionally the
+last Lq of Lk key positions. The compute lives in the HIP library libsdpa.so (C ABI in
 include/sdpa.h); this package is its thin Python binding.
 """
 from ._lib import SdpaError, load, sdpa_bwd, sdpa_fwd_lse, workspace_bytes  # noqa: F401

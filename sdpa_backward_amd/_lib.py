@@ -20,7 +20,7 @@ SDPA_OK = 0
 STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", -3: "SDPA_ERR_WORKSPACE",
           -4: "SDPA_ERR_LAUNCH"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1}
-MASK = {"none": 0, "causal": 1, "causal_window": 2}
+MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
 EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_timed", "sdpa_bwd_workspace_bytes", "sdpa_status_string",
            "sdpa_abi_version")
@@ -43,7 +43,7 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is missing: build it with `python -m sdpa_backward_amd.build`")
     lib = ctypes.CDLL(path)
     p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-    shape = [i32, i32, i32, i32, i32, i32, i32, i32, f32, p]  # B Hq group L D dtype mask window scale stream
+    shape = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, p]  # B Hq group Lq Lk D dtype mask window scale stream
     lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + shape
     lib.sdpa_fwd_lse.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape
@@ -75,6 +75,7 @@ def _stream(device):
 
 
 def _validate(q, k, v, extra=()):
+    """(B, Hq, group, Lq, Lk, D) of q [B, Hq, Lq, D] and k, v [B, Hkv, Lk, D]."""
     for name, t in (("q", q), ("k", k), ("v", v), *extra):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -86,19 +87,19 @@ def _validate(q, k, v, extra=()):
         raise ValueError(f"unsupported dtype {q.dtype}")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, L, D]")
-    B, Hq, L, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != D:
+    B, Hq, Lq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    Hkv = k.shape[1]
+    Hkv, Lk = k.shape[1], k.shape[2]
     if Hkv == 0 or Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    return B, Hq, Hq // Hkv, L, D
+    return B, Hq, Hq // Hkv, Lq, Lk, D
 
 
 def _mask_args(mask, window):
     if mask not in MASK:
         raise ValueError(f"mask must be one of {tuple(MASK)}")
-    return MASK[mask], int(window) if mask == "causal_window" else 0
+    return MASK[mask], int(window) if mask in ("causal_window", "window") else 0
 
 
 def default_scale(D):
@@ -106,8 +107,12 @@ def default_scale(D):
 
 
 def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None):
-    """O [B,Hq,L,D] (q.dtype) and lse [B,Hq,L] (float32, natural log)."""
-    B, Hq, group, L, D = _validate(q, k, v)
+    """O [B,Hq,Lq,D] (q.dtype) and lse [B,Hq,Lq] (float32, natural log).
+
+    k, v are [B, Hkv, Lk, D]; with Lk != Lq the queries are the last Lq key
+    positions. mask: "none", "causal", "causal_window" (window keys up to the
+    diagonal) or "window" (window - 1 keys either side of it)."""
+    B, Hq, group, L, Lk, D = _validate(q, k, v)
     scale = default_scale(D) if scale is None else float(scale)
     m, w = _mask_args(mask, window)
     o = torch.empty_like(q) if out is None else out
@@ -116,7 +121,7 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
         raise ValueError("out must match q")
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, L]")
-    st = load().sdpa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, D,
+    st = load().sdpa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
                              DTYPE[q.dtype], m, w, scale, _stream(q.device))
     _check("sdpa_fwd_lse", st)
     return o, lse
@@ -132,7 +137,7 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
 
     ``main_events``: optional pair of raw hipEvent_t handles recorded around the
     main backward kernel (sdpa_bwd_timed)."""
-    B, Hq, group, L, D = _validate(q, k, v, (("o", o), ("do", do)))
+    B, Hq, group, L, Lk, D = _validate(q, k, v, (("o", o), ("do", do)))
     if o.shape != q.shape or do.shape != q.shape:
         raise ValueError("o and do must match q")
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -147,7 +152,7 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
     else:
         dq, dk, dv = out
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-            _ptr(workspace), workspace.numel(), B, Hq, group, L, D, DTYPE[q.dtype], m, w, scale,
+            _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale,
             _stream(q.device))
     if main_events is None:
         _check("sdpa_bwd", load().sdpa_bwd(*args))

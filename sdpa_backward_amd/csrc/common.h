@@ -124,15 +124,23 @@ SDPA_DEV void scale_in_agpr(f32x16 (&x)[N], float a) {
   asm volatile("s_nop 7");
 }
 
-// Allowed (query i, key j) pair: causal diagonal and window (w_eff = min(window, L),
-// or L for plain causal); rows i >= L do not exist (j <= i < L then implies j < L).
-SDPA_DEV bool allowed(int i, int j, int w_eff, int L) { return j <= i && j > i - w_eff && i < L; }
-
-// The same test in two steps for a run of keys j = j0 + r: base = i - j0 (or a
-// value that fails every test when row i does not exist), then key j0 + r is
-// allowed iff 0 <= base - r < w_eff, one unsigned compare per key.
-SDPA_DEV int band_base(int i, int j0, int L) { return i < L ? i - j0 : INT32_MIN; }
-SDPA_DEV bool in_band(int base, int r, int w_eff) { return (uint32_t)base - (uint32_t)r < (uint32_t)w_eff; }
+// Allowed (query row i, key j) pairs, every mask as one band: with Lq query
+// rows and Lk keys, the pair is allowed iff i < Lq, 0 <= j < Lk and
+// dlo <= j - i <= dhi. The host derives dlo <= dhi from the mask, the window
+// and the diagonal offset Lk - Lq (queries are the last Lq key positions):
+//   no mask        [-(Lq-1), Lk-1]          (every pair)
+//   causal         [-(Lq-1), off]
+//   causal window  [off - W + 1, off]
+//   window         [off - W + 1, off + W - 1]   (both sides of the diagonal)
+// clamped to [-(Lq-1), Lk-1], so i + dhi and j - dlo never overflow.
+// Row i's keys are [max(0, i + dlo), min(Lk - 1, i + dhi)] and key j's rows
+// [max(0, j - dhi), min(Lq - 1, j - dlo)]: both ends rise with i (with j), so
+// the rows of a tile see the union of their first and last row's ranges.
+//
+// A run of indices x0 + r is tested against a range [hi - span + 1, hi]
+// (span = 0: empty) with one unsigned compare per element: x0 + r is inside
+// iff (uint32)(hi - x0 - r) < span, so callers form base = hi - x0 once.
+SDPA_DEV bool in_band(int base, int r, int span) { return (uint32_t)base - (uint32_t)r < (uint32_t)span; }
 
 // ---------------------------------------------------------------- swizzled tiles
 // Chunk c (16 bytes) of row r sits at chunk slot c ^ swz(r), swz(r) < 16:

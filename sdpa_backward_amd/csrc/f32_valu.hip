@@ -15,38 +15,39 @@ namespace sdpa {
 template <int D>
 __global__ void __launch_bounds__(128)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-               float* __restrict__ O, float* __restrict__ LSE, int Hq, int group, int L, int w_eff,
-               float scale) {
+               float* __restrict__ O, float* __restrict__ LSE, int Hq, int group, int Lq, int Lk, int dlo,
+               int dhi, float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  if (i >= L) return;
+  if (i >= Lq) return;
   const int Hkv = Hq / group, g = h / group;
-  const float* q = Q + ((size_t)b * Hq + h) * L * D + (size_t)i * D;
-  const float* Kg = K + ((size_t)b * Hkv + g) * L * D;
-  const float* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  const float* q = Q + ((size_t)b * Hq + h) * Lq * D + (size_t)i * D;
+  const float* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const float* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
   float qr[D];
 #pragma unroll
   for (int d = 0; d < D; d++) qr[d] = q[d];
-  const int jlo = max(0, i - w_eff + 1);
+  // allowed keys of row i: dlo <= j - i <= dhi, 0 <= j < Lk (empty: O = 0, lse = -inf)
+  const int jlo = max(0, i + dlo), jhi = min(Lk - 1, i + dhi);
   float m = -INFINITY;
-  for (int j = jlo; j <= i; j++) {
+  for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
     m = fmaxf(m, s * scale);
   }
   float l = 0.f;
-  for (int j = jlo; j <= i; j++) {
+  for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
     l += expf(s * scale - m);
   }
-  const float lse = m + logf(l);
+  const float lse = jlo <= jhi ? m + logf(l) : -INFINITY;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; d++) acc[d] = 0.f;
-  for (int j = jlo; j <= i; j++) {
+  for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
@@ -54,10 +55,10 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 #pragma unroll
     for (int d = 0; d < D; d++) acc[d] = fmaf(p, Vg[(size_t)j * D + d], acc[d]);
   }
-  float* o = O + ((size_t)b * Hq + h) * L * D + (size_t)i * D;
+  float* o = O + ((size_t)b * Hq + h) * Lq * D + (size_t)i * D;
 #pragma unroll
   for (int d = 0; d < D; d++) o[d] = acc[d];
-  LSE[((size_t)b * Hq + h) * L + i] = lse;
+  LSE[((size_t)b * Hq + h) * Lq + i] = lse;
 }
 
 // dQ rows (and Delta_i = <dO_i, O_i>, kept for the key pass)
@@ -65,18 +66,18 @@ template <int D>
 __global__ void __launch_bounds__(128)
 bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                   const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
-                  float* __restrict__ dQ, float* __restrict__ Delta, int Hq, int group, int L, int w_eff,
-                  float scale) {
+                  float* __restrict__ dQ, float* __restrict__ Delta, int Hq, int group, int Lq, int Lk,
+                  int dlo, int dhi, float scale) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  if (i >= L) return;
+  if (i >= Lq) return;
   const int Hkv = Hq / group, g = h / group;
-  const size_t row = ((size_t)b * Hq + h) * L + i;
+  const size_t row = ((size_t)b * Hq + h) * Lq + i;
   const float* q = Q + row * D;
   const float* o = O + row * D;
   const float* dor = dO + row * D;
-  const float* Kg = K + ((size_t)b * Hkv + g) * L * D;
-  const float* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  const float* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const float* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
   float qr[D], dr[D], acc[D];
   float delta = 0.f;
 #pragma unroll
@@ -87,7 +88,7 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
     acc[d] = 0.f;
   }
   const float lse = LSE[row];
-  for (int j = max(0, i - w_eff + 1); j <= i; j++) {
+  for (int j = max(0, i + dlo), jhi = min(Lk - 1, i + dhi); j <= jhi; j++) {
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) {
@@ -110,12 +111,12 @@ __global__ void __launch_bounds__(128)
 bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                    const float* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV, int Hq,
-                   int group, int L, int w_eff, float scale) {
+                   int group, int Lq, int Lk, int dlo, int dhi, float scale) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
-  if (j >= L) return;
+  if (j >= Lk) return;
   const int Hkv = Hq / group;
-  const size_t krow = ((size_t)b * Hkv + g) * L + j;
+  const size_t krow = ((size_t)b * Hkv + g) * Lk + j;
   float kr[D], vr[D], dk[D], dv[D];
 #pragma unroll
   for (int d = 0; d < D; d++) {
@@ -124,10 +125,11 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
-  const int ihi = min(L - 1, j + w_eff - 1);
+  // rows that see key j: dlo <= j - i <= dhi, 0 <= i < Lq
+  const int ilo = max(0, j - dhi), ihi = min(Lq - 1, j - dlo);
   for (int h = g * group; h < (g + 1) * group; h++) {
-    const size_t hrow = ((size_t)b * Hq + h) * L;
-    for (int i = j; i <= ihi; i++) {
+    const size_t hrow = ((size_t)b * Hq + h) * Lq;
+    for (int i = ilo; i <= ihi; i++) {
       const float* q = Q + (hrow + i) * D;
       const float* dor = dO + (hrow + i) * D;
       float s = 0.f, dp = 0.f;
@@ -154,46 +156,48 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
 
 template <int D>
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          int group, int L, int w_eff, float scale, hipStream_t stream) {
-  dim3 grid((L + 127) / 128, Hq, B);
+                          int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream) {
+  dim3 grid((Lq + 127) / 128, Hq, B);
   hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (float*)o, lse, Hq, group, L, w_eff, scale);
+                     (const float*)v, (float*)o, lse, Hq, group, Lq, Lk, dlo, dhi, scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                          int group, int L, int w_eff, float scale, hipStream_t stream, hipEvent_t ev0,
-                          hipEvent_t ev1) {
+                          int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream,
+                          hipEvent_t ev0, hipEvent_t ev1) {
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   hipError_t e;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  dim3 grid((L + 127) / 128, Hq, B);
-  hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
-                     L, w_eff, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid2((L + 127) / 128, Hq / group, B);
-  hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
-                     group, L, w_eff, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (Lq > 0) {
+    dim3 grid((Lq + 127) / 128, Hq, B);
+    hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
+                       Lq, Lk, dlo, dhi, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (Lk > 0) {
+    dim3 grid2((Lk + 127) / 128, Hq / group, B);
+    hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
+                       (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
+                       group, Lq, Lk, dlo, dhi, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 
-template hipError_t launch_fwd_f32<64>(const void*, const void*, const void*, void*, float*, int, int, int,
-                                       int, int, float, hipStream_t);
-template hipError_t launch_fwd_f32<128>(const void*, const void*, const void*, void*, float*, int, int, int,
-                                        int, int, float, hipStream_t);
-template hipError_t launch_bwd_f32<64>(const void*, const void*, const void*, const void*, const void*,
-                                       const float*, void*, void*, void*, float*, int, int, int, int, int,
-                                       float, hipStream_t, hipEvent_t, hipEvent_t);
-template hipError_t launch_bwd_f32<128>(const void*, const void*, const void*, const void*, const void*,
-                                        const float*, void*, void*, void*, float*, int, int, int, int, int,
-                                        float, hipStream_t, hipEvent_t, hipEvent_t);
+#define SDPA_INST_F32(D)                                                                                    \
+  template hipError_t launch_fwd_f32<D>(const void*, const void*, const void*, void*, float*, int, int, int, \
+                                        int, int, int, int, float, hipStream_t);                            \
+  template hipError_t launch_bwd_f32<D>(const void*, const void*, const void*, const void*, const void*,     \
+                                        const float*, void*, void*, void*, float*, int, int, int, int, int,  \
+                                        int, int, float, hipStream_t, hipEvent_t, hipEvent_t);
+SDPA_INST_F32(64)
+SDPA_INST_F32(128)
 
 }  // namespace sdpa

@@ -2,8 +2,8 @@
 //
 // One workgroup = 4 waves = one (b, kv head g) and a block of BKT keys. It
 // walks every query tile of every q-head of the GQA group whose rows can see
-// one of its keys (tiles above the diagonal or entirely past the window are
-// never visited), so dK and dV of the group are summed in registers without
+// one of its keys (tiles wholly outside the mask's band are never visited), so
+// dK and dV of the group are summed in registers without
 // atomics, and every key gets its dK/dV written, attended or not (page "Lab
 // 028 lab detail: Off NVIDIA, you fix the platform yourself", section "What I
 // changed, in plain terms", items 3-5). P is recomputed from S and the stored
@@ -63,8 +63,8 @@ template <int D, int PASS>
 __global__ void __launch_bounds__(256, 1)
 kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
           const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-          bf16* __restrict__ dK, bf16* __restrict__ dV, int Hq, int group, int L, int w_eff, float scale,
-          float scale_log2) {
+          bf16* __restrict__ dK, bf16* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
+          float scale, float scale_log2) {
   using C = KvCfg<D>;
   constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
   __shared__ __attribute__((aligned(16))) bf16 ks[C::BKT * D];
@@ -82,14 +82,17 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   la.init(lane);
   const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
-  const int nkt = (L + C::BKT - 1) / C::BKT;
+  const int nkt = (Lk + C::BKT - 1) / C::BKT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
   const int k0 = kt * C::BKT;
   const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
-  const bf16* Kg = K + ((size_t)b * Hkv + g) * L * D;
-  const bf16* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  const bf16* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const bf16* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist)
+  const int ihi = min(Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
+  const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
 
   zero_lds(ks, C::BKT * D, tid);
   zero_lds(qb0, QT, tid);
@@ -102,7 +105,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   {
     TileLoader<D, C::BKT, C::NW> kld;
     kld.init(w, lane);
-    kld.issue(ks, Kg + (size_t)k0 * D, L - k0, w);
+    kld.issue(ks, Kg + (size_t)k0 * D, Lk - k0, w);
   }
   TileLoader<D, C::BQ, C::NW> ld;  // per-lane source offsets of the Q/dO tile loads
   ld.init(w, lane);
@@ -110,9 +113,9 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
   bf16x8 vreg[WANT_DK ? NKS : 1];
   if constexpr (WANT_DK) {
-    const bf16* vrow = Vg + (size_t)(kj < L ? kj : 0) * D;
+    const bf16* vrow = Vg + (size_t)(kj < Lk ? kj : 0) * D;
 #pragma unroll
-    for (int s = 0; s < NKS; s++) vreg[s] = kj < L ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+    for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
   }
 
   f32x16 dkacc[WANT_DK ? NDB : 1], dvacc[WANT_DV ? NDB : 1];
@@ -123,26 +126,28 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   }
 
   // query tiles that can see a key of this workgroup, for each q-head of the group
-  const int klast = min(k0 + C::BKT - 1, L - 1);
-  const int qt_lo = k0 / C::BQ;
-  const int qt_hi = min(L - 1, klast + w_eff - 1) / C::BQ;
-  const int nq = qt_hi - qt_lo + 1;
+  // (none: total = 0, and the keys get zero gradients)
+  const int klast = min(k0 + C::BKT - 1, Lk - 1);
+  const int rlo = max(0, k0 - dhi), rhi = min(Lq - 1, klast - dlo);
+  const int qt_lo = rlo / C::BQ;
+  const int nq = rlo <= rhi ? rhi / C::BQ - qt_lo + 1 : 0;
   const int total = group * nq;
+  const int kb1 = min(kb0 + 31, Lk - 1);  // this wave's last key (kb1 < kb0: none)
 
   auto tile_src = [&](int it, const bf16*& qs, const bf16*& ds, int& q0) {
     const int hq = g * group + it / nq;
     q0 = (qt_lo + it % nq) * C::BQ;
-    const size_t off = (((size_t)b * Hq + hq) * L + q0) * D;
+    const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
     qs = Q + off;
     ds = dO + off;
   };
   // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta of them (rows
-  // clamped to L-1); one 4-byte global->LDS load per lane (wave 0 only)
+  // clamped to Lq-1); one 4-byte global->LDS load per lane (wave 0 only)
   auto load_rows = [&](int it, float* rv) {
     const int hq = g * group + it / nq;
     const int q0 = (qt_lo + it % nq) * C::BQ;
-    const int row = min(q0 + (lane & 31), L - 1);
-    const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * L + row;
+    const int row = min(q0 + (lane & 31), Lq - 1);
+    const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * Lq + row;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
   };
@@ -150,8 +155,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     const bf16 *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
-    ld.issue(qd, qs, L - q0, w);
-    ld.issue(dd, ds, L - q0, w);
+    ld.issue(qd, qs, Lq - q0, w);
+    ld.issue(dd, ds, Lq - q0, w);
     if (w == 0) load_rows(it, rv);
   };
 
@@ -161,9 +166,9 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
                              const bf16* Qc, const bf16* dOc) {
   // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
   // tiles, as a select (the wave-uniform test stays outside the element loop)
-  // rows q0 + c_row(i, hh) vs this lane's key kj: in the band iff
-  // 0 <= q0 + c_row - kj < w_eff, and the row must exist (< L)
-  const int base = q0 + 4 * hh - kj, rowlim = L - q0 - 4 * hh;
+  // row q0 + c_row(i, hh) is allowed for this lane's key iff it lies in
+  // [ihi - kspan + 1, ihi]: ihi - q0 - c_row = base - rr, one unsigned compare
+  const int base = ihi - q0 - 4 * hh;
   auto form = [&](auto masked) {
 #pragma unroll
     for (int blk = 0; blk < 4; blk++) {
@@ -176,7 +181,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], scale_log2, -lv));
         if constexpr (decltype(masked)::value) {
           const int rr = 8 * blk + r;  // c_row(i, hh) - 4 hh
-          p = (uint32_t)(base + rr) < (uint32_t)w_eff && rr < rowlim ? p : 0.f;
+          p = in_band(base, rr, kspan) ? p : 0.f;
         }
         s_acc[i] = p;
         if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
@@ -221,9 +226,10 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
                      bf16* dn, float* rvn) {
     constexpr bool PF = decltype(prefetch)::value;
     const int q0 = (qt_lo + it % nq) * C::BQ;
-    const int r1 = min(q0 + 31, L - 1);
-    const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
-    const bool full = kb0 + 31 <= q0 && kb0 > q0 + 31 - w_eff && q0 + 31 < L;
+    // some pair of the tile's rows and the wave's keys allowed / every pair allowed
+    const int r1 = min(q0 + 31, Lq - 1);
+    const bool active = kb0 <= kb1 && q0 <= kb1 - dlo && r1 >= kb0 - dhi;
+    const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi;
 
     __amdgpu_buffer_rsrc_t qrs, drs;
     if constexpr (PF) {
@@ -231,8 +237,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       const bf16 *qs, *ds;
       int q0n;
       tile_src(more ? it + 1 : it, qs, ds, q0n);
-      qrs = decltype(ld)::rsrc_of(qs, more ? L - q0n : 0);
-      drs = decltype(ld)::rsrc_of(ds, more ? L - q0n : 0);
+      qrs = decltype(ld)::rsrc_of(qs, more ? Lq - q0n : 0);
+      drs = decltype(ld)::rsrc_of(ds, more ? Lq - q0n : 0);
       if (w == 0) load_rows(more ? it + 1 : it, rvn);
     }
     constexpr int NJ = decltype(ld)::NJ;
@@ -285,7 +291,9 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     form_and_update(q0, full, rv, s_acc, dp_acc, Qc, dOc);
   };
 
-  if constexpr (C::NBUF == 2) {
+  if (total == 0) {
+    // no row sees these keys: zero gradients
+  } else if constexpr (C::NBUF == 2) {
     issue(0, qb0, db0, rv0);
     wait_all_and_barrier();
     for (int it = 0; it < total; it += 2) {
@@ -312,14 +320,14 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       const bf16 *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
-      ld.issue(dst, qs, more ? L - q0n : 0, w);
+      ld.issue(dst, qs, more ? Lq - q0n : 0, w);
       if (w == 0) load_rows(it, rvd);
     };
     auto issue_do = [&](int it, bool more, bf16* dst) {
       const bf16 *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
-      ld.issue(dst, ds, more ? L - q0n : 0, w);
+      ld.issue(dst, ds, more ? Lq - q0n : 0, w);
     };
     // S, then (dK pass) dP once dO has landed; operand reads pipelined by hand
     auto sdp = [&](const bf16* Qc, const bf16* dOc, f32x16& s_acc, f32x16& dp_acc) {
@@ -353,9 +361,9 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     };
     auto tile = [&](int it, bf16* Qb, bf16* Db, float* rvc, float* rvn) {
       const int q0 = (qt_lo + it % nq) * C::BQ;
-      const int r1 = min(q0 + 31, L - 1);
-      const bool active = kb0 < L && kb0 <= r1 && kb0 + 31 > q0 - w_eff;
-      const bool full = kb0 + 31 <= q0 && kb0 > q0 + 31 - w_eff && q0 + 31 < L;
+      const int r1 = min(q0 + 31, Lq - 1);
+      const bool active = kb0 <= kb1 && q0 <= kb1 - dlo && r1 >= kb0 - dhi;
+      const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi;
       const bool more = it + 1 < total;
       const int itn = more ? it + 1 : it;
       wait_vm_and_barrier<NJ>();  // Q(t) and lse/Delta(t) landed (dO(t) may not have)
@@ -382,15 +390,15 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
-  bf16* dKg = dK + ((size_t)b * Hkv + g) * L * D;
-  bf16* dVg = dV + ((size_t)b * Hkv + g) * L * D;
+  bf16* dKg = dK + ((size_t)b * Hkv + g) * Lk * D;
+  bf16* dVg = dV + ((size_t)b * Hkv + g) * Lk * D;
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
     const int col = dw0 + 32 * d + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
       const int key = kb0 + c_row(i, hh);
-      if (key < L) {
+      if (key < Lk) {
         if constexpr (WANT_DK) dKg[(size_t)key * D + col] = (bf16)(dkacc[d][i] * scale);
         if constexpr (WANT_DV) dVg[(size_t)key * D + col] = (bf16)dvacc[d][i];
       }
@@ -400,31 +408,31 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
 template <int D>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int L, int w_eff,
-                     float scale, hipStream_t stream) {
+                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                     int dhi, float scale, hipStream_t stream) {
   using C = KvCfg<D>;
-  const long nwg = (long)((L + C::BKT - 1) / C::BKT) * (Hq / group) * B;
+  const long nwg = (long)((Lk + C::BKT - 1) / C::BKT) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  if (nwg == 0) return hipSuccess;
+  auto run = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq, group, Lq, Lk,
+                       dlo, dhi, scale, scale * kLog2e);
+    return hipGetLastError();
+  };
   if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
-    hipLaunchKernelGGL((kv_kernel<D, KV_DV>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
-                       group, L, w_eff, scale, scale * kLog2e);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = run(kv_kernel<D, KV_DV>);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kv_kernel<D, KV_DK>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
-                       group, L, w_eff, scale, scale * kLog2e);
+    return run(kv_kernel<D, KV_DK>);
   } else {
-    hipLaunchKernelGGL((kv_kernel<D, KV_BOTH>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq,
-                       group, L, w_eff, scale, scale * kLog2e);
+    return run(kv_kernel<D, KV_BOTH>);
   }
-  return hipGetLastError();
 }
 
 #define SDPA_INST_KV(D)                                                                                  \
   template hipError_t launch_kv<D>(const void*, const void*, const void*, const void*, const float*,    \
-                                   const float*, void*, void*, int, int, int, int, int, float, hipStream_t);
+                                   const float*, void*, void*, int, int, int, int, int, int, int, float, \
+                                   hipStream_t);
 SDPA_INST_KV(64)
 SDPA_INST_KV(128)
 SDPA_INST_KV(256)

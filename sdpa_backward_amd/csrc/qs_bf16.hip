@@ -12,9 +12,9 @@
 // One workgroup = 4 waves = BQ query rows of one (b, h). Each wave owns 32 rows
 // (for D = 512 two waves share 32 rows and split the head dimension, adding
 // their partial score tiles through LDS). The loop walks key tiles of BK keys
-// in the causal/window band only (tiles above the diagonal or entirely behind
-// the window are never visited; a wave skips tiles outside its own rows' band,
-// and applies the element mask only on edge tiles). K and V tiles stream into
+// in the mask's band only (tiles wholly outside it, above the diagonal, behind
+// or ahead of a window, are never visited; a wave skips tiles outside its own
+// rows' band, and applies the element mask only on edge tiles). K and V tiles stream into
 // double-buffered LDS with asynchronous global->LDS loads.
 //
 // Per key tile, per wave (C tiles are 32x32 fp32, one query per lane column):
@@ -77,8 +77,8 @@ template <int D, int MODE>
 __global__ void __launch_bounds__(256, 1)
 qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
           const bf16* __restrict__ O, const bf16* __restrict__ dO, float* __restrict__ LSE,
-          float* __restrict__ Delta, bf16* __restrict__ Out, int Hq, int group, int L, int w_eff,
-          float scale, float scale_log2) {
+          float* __restrict__ Delta, bf16* __restrict__ Out, int Hq, int group, int Lq, int Lk, int dlo,
+          int dhi, float scale, float scale_log2) {
   using C = QsCfg<D>;
   constexpr int BK = C::BK, NMB = C::NMB, DW = C::DW, NKS = DW / 16, NDB = DW / 32;
   constexpr int NX = MODE == QS_DQ ? 2 * NMB : NMB;  // C tiles exchanged when the head dim is split
@@ -95,30 +95,33 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   TileLoader<D, C::BK, C::NW> ld;  // per-lane source offsets of the K/V tile loads
   ld.init(w, lane);
   const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
-  const int nqt = (L + C::BQ - 1) / C::BQ;
+  const int nqt = (Lq + C::BQ - 1) / C::BQ;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = nqt - 1 - logical % nqt;  // longest causal rows first within a head
   const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
   const int Hkv = Hq / group, g = h / group;
   const size_t hrow = (size_t)b * Hq + h;
-  const bf16* Kg = K + ((size_t)b * Hkv + g) * L * D;
-  const bf16* Vg = V + ((size_t)b * Hkv + g) * L * D;
+  const bf16* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const bf16* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
 
   const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
   const int qi = iw0 + (lane & 31);  // this lane's query row
-  const bool qok = qi < L;
+  const bool qok = qi < Lq;
+  // this row's keys: [jhi - span + 1, jhi] (span 0: none, or the row does not exist)
+  const int jhi = min(Lk - 1, qi + dhi), jlo = max(0, qi + dlo);
+  const int span = qok && jhi >= jlo ? jhi - jlo + 1 : 0;
 
   // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
   bf16x8 qreg[NKS];
-  const bf16* qrow = Q + (hrow * L + (qok ? qi : 0)) * D;
+  const bf16* qrow = Q + (hrow * Lq + (qok ? qi : 0)) * D;
 #pragma unroll
   for (int s = 0; s < NKS; s++) qreg[s] = qok ? *(const bf16x8*)(qrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
 
   bf16x8 dreg[MODE == QS_DQ ? NKS : 1];
   float lse2 = 0.f, dlt = 0.f;
   if constexpr (MODE == QS_DQ) {
-    const bf16* drow = dO + (hrow * L + (qok ? qi : 0)) * D;
-    const bf16* orow = O + (hrow * L + (qok ? qi : 0)) * D;
+    const bf16* drow = dO + (hrow * Lq + (qok ? qi : 0)) * D;
+    const bf16* orow = O + (hrow * Lq + (qok ? qi : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NKS; s++) dreg[s] = qok ? *(const bf16x8*)(drow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
     // Delta_i = <dO_i, O_i> over the whole head dimension, fp32
@@ -133,8 +136,8 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       }
     }
     dlt = dot + __shfl_xor(dot, 32);
-    lse2 = qok ? LSE[hrow * L + qi] * kLog2e : 0.f;
-    if (qok && dsi == 0 && hh == 0) Delta[hrow * L + qi] = dlt;
+    lse2 = qok ? LSE[hrow * Lq + qi] * kLog2e : 0.f;  // -inf for a row with no key (then every p is masked)
+    if (qok && dsi == 0 && hh == 0) Delta[hrow * Lq + qi] = dlt;
   }
 
   f32x16 acc[NDB];
@@ -142,9 +145,11 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   for (int d = 0; d < NDB; d++) acc[d] = zero16();
   float m = -INFINITY, lsum = 0.f;  // forward: running (used) max in log2 units and row sum
 
-  const int i1 = min(i0 + C::BQ - 1, L - 1);
-  const int kt_lo = max(0, i0 - w_eff + 1) / BK, kt_hi = i1 / BK;
-  const int wr0 = iw0, wr1 = min(iw0 + 31, L - 1);  // this wave's rows (wr1 < wr0: none)
+  // key tiles that a row of this workgroup can see (none: kt_hi < kt_lo)
+  const int i1 = min(i0 + C::BQ - 1, Lq - 1);
+  const int klo = max(0, i0 + dlo), khi = min(Lk - 1, i1 + dhi);
+  const int kt_lo = klo / BK, kt_hi = klo <= khi ? khi / BK : kt_lo - 1;
+  const int wr0 = iw0, wr1 = min(iw0 + 31, Lq - 1);  // this wave's rows (wr1 < wr0: none)
 
   auto step = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
     // The next tile's loads (into the other buffers) are issued one at a time
@@ -156,8 +161,8 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     // rows and the loads read nothing.
     const bool more = kt + 1 <= kt_hi;
     const int jn = more ? (kt + 1) * BK : 0;
-    const auto krs = decltype(ld)::rsrc_of(Kg + (size_t)jn * D, more ? L - jn : 0);
-    const auto vrs = decltype(ld)::rsrc_of(Vg + (size_t)jn * D, more ? L - jn : 0);
+    const auto krs = decltype(ld)::rsrc_of(Kg + (size_t)jn * D, more ? Lk - jn : 0);
+    const auto vrs = decltype(ld)::rsrc_of(Vg + (size_t)jn * D, more ? Lk - jn : 0);
     constexpr int NJ = decltype(ld)::NJ;
     auto load_one = [&, krs, vrs](int j) {  // j in [0, 2 NJ): K blocks, then V blocks
       if constexpr (decltype(ld)::PER % C::NW != 0) {
@@ -171,8 +176,9 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 #pragma unroll
     for (int d = 0; d < NDB; d++) keep_in_agpr(acc[d]);
     const int j0 = kt * BK;
-    const bool active = wr0 <= wr1 && j0 <= wr1 && j0 + BK - 1 > wr0 - w_eff;
-    const bool full = j0 + BK - 1 <= wr0 && j0 > wr1 - w_eff && wr1 == wr0 + 31;
+    // some pair of the wave's rows and the tile's keys allowed / every pair allowed
+    const bool active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo;
+    const bool full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk;
 
     // Scores of every wave, also of waves whose rows miss this tile (they
     // would only wait at the tile barrier): no branch around the MFMAs.
@@ -212,11 +218,11 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       auto scores = [&](auto masked) {
 #pragma unroll
         for (int mb = 0; mb < NMB; mb++) {
-          const int base = band_base(qi, j0 + 32 * mb + 4 * hh, L);
+          const int base = jhi - (j0 + 32 * mb + 4 * hh);
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             if constexpr (decltype(masked)::value)
-              st[mb][i] = in_band(base, 8 * (i >> 2) + (i & 3), w_eff) ? st[mb][i] : -INFINITY;
+              st[mb][i] = in_band(base, 8 * (i >> 2) + (i & 3), span) ? st[mb][i] : -INFINITY;
             mx = fmaxf(mx, st[mb][i]);
           }
         }
@@ -261,13 +267,13 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
-        const int base = band_base(qi, j0 + 32 * mb + 4 * hh, L);
+        const int base = jhi - (j0 + 32 * mb + 4 * hh);
         auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, -lse2));
             if constexpr (decltype(masked)::value)
-              p = in_band(base, 8 * (i >> 2) + (i & 3), w_eff) ? p : 0.f;
+              p = in_band(base, 8 * (i >> 2) + (i & 3), span) ? p : 0.f;
             st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
           }
         };
@@ -289,15 +295,15 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     }
   };
 
-  {  // first tile
+  if (kt_lo <= kt_hi) {  // first tile (uniform over the workgroup)
     const int j0 = kt_lo * BK;
     zero_lds(kb0, C::TILE, tid);
     zero_lds(kb1, C::TILE, tid);
     zero_lds(vb0, C::TILE, tid);
     zero_lds(vb1, C::TILE, tid);
     lds_barrier();
-    ld.issue(kb0, Kg + (size_t)j0 * D, L - j0, w);
-    ld.issue(vb0, Vg + (size_t)j0 * D, L - j0, w);
+    ld.issue(kb0, Kg + (size_t)j0 * D, Lk - j0, w);
+    ld.issue(vb0, Vg + (size_t)j0 * D, Lk - j0, w);
     wait_all_and_barrier();
   }
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
@@ -309,7 +315,7 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   }
 
   if (!qok) return;
-  bf16* orow = Out + (hrow * L + qi) * D;
+  bf16* orow = Out + (hrow * Lq + qi) * D;
   if constexpr (MODE == QS_FWD) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
@@ -321,7 +327,7 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         for (int r = 0; r < 4; r++) v[r] = (bf16)(acc[d][4 * blk + r] * inv);
         *(bf16x4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
       }
-    if (dsi == 0 && hh == 0) LSE[hrow * L + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+    if (dsi == 0 && hh == 0) LSE[hrow * Lq + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
   } else {
 #pragma unroll
     for (int d = 0; d < NDB; d++)
@@ -337,24 +343,25 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
 
 template <int D, int MODE>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
-                     float* delta, void* out, int B, int Hq, int group, int L, int w_eff, float scale,
-                     hipStream_t stream) {
+                     float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
+                     float scale, hipStream_t stream) {
   using C = QsCfg<D>;
-  const long nwg = (long)((L + C::BQ - 1) / C::BQ) * Hq * B;
+  const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL((qs_kernel<D, MODE>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)o, (const bf16*)dO, lse, delta, (bf16*)out,
-                     Hq, group, L, w_eff, scale, scale * kLog2e);
+                     Hq, group, Lq, Lk, dlo, dhi, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 #define SDPA_INST_QS(D)                                                                                 \
   template hipError_t launch_qs<D, QS_FWD>(const void*, const void*, const void*, const void*,          \
                                            const void*, float*, float*, void*, int, int, int, int, int, \
-                                           float, hipStream_t);                                         \
+                                           int, int, float, hipStream_t);                                         \
   template hipError_t launch_qs<D, QS_DQ>(const void*, const void*, const void*, const void*,           \
                                           const void*, float*, float*, void*, int, int, int, int, int,  \
-                                          float, hipStream_t);
+                                          int, int, float, hipStream_t);
 SDPA_INST_QS(64)
 SDPA_INST_QS(128)
 SDPA_INST_QS(256)

@@ -18,18 +18,18 @@ namespace sdpa {
 enum { QS_FWD = 0, QS_DQ = 1 };
 template <int D, int MODE>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
-                     float* delta, void* out, int B, int Hq, int group, int L, int w_eff, float scale,
-                     hipStream_t stream);
-template <int D>
-hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int L, int w_eff,
+                     float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
                      float scale, hipStream_t stream);
 template <int D>
-hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
-                          float, hipStream_t);
+hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                     const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                     int dhi, float scale, hipStream_t stream);
+template <int D>
+hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
+                          int, float, hipStream_t);
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
-                          void*, void*, void*, float*, int, int, int, int, int, float, hipStream_t,
+                          void*, void*, void*, float*, int, int, int, int, int, int, int, float, hipStream_t,
                           hipEvent_t, hipEvent_t);
 
 // bf16 backward: dQ pass (also writes Delta), then the dK/dV pass; the
@@ -37,14 +37,14 @@ hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, co
 template <int D>
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                           int group, int L, int w_eff, float scale, hipStream_t stream, hipEvent_t ev0,
-                           hipEvent_t ev1) {
-  hipError_t e = launch_qs<D, QS_DQ>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, L,
-                                     w_eff, scale, stream);
+                           int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream,
+                           hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e = launch_qs<D, QS_DQ>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, Lq, Lk,
+                                     dlo, dhi, scale, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, L, w_eff, scale, stream);
+  e = launch_kv<D>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -59,10 +59,29 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Shape {
-  int B, Hq, group, L, D, dtype, mask, window;
+  int B, Hq, group, Lq, Lk, D, dtype, mask, window;
   float scale;
-  bool empty() const { return B == 0 || Hq == 0 || L == 0; }
-  int w_eff() const { return mask == SDPA_MASK_CAUSAL ? L : std::min(window, L); }
+  bool no_rows() const { return B == 0 || Hq == 0 || Lq == 0; }
+  bool no_keys() const { return B == 0 || Hq == 0 || Lk == 0; }
+  // The mask as a band dlo <= j - i <= dhi (query rows are the last Lq of the
+  // Lk key positions, so the diagonal sits at j - i = Lk - Lq), clamped to the
+  // differences that occur, [-(Lq - 1), Lk - 1]. The window counts the
+  // diagonal: causal window [off - W + 1, off]; a window without the causal
+  // mask extends the same distance past the diagonal, [off - W + 1, off + W - 1]
+  // (page "Lab 028 lab detail: Off NVIDIA, you fix the platform yourself",
+  // section "What I changed, in plain terms", items 3-5).
+  void band(int& dlo, int& dhi) const {
+    const int64_t off = (int64_t)Lk - Lq, lo_min = -((int64_t)Lq - 1), hi_max = (int64_t)Lk - 1;
+    int64_t lo = lo_min, hi = hi_max;
+    if (mask == SDPA_MASK_CAUSAL) hi = off;
+    if (mask == SDPA_MASK_CAUSAL_WINDOW) lo = off - window + 1, hi = off;
+    if (mask == SDPA_MASK_WINDOW) lo = off - window + 1, hi = off + window - 1;
+    lo = std::max(lo, lo_min);
+    hi = std::min(hi, hi_max);
+    if (lo > hi) lo = hi_max, hi = lo_min - 1;  // empty band (the kernels see empty row and key ranges)
+    dlo = (int)std::max<int64_t>(std::min<int64_t>(lo, INT32_MAX), INT32_MIN);
+    dhi = (int)std::max<int64_t>(std::min<int64_t>(hi, INT32_MAX), INT32_MIN);
+  }
 };
 
 bool d_supported(int dtype, int D) {
@@ -70,37 +89,44 @@ bool d_supported(int dtype, int D) {
   return D == 64 || D == 128;
 }
 
+bool windowed(int mask) { return mask == SDPA_MASK_CAUSAL_WINDOW || mask == SDPA_MASK_WINDOW; }
+
 // Shape checks shared by both entry points (pointers are checked by the caller).
 int check_shape(const Shape& s) {
   if (s.dtype != SDPA_BF16 && s.dtype != SDPA_F32) return SDPA_ERR_INVALID_ARG;
-  if (s.mask != SDPA_MASK_NONE && s.mask != SDPA_MASK_CAUSAL && s.mask != SDPA_MASK_CAUSAL_WINDOW)
-    return SDPA_ERR_INVALID_ARG;
-  if (s.B < 0 || s.Hq < 0 || s.L < 0 || s.D <= 0 || s.group <= 0) return SDPA_ERR_INVALID_ARG;
+  if (s.mask != SDPA_MASK_NONE && s.mask != SDPA_MASK_CAUSAL && !windowed(s.mask)) return SDPA_ERR_INVALID_ARG;
+  if (s.B < 0 || s.Hq < 0 || s.Lq < 0 || s.Lk < 0 || s.D <= 0 || s.group <= 0) return SDPA_ERR_INVALID_ARG;
   if (s.Hq % s.group != 0) return SDPA_ERR_INVALID_ARG;
-  if (s.mask == SDPA_MASK_CAUSAL_WINDOW && s.window < 1) return SDPA_ERR_INVALID_ARG;
+  if (windowed(s.mask) && s.window < 1) return SDPA_ERR_INVALID_ARG;
   if (!isfinite(s.scale) || !(s.scale > 0.f)) return SDPA_ERR_INVALID_ARG;
-  if (s.mask == SDPA_MASK_NONE) return SDPA_ERR_UNSUPPORTED;
   if (!d_supported(s.dtype, s.D)) return SDPA_ERR_UNSUPPORTED;
   // size limits: the kernels' 1-D grids hold at most 2^31 - 1 workgroups (checked
-  // again at launch), head and batch counts stay far below that
+  // again at launch), head and batch counts stay far below that, and row / key
+  // indices plus band offsets stay inside int32
   if (s.Hq > 65535 || s.B > 65535) return SDPA_ERR_UNSUPPORTED;
-  if ((int64_t)s.B * s.Hq * s.L > (int64_t(1) << 40)) return SDPA_ERR_UNSUPPORTED;
+  if ((int64_t)s.Lq + s.Lk > (int64_t(1) << 30)) return SDPA_ERR_UNSUPPORTED;
+  if ((int64_t)s.B * s.Hq * s.Lq > (int64_t(1) << 40) || (int64_t)s.B * s.Hq * s.Lk > (int64_t(1) << 40))
+    return SDPA_ERR_UNSUPPORTED;
   return SDPA_OK;
 }
 
 size_t workspace_for(const Shape& s) {
-  if (s.empty()) return 0;
-  const size_t rows = (size_t)s.B * s.Hq * s.L;
+  if (s.no_rows()) return 0;
+  const size_t rows = (size_t)s.B * s.Hq * s.Lq;
   return align_up(rows * sizeof(float));  // Delta_i = <dO_i, O_i>, one float per query row
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
 
+// Pointers of tensors that hold elements must be set and 16-byte aligned;
+// those of empty tensors are not used.
+bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned16(p)); }
+
 }  // namespace
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 100; }
+int sdpa_abi_version(void) { return 200; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -113,34 +139,40 @@ const char* sdpa_status_string(int status) {
   }
 }
 
-size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t L, int32_t D, int32_t dtype) {
-  Shape s{B, Hq, 1, L, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
+size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, int32_t dtype) {
+  Shape s{B, Hq, 1, Lq, 0, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
   if (check_shape(s) != SDPA_OK) return 0;
   return workspace_for(s);
 }
 
 int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
-                 int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                 int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
                  float scale, hipStream_t stream) {
-  const Shape s{B, Hq, group, L, D, dtype, mask, window, scale};
+  const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
-  if (s.empty()) return SDPA_OK;
-  const void* ptrs[] = {q, k, v, o, lse};
-  for (const void* p : ptrs)
-    if (p == nullptr || !aligned16(p)) return SDPA_ERR_INVALID_ARG;
-  const int w = s.w_eff();
+  if (s.no_rows()) return SDPA_OK;
+  const bool rows = true, keys = !s.no_keys();
+  if (!ptr_ok(q, rows) || !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(o, rows) || !ptr_ok(lse, rows))
+    return SDPA_ERR_INVALID_ARG;
+  int dlo, dhi;
+  s.band(dlo, dhi);
   if (dtype == SDPA_BF16) {
     switch (D) {
-      case 64: return to_status(sdpa::launch_qs<64, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
-      case 128: return to_status(sdpa::launch_qs<128, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
-      case 256: return to_status(sdpa::launch_qs<256, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
-      case 512: return to_status(sdpa::launch_qs<512, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq, group, L, w, scale, stream));
+#define SDPA_FWD_CASE(DD)                                                                                     \
+  case DD:                                                                                                    \
+    return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq,     \
+                                                       group, Lq, Lk, dlo, dhi, scale, stream));
+      SDPA_FWD_CASE(64)
+      SDPA_FWD_CASE(128)
+      SDPA_FWD_CASE(256)
+      SDPA_FWD_CASE(512)
+#undef SDPA_FWD_CASE
     }
   } else {
     switch (D) {
-      case 64: return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
-      case 128: return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, L, w, scale, stream));
+      case 64: return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+      case 128: return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
     }
   }
   return SDPA_ERR_UNSUPPORTED;
@@ -148,26 +180,29 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
 
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                   int32_t B, int32_t Hq, int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask,
-                   int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
+                   int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
+                   int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
                    hipEvent_t main_end) {
-  const Shape s{B, Hq, group, L, D, dtype, mask, window, scale};
+  const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
-  if (s.empty()) return SDPA_OK;
-  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (p == nullptr || !aligned16(p)) return SDPA_ERR_INVALID_ARG;
+  if (s.no_rows() && s.no_keys()) return SDPA_OK;
+  const bool rows = !s.no_rows(), keys = !s.no_keys();
+  if (!ptr_ok(q, rows) || !ptr_ok(o, rows) || !ptr_ok(dO, rows) || !ptr_ok(lse, rows) || !ptr_ok(dq, rows) ||
+      !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(dk, keys) || !ptr_ok(dv, keys))
+    return SDPA_ERR_INVALID_ARG;
   const size_t need = workspace_for(s);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SDPA_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return SDPA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
-  const int w = s.w_eff();
+  int dlo, dhi;
+  s.band(dlo, dhi);
   if (dtype == SDPA_BF16) {
     switch (D) {
-#define SDPA_BWD_CASE(DD)                                                                             \
-  case DD:                                                                                            \
-    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w, \
-                                               scale, stream, main_begin, main_end));
+#define SDPA_BWD_CASE(DD)                                                                                   \
+  case DD:                                                                                                  \
+    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, \
+                                               dlo, dhi, scale, stream, main_begin, main_end));
       SDPA_BWD_CASE(64)
       SDPA_BWD_CASE(128)
       SDPA_BWD_CASE(256)
@@ -177,11 +212,11 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
   } else {
     switch (D) {
       case 64:
-        return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
-                                                  scale, stream, main_begin, main_end));
+        return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
+                                                  dlo, dhi, scale, stream, main_begin, main_end));
       case 128:
-        return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, L, w,
-                                                   scale, stream, main_begin, main_end));
+        return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
+                                                   dlo, dhi, scale, stream, main_begin, main_end));
     }
   }
   return SDPA_ERR_UNSUPPORTED;
@@ -189,10 +224,10 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
-             int32_t group, int32_t L, int32_t D, int32_t dtype, int32_t mask, int32_t window, float scale,
-             hipStream_t stream) {
-  return sdpa_bwd_timed(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, L, D, dtype,
-                        mask, window, scale, stream, nullptr, nullptr);
+             int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+             float scale, hipStream_t stream) {
+  return sdpa_bwd_timed(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D,
+                        dtype, mask, window, scale, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

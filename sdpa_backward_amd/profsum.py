@@ -38,8 +38,9 @@ def sources_sha256() -> str:
 
 
 def tag(w) -> str:
-    mask = f"window{w.window}" if w.mask == "causal_window" else "causal"
-    return f"{mask}_L{w.L}_D{w.D}"
+    mask = {"causal_window": f"window{w.window}", "window": f"twosided{w.window}"}.get(w.mask, w.mask)
+    length = f"L{w.L}" if w.Lkv == w.L else f"Lq{w.L}_Lk{w.Lkv}"
+    return f"{mask}_{length}_D{w.D}"
 
 
 def short(name: str) -> str:
@@ -54,7 +55,7 @@ def roles(w):
     N = allowed_pairs(w)
     e = 2  # bf16
     q = w.B * w.Hq * w.L * w.D * e
-    kv = w.B * w.Hkv * w.L * w.D * e
+    kv = w.B * w.Hkv * w.Lkv * w.D * e
     row = w.B * w.Hq * w.L * 4
     D = w.D
     return {
@@ -112,7 +113,7 @@ def main():
     out = a.outdir
     script = "bash sdpa_backward_amd/collect_profiles.sh OUTDIR " + w.name
     wl = f"{w.name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, L={w.L}, D={w.D}, mask={w.mask}" + \
-         (f", window={w.window}" if w.mask == "causal_window" else "")
+         (f", Lk={w.Lkv}" if w.Lkv != w.L else "") + (f", window={w.window}" if w.window else "")
 
     # ---------------------------------------------------------------- kernel time
     tr = read_trace(os.path.join(out, "trace"))

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "sdpa.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 BF16, F32 = 0, 1
-NONE, CAUSAL, WINDOW = 0, 1, 2
+NONE, CAUSAL, WINDOW, TWO_SIDED = 0, 1, 2, 3
 FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
 
 
@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 100
+    assert lib.sdpa_abi_version() == 200
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -77,37 +77,43 @@ def test_workspace_is_linear_in_L(lib):
     assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, 7) == 0       # unknown dtype
 
 
-def fwd(lib, B=1, Hq=4, group=2, L=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
+def fwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
         ptrs=(FAKE,) * 5):
-    return lib.sdpa_fwd_lse(*[ctypes.c_void_p(p) for p in ptrs], B, Hq, group, L, D, dtype, mask, window,
+    """sdpa_fwd_lse; pointer order q, k, v, o, lse."""
+    return lib.sdpa_fwd_lse(*[ctypes.c_void_p(p) for p in ptrs], B, Hq, group, Lq, Lk, D, dtype, mask, window,
                             scale, None)
 
 
-def bwd(lib, B=1, Hq=4, group=2, L=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
+def bwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
         ptrs=(FAKE,) * 9, ws=FAKE, ws_bytes=1 << 40):
-    return lib.sdpa_bwd(*[ctypes.c_void_p(p) for p in ptrs], ctypes.c_void_p(ws), ws_bytes, B, Hq, group, L,
-                        D, dtype, mask, window, scale, None)
+    """sdpa_bwd; pointer order q, k, v, o, dO, lse, dq, dk, dv."""
+    return lib.sdpa_bwd(*[ctypes.c_void_p(p) for p in ptrs], ctypes.c_void_p(ws), ws_bytes, B, Hq, group, Lq,
+                        Lk, D, dtype, mask, window, scale, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
     ({"dtype": 2}, INVALID),
-    ({"mask": 3}, INVALID),
+    ({"mask": 4}, INVALID),
+    ({"mask": -1}, INVALID),
     ({"B": -1}, INVALID),
-    ({"L": -5}, INVALID),
+    ({"Lq": -5}, INVALID),
+    ({"Lk": -5}, INVALID),
     ({"Hq": -4}, INVALID),
     ({"D": 0}, INVALID),
     ({"group": 0}, INVALID),
     ({"Hq": 6, "group": 4}, INVALID),
     ({"mask": WINDOW, "window": 0}, INVALID),
+    ({"mask": TWO_SIDED, "window": 0}, INVALID),
+    ({"mask": TWO_SIDED, "window": -3}, INVALID),
     ({"scale": 0.0}, INVALID),
     ({"scale": -1.0}, INVALID),
     ({"scale": float("inf")}, INVALID),
     ({"scale": float("nan")}, INVALID),
-    ({"mask": NONE}, UNSUPPORTED),
     ({"D": 96}, UNSUPPORTED),
     ({"D": 1024}, UNSUPPORTED),
     ({"dtype": F32, "D": 256}, UNSUPPORTED),
     ({"Hq": 70000, "group": 1}, UNSUPPORTED),
+    ({"Lq": 1 << 29, "Lk": (1 << 29) + 1}, UNSUPPORTED),   # row / key indices plus offsets must fit int32
 ])
 def test_argument_errors(lib, kw, expect):
     assert fwd(lib, **kw) == expect
@@ -135,9 +141,36 @@ def test_workspace_errors(lib):
 
 
 def test_empty_problems_launch_nothing(lib):
-    for kw in ({"B": 0}, {"L": 0}, {"Hq": 0}):
+    for kw in ({"B": 0}, {"Lq": 0, "Lk": 0}, {"Hq": 0}):
         assert fwd(lib, ptrs=(0,) * 5, **kw) == OK
         assert bwd(lib, ptrs=(0,) * 9, ws=0, ws_bytes=0, **kw) == OK
+    # no query rows: the forward has nothing to write, whatever the keys
+    assert fwd(lib, Lq=0, Lk=64, ptrs=(0,) * 5) == OK
+
+
+def test_pointers_of_empty_tensors_are_not_checked(lib):
+    # no rows but keys: the backward still writes dK, dV (zeros), so those and
+    # K, V must be valid while Q, O, dO, lse, dQ may be null; a null one of
+    # the four is refused before any launch
+    for n in (1, 2, 7, 8):
+        p = [0] * 9
+        for m in (1, 2, 7, 8):
+            p[m] = FAKE
+        p[n] = 0
+        assert bwd(lib, Lq=0, Lk=64, ptrs=p, ws=0, ws_bytes=0) == INVALID
+    # keys but no rows in the forward: returns before looking at any pointer
+    assert fwd(lib, Lq=0, Lk=64, ptrs=(0, FAKE + 2, 0, 0, 0)) == OK
+    # rows but no keys: Q, O, lse (forward) must be valid
+    for n in (0, 3, 4):
+        p = [FAKE, 0, 0, FAKE, FAKE]
+        p[n] = 0
+        assert fwd(lib, Lk=0, ptrs=p) == INVALID
+    # ... and Q, O, dO, lse, dQ (backward), with the workspace
+    for n in (0, 3, 4, 5, 6):
+        p = [FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, 0, 0]
+        p[n] = 0
+        assert bwd(lib, Lk=0, ptrs=p) == INVALID
+    assert bwd(lib, Lk=0, ptrs=[FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, 0, 0], ws=0) == WORKSPACE
 
 
 def test_binding_refuses_cpu_tensors():

@@ -168,7 +168,7 @@ def _sample_keys(w, rng):
 def _poisoned_outputs(w):
     """Output buffers prefilled with NaN, each followed by a canary tail."""
     shapes = {"O": (w.B, w.Hq, w.L, w.D), "lse": (w.B, w.Hq, w.L), "dQ": (w.B, w.Hq, w.L, w.D),
-              "dK": (w.B, w.Hkv, w.L, w.D), "dV": (w.B, w.Hkv, w.L, w.D)}
+              "dK": (w.B, w.Hkv, w.Lkv, w.D), "dV": (w.B, w.Hkv, w.Lkv, w.D)}
     bufs, views = {}, {}
     for n, shp in shapes.items():
         dt = torch.float32 if n == "lse" else w.torch_dtype
@@ -302,6 +302,8 @@ def test_binding_errors_are_raised():
     q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
     k = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(SdpaError):
-        sdpa_fwd_lse(q, k, k, "none")            # no mask mode is reserved
-    with pytest.raises(SdpaError):
         sdpa_fwd_lse(q, k, k, "causal_window", 0)
+    with pytest.raises(SdpaError):
+        sdpa_fwd_lse(q, k, k, "window", 0)
+    with pytest.raises(ValueError):
+        sdpa_fwd_lse(q, k, k, "sliding")       # not a mask name

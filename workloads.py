@@ -25,8 +25,10 @@ from typing import Optional
 
 import torch
 
+MASK_NONE = "none"
 MASK_CAUSAL = "causal"
-MASK_WINDOW = "causal_window"
+MASK_WINDOW = "causal_window"      # window keys up to and including the diagonal
+MASK_TWO_SIDED = "window"          # window - 1 keys on either side of the diagonal, no causal mask
 
 
 @dataclass(frozen=True)
@@ -38,9 +40,14 @@ class Workload:
     L: int
     D: int
     dtype: str          # "bf16" or "f32"
-    mask: str           # MASK_CAUSAL or MASK_WINDOW
-    window: int = 0     # keys per query row (diagonal included); 0 for plain causal
+    mask: str           # MASK_NONE, MASK_CAUSAL, MASK_WINDOW or MASK_TWO_SIDED
+    window: int = 0     # window size (diagonal included); 0 without a window
     seed: int = 1000
+    Lk: Optional[int] = None  # keys (default L); the L queries are the last L of the Lk positions
+
+    @property
+    def Lkv(self) -> int:
+        return self.L if self.Lk is None else self.Lk
 
     @property
     def group(self) -> int:
@@ -66,7 +73,18 @@ CONFIGS = [
     Workload("bf16_window1024_L16384_D256_h32kv16", 1, 32, 16, 16384, 256, "bf16", MASK_WINDOW, 1024, 1003),
     Workload("bf16_window1024_ragged_L30553_D256_h32kv16", 1, 32, 16, 30553, 256, "bf16", MASK_WINDOW, 1024, 1004),
 ]
-BY_NAME = {w.name: w for w in CONFIGS}
+# The variants beside them, at the sliding layers' geometry: the window on
+# both sides of the diagonal, the queries as the last quarter of the key
+# positions (keys behind every query's window must get zero gradients), and
+# no mask at all (page "Lab 028 lab detail: Off NVIDIA, you fix the platform
+# yourself", "What I changed, in plain terms", items 3-5).
+VARIANTS = [
+    Workload("bf16_twosided_window1024_L16384_D256_h32kv16", 1, 32, 16, 16384, 256, "bf16", MASK_TWO_SIDED, 1024, 1005),
+    Workload("bf16_window1024_Lq4096_Lk16384_D256_h32kv16", 1, 32, 16, 4096, 256, "bf16", MASK_WINDOW, 1024, 1006,
+             Lk=16384),
+    Workload("bf16_nomask_L4096_D256_h32kv16", 1, 32, 16, 4096, 256, "bf16", MASK_NONE, 0, 1007),
+]
+BY_NAME = {w.name: w for w in CONFIGS + VARIANTS}
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
@@ -74,8 +92,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     g = torch.Generator(device="cpu").manual_seed(w.seed if seed is None else seed)
     shapes = {
         "q": (w.B, w.Hq, w.L, w.D),
-        "k": (w.B, w.Hkv, w.L, w.D),
-        "v": (w.B, w.Hkv, w.L, w.D),
+        "k": (w.B, w.Hkv, w.Lkv, w.D),
+        "v": (w.B, w.Hkv, w.Lkv, w.D),
         "do": (w.B, w.Hq, w.L, w.D),
     }
     out = {}
