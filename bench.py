@@ -35,7 +35,7 @@ BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public figure (no spar
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_window1024_L16384_D256_h32kv16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv_kernel_window1024_L16384_D256.json")
-MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_bf16.hip", "sdpa_backward_amd/csrc/common.h"]
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
 
 
 def log(*a):

@@ -48,8 +48,10 @@
  * Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
  * contiguous row-major: Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
  * [B, Hq/group, Lk, D]; lse [B, Hq, Lq] float32. Element type: bfloat16
- * (SDPA_BF16) or float32 (SDPA_F32) for Q, K, V, O, dO, dQ, dK, dV; lse is
- * always float32. Pointers of non-empty tensors must be non-null and 16-byte
+ * (SDPA_BF16), float16 (SDPA_F16) or float32 (SDPA_F32) for Q, K, V, O, dO,
+ * dQ, dK, dV; lse is always float32. The 16-bit types run on the matrix
+ * cores with fp32 accumulation, S, dP and the softmax state in fp32, and P and
+ * dS rounded to the input type as operands; float32 runs in fp32 throughout. Pointers of non-empty tensors must be non-null and 16-byte
  * aligned (pointers of tensors with no elements are not read). Outputs must
  * not alias inputs. The library never allocates device memory: the
  * backward's scratch space is the caller's `workspace` buffer.
@@ -83,13 +85,13 @@ enum sdpa_status {
                                 window < 1 with a window mask, scale not
                                 finite or <= 0, unknown enum, misaligned ptr */
   SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64,128,256,512}
-                                (bf16) / {64,128} (f32); Lq + Lk > 2^30; B or
-                                Hq > 65535 */
+                                (bf16, f16) / {64,128} (f32); Lq + Lk > 2^30;
+                                B or Hq > 65535 */
   SDPA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
   SDPA_ERR_LAUNCH = -4       /* the HIP runtime reported a launch error */
 };
 
-enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F32 = 1 };
+enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F32 = 1, SDPA_F16 = 2 };
 
 enum sdpa_mask {
   SDPA_MASK_NONE = 0,

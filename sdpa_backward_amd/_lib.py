@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 SDPA_OK = 0
 STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", -3: "SDPA_ERR_WORKSPACE",
           -4: "SDPA_ERR_LAUNCH"}
-DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
 EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_timed", "sdpa_bwd_workspace_bytes", "sdpa_status_string",

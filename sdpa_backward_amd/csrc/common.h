@@ -1,7 +1,8 @@
 // Device-side building blocks shared by the gfx950 attention kernels.
 //
-// MFMA used: v_mfma_f32_32x32x16_bf16 (wave64). Lane layouts (checked on the
-// hardware):
+// MFMA used: v_mfma_f32_32x32x16_bf16 and its float16 twin
+// v_mfma_f32_32x32x16_f16 (wave64), which share these lane layouts (checked
+// on the hardware for bf16; the fp16 parity tests cover the other):
 //   A (32x16, M x K): lane l holds row l%32, k-slots for half h = l/32
 //   B (16x32, K x N): lane l holds col l%32, k-slots for half h = l/32
 //   C (32x32 fp32):   lane l holds col l%32, rows 8*(i/4) + 4*h + (i%4), i = 0..15
@@ -19,7 +20,7 @@
 // column c0 + 4*(i%4) of a row-major tile, lane j receives column c0 + j,
 // rows r0..r0+3: a 4x16 block arrives transposed.
 //
-// LDS tiles are row-major bf16 [rows][D] with no padding; the 16-byte chunk c
+// LDS tiles are row-major 16-bit [rows][D] with no padding; the 16-byte chunk c
 // of row r sits at chunk slot c ^ swz(r). swz maps 16 consecutive rows to 16
 // distinct slots (conflict-free 16-byte reads of one column chunk across rows)
 // and 4 consecutive rows to 4 distinct chunk pairs (transposed reads).
@@ -39,6 +40,10 @@
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -51,8 +56,27 @@ namespace sdpa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// The 16-bit input types (bfloat16, float16) share every kernel: the two MFMAs
+// below have the same shape, lane layouts and fp32 accumulator; only the
+// operand format and the rounding of P, dS and the outputs differ.
+template <typename E>
+struct Vec;
+template <>
+struct Vec<bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+};
+template <>
+struct Vec<f16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+};
+
 SDPA_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+SDPA_DEV f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 SDPA_DEV f32x16 zero16() {
@@ -62,22 +86,25 @@ SDPA_DEV f32x16 zero16() {
   return z;
 }
 
-SDPA_DEV bf16x8 zero_bf16x8() {
-  bf16x8 z;
+template <typename E>
+SDPA_DEV typename Vec<E>::x8 zero8() {
+  typename Vec<E>::x8 z;
 #pragma unroll
-  for (int i = 0; i < 8; i++) z[i] = (bf16)0.f;
+  for (int i = 0; i < 8; i++) z[i] = (E)0.f;
   return z;
 }
 
 // Row of the C tile held in accumulator slot i by a lane in half h.
 SDPA_DEV int c_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// fp32 C-tile values [8*op, 8*op+8) as a bf16 "paired" operand (rows of the
-// C tile become k: op 0 covers C rows 0..15, op 1 rows 16..31).
-SDPA_DEV bf16x8 c_to_op(const f32x16& c, int op) {
-  bf16x8 r;
+// fp32 C-tile values [8*op, 8*op+8) as a 16-bit "paired" operand (rows of the
+// C tile become k: op 0 covers C rows 0..15, op 1 rows 16..31), rounded to
+// nearest even.
+template <typename E>
+SDPA_DEV typename Vec<E>::x8 c_to_op(const f32x16& c, int op) {
+  typename Vec<E>::x8 r;
 #pragma unroll
-  for (int j = 0; j < 8; j++) r[j] = (bf16)c[8 * op + j];
+  for (int j = 0; j < 8; j++) r[j] = (E)c[8 * op + j];
   return r;
 }
 
@@ -97,6 +124,7 @@ SDPA_DEV float half_sum(float x) {
 // and write AGPRs directly; only VALU arithmetic needs VGPRs).
 SDPA_DEV void keep_in_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
 SDPA_DEV void keep_in_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
+SDPA_DEV void keep_in_agpr(f16x8& x) { asm volatile("" : "+a"(x)); }
 
 // x[t] *= a for accumulator tiles that stay in AGPRs: each element is read
 // into a VGPR, multiplied and written back inside one asm statement, so the
@@ -186,33 +214,34 @@ struct LaneAddr {
   }
 };
 
-// 4 consecutive bf16 of a row-major LDS tile, delivered transposed across
-// each 16-lane group (see header comment).
-SDPA_DEV bf16x4 lds_tr4(const char* p) {
+// 4 consecutive 16-bit elements of a row-major LDS tile, delivered transposed
+// across each 16-lane group (see header comment).
+template <typename E>
+SDPA_DEV typename Vec<E>::x4 lds_tr4(const char* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, r);
+  return __builtin_bit_cast(typename Vec<E>::x4, r);
 }
 
 // Operand from a swizzled tile T[k][mn] (rows are the contraction index):
 // lane l gets column mn0 + l%32 with "paired" k-slots over rows [k0, k0+16).
 // k0: multiple of 16; mn0: multiple of 32.
-template <int D>
-SDPA_DEV bf16x8 op_tr(const bf16* T, const LaneAddr<D>& a, int k0, int mn0) {
+template <int D, typename E>
+SDPA_DEV typename Vec<E>::x8 op_tr(const E* T, const LaneAddr<D>& a, int k0, int mn0) {
   const int q = mn0 / 32;  // 4 chunks per 32-column block
   const char* base = reinterpret_cast<const char*>(T) + k0 * D * 2 + (q >> 2) * 256;
-  bf16x4 lo = lds_tr4(base + a.trn[2 * (q & 3)]);
-  bf16x4 hi = lds_tr4(base + a.trn[2 * (q & 3) + 1]);
+  const typename Vec<E>::x4 lo = lds_tr4<E>(base + a.trn[2 * (q & 3)]);
+  const typename Vec<E>::x4 hi = lds_tr4<E>(base + a.trn[2 * (q & 3) + 1]);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Operand from a swizzled tile T[mn][k] (columns are the contraction index):
 // lane l gets row mn0 + l%32 with "direct" k-slots k0 + 8*(l/32) + j.
 // k0: multiple of 16; mn0: multiple of 32.
-template <int D>
-SDPA_DEV bf16x8 op_direct(const bf16* T, const LaneAddr<D>& a, int k0, int mn0) {
+template <int D, typename E>
+SDPA_DEV typename Vec<E>::x8 op_direct(const E* T, const LaneAddr<D>& a, int k0, int mn0) {
   const int c = k0 / 8;  // even
   const char* p = reinterpret_cast<const char*>(T) + a.dir[(c & 15) >> 1] + (c >> 4) * 256 + mn0 * D * 2;
-  return *(const bf16x8*)p;
+  return *(const typename Vec<E>::x8*)p;
 }
 
 // Asynchronous global->LDS tile loads through a buffer resource. A wave
@@ -241,17 +270,18 @@ struct TileLoader {
   }
   // Resource covering rows [0, min(valid, R)) of the [R][D] tile starting at
   // src (row stride D); valid <= 0 gives an empty range (loads read nothing).
-  SDPA_DEV static __amdgpu_buffer_rsrc_t rsrc_of(const bf16* src, int valid) {
+  SDPA_DEV static __amdgpu_buffer_rsrc_t rsrc_of(const void* src, int valid) {
     const int rows = __builtin_amdgcn_readfirstlane(valid < 0 ? 0 : valid < R ? valid : R);  // uniform
     return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
   }
   // This wave's block jj of a tile (jj < NJ, and jj * NW + w < PER).
-  SDPA_DEV void issue_one(bf16* lds, __amdgpu_buffer_rsrc_t rsrc, int jj, int w) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + (jj * NW + w) * 512),
+  SDPA_DEV void issue_one(void* lds, __amdgpu_buffer_rsrc_t rsrc, int jj, int w) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+                                             (__attribute__((address_space(3))) void*)((char*)lds + (jj * NW + w) * 1024),
                                              16, (int)voff[jj], 0, 0, 0);
   }
   // Rows [0, min(valid, R)) of the [R][D] tile starting at src (row stride D).
-  SDPA_DEV void issue(bf16* lds, const bf16* src, int valid, int w) const {
+  SDPA_DEV void issue(void* lds, const void* src, int valid, int w) const {
     const int rows = valid < R ? valid : R;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
@@ -259,16 +289,18 @@ struct TileLoader {
     for (int jj = 0; jj < NJ; jj++) {
       const int j = jj * NW + w;
       if (PER % NW != 0 && j >= PER) break;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + j * 512), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)((char*)lds + j * 1024), 16,
                                                (int)voff[jj], 0, 0, 0);
     }
   }
 };
 
-// Zero n bf16 elements of an LDS buffer with the workgroup's 256 threads
+// Zero n 16-bit elements of an LDS buffer with the workgroup's 256 threads
 // (n a multiple of 8 * 256).
-SDPA_DEV void zero_lds(bf16* p, int n, int tid) {
-  for (int i = tid * 8; i < n; i += 256 * 8) *(bf16x8*)(p + i) = zero_bf16x8();
+template <typename E>
+SDPA_DEV void zero_lds(E* p, int n, int tid) {
+  const i32x4 z = {0, 0, 0, 0};
+  for (int i = tid * 8; i < n; i += 256 * 8) *(i32x4*)(p + i) = z;
 }
 
 // Wait for this wave's outstanding vector-memory loads and LDS operations,

@@ -1,4 +1,4 @@
-// Key-stationary dK/dV kernel for gfx950 (bf16 in, fp32 accumulate).
+// Key-stationary dK/dV kernel for gfx950 (bf16 or fp16 in, fp32 accumulate).
 //
 // One workgroup = 4 waves = one (b, kv head g) and a block of BKT keys. It
 // walks every query tile of every q-head of the GQA group whose rows can see
@@ -8,8 +8,8 @@
 // 028 lab detail: Off NVIDIA, you fix the platform yourself", section "What I
 // changed, in plain terms", items 3-5). P is recomputed from S and the stored
 // lse and dS is formed per element (section "2026-10-21", "What the code
-// says"); S and dP stay in fp32 registers, only P and dS are rounded to bf16
-// as MFMA operands (section "fp32 score tiles").
+// says"); S and dP stay in fp32 registers, only P and dS are rounded to the
+// input type as MFMA operands (section "fp32 score tiles").
 //
 // Per query tile of 32 rows, per wave (owning 32 keys; for D = 512 two waves
 // share a key block and split the head dimension, adding their partial S and
@@ -59,19 +59,20 @@ SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
   lds_barrier();
 }
 
-template <int D, int PASS>
+template <int D, int PASS, typename E>
 __global__ void __launch_bounds__(256, 1)
-kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-          const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-          bf16* __restrict__ dK, bf16* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
+kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+          const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+          E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
           float scale, float scale_log2) {
   using C = KvCfg<D>;
+  using ex8 = typename Vec<E>::x8;
   constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
-  __shared__ __attribute__((aligned(16))) bf16 ks[C::BKT * D];
-  __shared__ __attribute__((aligned(16))) bf16 qb0[QT];
-  __shared__ __attribute__((aligned(16))) bf16 db0[QT];
-  __shared__ __attribute__((aligned(16))) bf16 qb1[C::NBUF == 2 ? QT : 8];
-  __shared__ __attribute__((aligned(16))) bf16 db1[C::NBUF == 2 ? QT : 8];
+  __shared__ __attribute__((aligned(16))) E ks[C::BKT * D];
+  __shared__ __attribute__((aligned(16))) E qb0[QT];
+  __shared__ __attribute__((aligned(16))) E db0[QT];
+  __shared__ __attribute__((aligned(16))) E qb1[C::NBUF == 2 ? QT : 8];
+  __shared__ __attribute__((aligned(16))) E db1[C::NBUF == 2 ? QT : 8];
   __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * 1024 : 4];
   __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
   __shared__ __attribute__((aligned(16))) float rv1[64];
@@ -88,8 +89,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int k0 = kt * C::BKT;
   const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
-  const bf16* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const bf16* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const E* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const E* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
   // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist)
   const int ihi = min(Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
   const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
@@ -111,11 +112,11 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   ld.init(w, lane);
   // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
   constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
-  bf16x8 vreg[WANT_DK ? NKS : 1];
+  ex8 vreg[WANT_DK ? NKS : 1];
   if constexpr (WANT_DK) {
-    const bf16* vrow = Vg + (size_t)(kj < Lk ? kj : 0) * D;
+    const E* vrow = Vg + (size_t)(kj < Lk ? kj : 0) * D;
 #pragma unroll
-    for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const bf16x8*)(vrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+    for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const ex8*)(vrow + dw0 + 16 * s + 8 * hh) : zero8<E>();
   }
 
   f32x16 dkacc[WANT_DK ? NDB : 1], dvacc[WANT_DV ? NDB : 1];
@@ -134,7 +135,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int total = group * nq;
   const int kb1 = min(kb0 + 31, Lk - 1);  // this wave's last key (kb1 < kb0: none)
 
-  auto tile_src = [&](int it, const bf16*& qs, const bf16*& ds, int& q0) {
+  auto tile_src = [&](int it, const E*& qs, const E*& ds, int& q0) {
     const int hq = g * group + it / nq;
     q0 = (qt_lo + it % nq) * C::BQ;
     const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
@@ -151,8 +152,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
   };
-  auto issue = [&](int it, bf16* qd, bf16* dd, float* rv) {
-    const bf16 *qs, *ds;
+  auto issue = [&](int it, E* qd, E* dd, float* rv) {
+    const E *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
     ld.issue(qd, qs, Lq - q0, w);
@@ -163,7 +164,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   // P = exp(S - lse), dS = P (dP - Delta) from the score tiles, then
   // dV += P^T dO and dK += dS^T Q for the query tile whose rows start at q0.
   auto form_and_update = [&](int q0, bool full, const float* rv, f32x16& s_acc, f32x16& dp_acc,
-                             const bf16* Qc, const bf16* dOc) {
+                             const E* Qc, const E* dOc) {
   // P = exp(S - lse) and dS = P (dP - Delta); the element mask only on edge
   // tiles, as a select (the wave-uniform test stays outside the element loop)
   // row q0 + c_row(i, hh) is allowed for this lane's key iff it lies in
@@ -190,20 +191,20 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   };
   if (full) form(std::false_type{});
   else form(std::true_type{});
-  const bf16x8 pa0 = c_to_op(s_acc, 0), pa1 = c_to_op(s_acc, 1);
-  const bf16x8 da0 = c_to_op(dp_acc, 0), da1 = c_to_op(dp_acc, 1);
+  const ex8 pa0 = c_to_op<E>(s_acc, 0), pa1 = c_to_op<E>(s_acc, 1);
+  const ex8 da0 = c_to_op<E>(dp_acc, 0), da1 = c_to_op<E>(dp_acc, 1);
   (void)pa0; (void)pa1; (void)da0; (void)da1;
   constexpr int MPB = (WANT_DV ? 2 : 0) + (WANT_DK ? 2 : 0);  // MFMAs per head-dim block
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
     const int c0 = dw0 + 32 * d;
     if constexpr (WANT_DV) {
-      dvacc[d] = mfma(pa0, op_tr<D>(dOc, la, 0, c0), dvacc[d]);
-      dvacc[d] = mfma(pa1, op_tr<D>(dOc, la, 16, c0), dvacc[d]);
+      dvacc[d] = mfma(pa0, op_tr<D, E>(dOc, la, 0, c0), dvacc[d]);
+      dvacc[d] = mfma(pa1, op_tr<D, E>(dOc, la, 16, c0), dvacc[d]);
     }
     if constexpr (WANT_DK) {
-      dkacc[d] = mfma(da0, op_tr<D>(Qc, la, 0, c0), dkacc[d]);
-      dkacc[d] = mfma(da1, op_tr<D>(Qc, la, 16, c0), dkacc[d]);
+      dkacc[d] = mfma(da0, op_tr<D, E>(Qc, la, 0, c0), dkacc[d]);
+      dkacc[d] = mfma(da1, op_tr<D, E>(Qc, la, 16, c0), dkacc[d]);
     }
   }
   // schedule: transposed reads run one head-dim block ahead of their MFMAs
@@ -222,8 +223,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   // order (it writes LDS), so the operand reads are software-pipelined by hand
   // and the loads slot in between them. Past the last tile the resources cover
   // no rows (nothing is read).
-  auto compute = [&](auto prefetch, int it, const bf16* Qc, const bf16* dOc, const float* rv, bf16* qn,
-                     bf16* dn, float* rvn) {
+  auto compute = [&](auto prefetch, int it, const E* Qc, const E* dOc, const float* rv, E* qn,
+                     E* dn, float* rvn) {
     constexpr bool PF = decltype(prefetch)::value;
     const int q0 = (qt_lo + it % nq) * C::BQ;
     // some pair of the tile's rows and the wave's keys allowed / every pair allowed
@@ -234,7 +235,7 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     __amdgpu_buffer_rsrc_t qrs, drs;
     if constexpr (PF) {
       const bool more = it + 1 < total;
-      const bf16 *qs, *ds;
+      const E *qs, *ds;
       int q0n;
       tile_src(more ? it + 1 : it, qs, ds, q0n);
       qrs = decltype(ld)::rsrc_of(qs, more ? Lq - q0n : 0);
@@ -258,13 +259,13 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     {
       constexpr int NM = WANT_DK ? 2 * NKS : NKS, AH = KV_AHEAD, NLD = PF ? 2 * NJ : 0;
       constexpr int EVERY = NLD > 0 && NM / NLD > 0 ? NM / NLD : 1;
-      bf16x8 ra[AH], rb[AH];
+      ex8 ra[AH], rb[AH];
       auto rd = [&](int k) {
         if (k < NKS) {
-          ra[k % AH] = op_direct<D>(Qc, la, dw0 + 16 * k, 0);
-          rb[k % AH] = op_direct<D>(ks, la, dw0 + 16 * k, 32 * kwi);
+          ra[k % AH] = op_direct<D, E>(Qc, la, dw0 + 16 * k, 0);
+          rb[k % AH] = op_direct<D, E>(ks, la, dw0 + 16 * k, 32 * kwi);
         } else {
-          ra[k % AH] = op_direct<D>(dOc, la, dw0 + 16 * (k - NKS), 0);
+          ra[k % AH] = op_direct<D, E>(dOc, la, dw0 + 16 * (k - NKS), 0);
         }
       };
 #pragma unroll
@@ -316,50 +317,50 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     // flight" is vmcnt(NJ): at most one tile's worth of this wave's loads
     // outstanding (wave 0's extra lse/Delta load rides with the Q tile).
     constexpr int NJ = decltype(ld)::NJ;
-    auto issue_q = [&](int it, bool more, bf16* dst, float* rvd) {
-      const bf16 *qs, *ds;
+    auto issue_q = [&](int it, bool more, E* dst, float* rvd) {
+      const E *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
       ld.issue(dst, qs, more ? Lq - q0n : 0, w);
       if (w == 0) load_rows(it, rvd);
     };
-    auto issue_do = [&](int it, bool more, bf16* dst) {
-      const bf16 *qs, *ds;
+    auto issue_do = [&](int it, bool more, E* dst) {
+      const E *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
       ld.issue(dst, ds, more ? Lq - q0n : 0, w);
     };
     // S, then (dK pass) dP once dO has landed; operand reads pipelined by hand
-    auto sdp = [&](const bf16* Qc, const bf16* dOc, f32x16& s_acc, f32x16& dp_acc) {
+    auto sdp = [&](const E* Qc, const E* dOc, f32x16& s_acc, f32x16& dp_acc) {
       constexpr int AH = KV_AHEAD;
-      bf16x8 ra[AH], rb[AH];
+      ex8 ra[AH], rb[AH];
       s_acc = zero16();
       dp_acc = zero16();
 #pragma unroll
       for (int k = 0; k < AH; k++) {
-        ra[k] = op_direct<D>(Qc, la, dw0 + 16 * k, 0);
-        rb[k] = op_direct<D>(ks, la, dw0 + 16 * k, 32 * kwi);
+        ra[k] = op_direct<D, E>(Qc, la, dw0 + 16 * k, 0);
+        rb[k] = op_direct<D, E>(ks, la, dw0 + 16 * k, 32 * kwi);
       }
 #pragma unroll
       for (int k = 0; k < NKS; k++) {
         s_acc = mfma(ra[k % AH], rb[k % AH], s_acc);
         if (k + AH < NKS) {
-          ra[k % AH] = op_direct<D>(Qc, la, dw0 + 16 * (k + AH), 0);
-          rb[k % AH] = op_direct<D>(ks, la, dw0 + 16 * (k + AH), 32 * kwi);
+          ra[k % AH] = op_direct<D, E>(Qc, la, dw0 + 16 * (k + AH), 0);
+          rb[k % AH] = op_direct<D, E>(ks, la, dw0 + 16 * (k + AH), 32 * kwi);
         }
       }
       if constexpr (WANT_DK) {
         wait_vm_and_barrier<0>();  // dO(t) in every wave's part of the buffer
 #pragma unroll
-        for (int k = 0; k < AH; k++) ra[k] = op_direct<D>(dOc, la, dw0 + 16 * k, 0);
+        for (int k = 0; k < AH; k++) ra[k] = op_direct<D, E>(dOc, la, dw0 + 16 * k, 0);
 #pragma unroll
         for (int k = 0; k < NKS; k++) {
           dp_acc = mfma(ra[k % AH], vreg[k], dp_acc);
-          if (k + AH < NKS) ra[k % AH] = op_direct<D>(dOc, la, dw0 + 16 * (k + AH), 0);
+          if (k + AH < NKS) ra[k % AH] = op_direct<D, E>(dOc, la, dw0 + 16 * (k + AH), 0);
         }
       }
     };
-    auto tile = [&](int it, bf16* Qb, bf16* Db, float* rvc, float* rvn) {
+    auto tile = [&](int it, E* Qb, E* Db, float* rvc, float* rvn) {
       const int q0 = (qt_lo + it % nq) * C::BQ;
       const int r1 = min(q0 + 31, Lq - 1);
       const bool active = kb0 <= kb1 && q0 <= kb1 - dlo && r1 >= kb0 - dhi;
@@ -390,8 +391,8 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
-  bf16* dKg = dK + ((size_t)b * Hkv + g) * Lk * D;
-  bf16* dVg = dV + ((size_t)b * Hkv + g) * Lk * D;
+  E* dKg = dK + ((size_t)b * Hkv + g) * Lk * D;
+  E* dVg = dV + ((size_t)b * Hkv + g) * Lk * D;
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
     const int col = dw0 + 32 * d + (lane & 31);
@@ -399,14 +400,14 @@ kv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     for (int i = 0; i < 16; i++) {
       const int key = kb0 + c_row(i, hh);
       if (key < Lk) {
-        if constexpr (WANT_DK) dKg[(size_t)key * D + col] = (bf16)(dkacc[d][i] * scale);
-        if constexpr (WANT_DV) dVg[(size_t)key * D + col] = (bf16)dvacc[d][i];
+        if constexpr (WANT_DK) dKg[(size_t)key * D + col] = (E)(dkacc[d][i] * scale);
+        if constexpr (WANT_DV) dVg[(size_t)key * D + col] = (E)dvacc[d][i];
       }
     }
   }
 }
 
-template <int D>
+template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
                      int dhi, float scale, hipStream_t stream) {
@@ -415,27 +416,31 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   auto run = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, lse, delta, (bf16*)dk, (bf16*)dv, Hq, group, Lq, Lk,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k,
+                       (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk,
                        dlo, dhi, scale, scale * kLog2e);
     return hipGetLastError();
   };
   if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
-    const hipError_t e = run(kv_kernel<D, KV_DV>);
+    const hipError_t e = run(kv_kernel<D, KV_DV, E>);
     if (e != hipSuccess) return e;
-    return run(kv_kernel<D, KV_DK>);
+    return run(kv_kernel<D, KV_DK, E>);
   } else {
-    return run(kv_kernel<D, KV_BOTH>);
+    return run(kv_kernel<D, KV_BOTH, E>);
   }
 }
 
-#define SDPA_INST_KV(D)                                                                                  \
-  template hipError_t launch_kv<D>(const void*, const void*, const void*, const void*, const float*,    \
-                                   const float*, void*, void*, int, int, int, int, int, int, int, float, \
-                                   hipStream_t);
-SDPA_INST_KV(64)
-SDPA_INST_KV(128)
-SDPA_INST_KV(256)
-SDPA_INST_KV(512)
+#define SDPA_INST_KV(D, E)                                                                                \
+  template hipError_t launch_kv<D, E>(const void*, const void*, const void*, const void*, const float*,    \
+                                      const float*, void*, void*, int, int, int, int, int, int, int, float, \
+                                      hipStream_t);
+SDPA_INST_KV(64, bf16)
+SDPA_INST_KV(128, bf16)
+SDPA_INST_KV(256, bf16)
+SDPA_INST_KV(512, bf16)
+SDPA_INST_KV(64, f16)
+SDPA_INST_KV(128, f16)
+SDPA_INST_KV(256, f16)
+SDPA_INST_KV(512, f16)
 
 }  // namespace sdpa

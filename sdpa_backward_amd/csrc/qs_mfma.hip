@@ -1,4 +1,4 @@
-// Query-stationary attention kernels for gfx950 (bf16 in, fp32 accumulate):
+// Query-stationary attention kernels for gfx950 (bf16 or fp16 in, fp32 accumulate):
 //
 //   QS_FWD  forward: O and the per-row logsumexp (lse) that the backward reuses
 //           (page "Lab 028 lab detail: Off NVIDIA, you fix the platform
@@ -25,7 +25,7 @@
 //   DQ:  dP^T = V_tile . dO_w^T             A: V (LDS, direct)  B: dO_w (registers)
 //        P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - Delta)
 //        dQ^T += K^T . dS^T                 A: K (transposed reads) B: dS^T (C tile reused)
-// S, P, dP stay fp32; only P and dS are rounded to bf16 as MFMA operands
+// S, P, dP stay fp32; only P and dS are rounded to the input type as MFMA operands
 // (section "fp32 score tiles" of the Lab 028 page).
 #include <type_traits>
 
@@ -73,19 +73,21 @@ SDPA_DEV void exchange_add(f32x16 (&c)[N], float* xbuf, int w, int lane) {
     for (int i = 0; i < 16; i++) c[t][i] += xbuf[((p * N + t) * 16 + i) * 64 + lane];
 }
 
-template <int D, int MODE>
+template <int D, int MODE, typename E>
 __global__ void __launch_bounds__(256, 1)
-qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-          const bf16* __restrict__ O, const bf16* __restrict__ dO, float* __restrict__ LSE,
-          float* __restrict__ Delta, bf16* __restrict__ Out, int Hq, int group, int Lq, int Lk, int dlo,
+qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+          const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ LSE,
+          float* __restrict__ Delta, E* __restrict__ Out, int Hq, int group, int Lq, int Lk, int dlo,
           int dhi, float scale, float scale_log2) {
   using C = QsCfg<D>;
+  using ex8 = typename Vec<E>::x8;
+  using ex4 = typename Vec<E>::x4;
   constexpr int BK = C::BK, NMB = C::NMB, DW = C::DW, NKS = DW / 16, NDB = DW / 32;
   constexpr int NX = MODE == QS_DQ ? 2 * NMB : NMB;  // C tiles exchanged when the head dim is split
-  __shared__ __attribute__((aligned(16))) bf16 kb0[C::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 kb1[C::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 vb0[C::TILE];
-  __shared__ __attribute__((aligned(16))) bf16 vb1[C::TILE];
+  __shared__ __attribute__((aligned(16))) E kb0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E kb1[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb0[C::TILE];
+  __shared__ __attribute__((aligned(16))) E vb1[C::TILE];
   __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * NX * 1024 : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
@@ -101,8 +103,8 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
   const int Hkv = Hq / group, g = h / group;
   const size_t hrow = (size_t)b * Hq + h;
-  const bf16* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const bf16* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const E* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
+  const E* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
 
   const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
   const int qi = iw0 + (lane & 31);  // this lane's query row
@@ -112,25 +114,25 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int span = qok && jhi >= jlo ? jhi - jlo + 1 : 0;
 
   // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
-  bf16x8 qreg[NKS];
-  const bf16* qrow = Q + (hrow * Lq + (qok ? qi : 0)) * D;
+  ex8 qreg[NKS];
+  const E* qrow = Q + (hrow * Lq + (qok ? qi : 0)) * D;
 #pragma unroll
-  for (int s = 0; s < NKS; s++) qreg[s] = qok ? *(const bf16x8*)(qrow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+  for (int s = 0; s < NKS; s++) qreg[s] = qok ? *(const ex8*)(qrow + dw0 + 16 * s + 8 * hh) : zero8<E>();
 
-  bf16x8 dreg[MODE == QS_DQ ? NKS : 1];
+  ex8 dreg[MODE == QS_DQ ? NKS : 1];
   float lse2 = 0.f, dlt = 0.f;
   if constexpr (MODE == QS_DQ) {
-    const bf16* drow = dO + (hrow * Lq + (qok ? qi : 0)) * D;
-    const bf16* orow = O + (hrow * Lq + (qok ? qi : 0)) * D;
+    const E* drow = dO + (hrow * Lq + (qok ? qi : 0)) * D;
+    const E* orow = O + (hrow * Lq + (qok ? qi : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < NKS; s++) dreg[s] = qok ? *(const bf16x8*)(drow + dw0 + 16 * s + 8 * hh) : zero_bf16x8();
+    for (int s = 0; s < NKS; s++) dreg[s] = qok ? *(const ex8*)(drow + dw0 + 16 * s + 8 * hh) : zero8<E>();
     // Delta_i = <dO_i, O_i> over the whole head dimension, fp32
     float dot = 0.f;
     if (qok) {
 #pragma unroll 4
       for (int s = 0; s < D / 16; s++) {
-        const bf16x8 a = *(const bf16x8*)(drow + 16 * s + 8 * hh);
-        const bf16x8 o = *(const bf16x8*)(orow + 16 * s + 8 * hh);
+        const ex8 a = *(const ex8*)(drow + 16 * s + 8 * hh);
+        const ex8 o = *(const ex8*)(orow + 16 * s + 8 * hh);
 #pragma unroll
         for (int j = 0; j < 8; j++) dot += (float)a[j] * (float)o[j];
       }
@@ -151,7 +153,7 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   const int kt_lo = klo / BK, kt_hi = klo <= khi ? khi / BK : kt_lo - 1;
   const int wr0 = iw0, wr1 = min(iw0 + 31, Lq - 1);  // this wave's rows (wr1 < wr0: none)
 
-  auto step = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
+  auto step = [&](int kt, const E* Kc, const E* Vc, E* Kn, E* Vn) {
     // The next tile's loads (into the other buffers) are issued one at a time
     // between the score MFMAs below: issued back to back they stall the wave
     // until the CU's vector-memory path has taken the workgroup's whole tile.
@@ -190,10 +192,10 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     {
       constexpr int NM = NMB * NKS, AH = QS_AHEAD_S, NLD = 2 * NJ;
       constexpr int EVERY = NM / NLD > 0 ? NM / NLD : 1;  // MFMA steps between loads
-      bf16x8 ka[AH], va[MODE == QS_DQ ? AH : 1];
+      ex8 ka[AH], va[MODE == QS_DQ ? AH : 1];
       auto rd = [&](int k) {
-        ka[k % AH] = op_direct<D>(Kc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
-        if constexpr (MODE == QS_DQ) va[k % AH] = op_direct<D>(Vc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
+        ka[k % AH] = op_direct<D, E>(Kc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
+        if constexpr (MODE == QS_DQ) va[k % AH] = op_direct<D, E>(Vc, la, dw0 + 16 * (k % NKS), 32 * (k / NKS));
       };
 #pragma unroll
       for (int k = 0; k < AH; k++) rd(k);
@@ -250,11 +252,11 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
       lsum += half_sum(rs);
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
-        const bf16x8 p0 = c_to_op(st[mb], 0), p1 = c_to_op(st[mb], 1);
+        const ex8 p0 = c_to_op<E>(st[mb], 0), p1 = c_to_op<E>(st[mb], 1);
 #pragma unroll
         for (int d = 0; d < NDB; d++) {
-          acc[d] = mfma(op_tr<D>(Vc, la, 32 * mb, dw0 + 32 * d), p0, acc[d]);
-          acc[d] = mfma(op_tr<D>(Vc, la, 32 * mb + 16, dw0 + 32 * d), p1, acc[d]);
+          acc[d] = mfma(op_tr<D, E>(Vc, la, 32 * mb, dw0 + 32 * d), p0, acc[d]);
+          acc[d] = mfma(op_tr<D, E>(Vc, la, 32 * mb + 16, dw0 + 32 * d), p1, acc[d]);
         }
       }
       // schedule: transposed reads run QS_AHEAD_O MFMAs ahead
@@ -279,11 +281,11 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
         };
         if (full) form(std::false_type{});
         else form(std::true_type{});
-        const bf16x8 d0 = c_to_op(st[NMB + mb], 0), d1 = c_to_op(st[NMB + mb], 1);
+        const ex8 d0 = c_to_op<E>(st[NMB + mb], 0), d1 = c_to_op<E>(st[NMB + mb], 1);
 #pragma unroll
         for (int d = 0; d < NDB; d++) {
-          acc[d] = mfma(op_tr<D>(Kc, la, 32 * mb, dw0 + 32 * d), d0, acc[d]);
-          acc[d] = mfma(op_tr<D>(Kc, la, 32 * mb + 16, dw0 + 32 * d), d1, acc[d]);
+          acc[d] = mfma(op_tr<D, E>(Kc, la, 32 * mb, dw0 + 32 * d), d0, acc[d]);
+          acc[d] = mfma(op_tr<D, E>(Kc, la, 32 * mb + 16, dw0 + 32 * d), d1, acc[d]);
         }
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * QS_AHEAD_O, 1);
@@ -315,17 +317,17 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
   }
 
   if (!qok) return;
-  bf16* orow = Out + (hrow * Lq + qi) * D;
+  E* orow = Out + (hrow * Lq + qi) * D;
   if constexpr (MODE == QS_FWD) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int d = 0; d < NDB; d++)
 #pragma unroll
       for (int blk = 0; blk < 4; blk++) {
-        bf16x4 v;
+        ex4 v;
 #pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = (bf16)(acc[d][4 * blk + r] * inv);
-        *(bf16x4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+        for (int r = 0; r < 4; r++) v[r] = (E)(acc[d][4 * blk + r] * inv);
+        *(ex4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
       }
     if (dsi == 0 && hh == 0) LSE[hrow * Lq + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
   } else {
@@ -333,15 +335,15 @@ qs_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __
     for (int d = 0; d < NDB; d++)
 #pragma unroll
       for (int blk = 0; blk < 4; blk++) {
-        bf16x4 v;
+        ex4 v;
 #pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = (bf16)(acc[d][4 * blk + r] * scale);
-        *(bf16x4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+        for (int r = 0; r < 4; r++) v[r] = (E)(acc[d][4 * blk + r] * scale);
+        *(ex4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
       }
   }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
                      float scale, hipStream_t stream) {
@@ -349,22 +351,26 @@ hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o,
   const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((qs_kernel<D, MODE>), dim3((unsigned)nwg), dim3(256), 0, stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (const bf16*)o, (const bf16*)dO, lse, delta, (bf16*)out,
+  hipLaunchKernelGGL((qs_kernel<D, MODE, E>), dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q,
+                     (const E*)k, (const E*)v, (const E*)o, (const E*)dO, lse, delta, (E*)out,
                      Hq, group, Lq, Lk, dlo, dhi, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
-#define SDPA_INST_QS(D)                                                                                 \
-  template hipError_t launch_qs<D, QS_FWD>(const void*, const void*, const void*, const void*,          \
-                                           const void*, float*, float*, void*, int, int, int, int, int, \
-                                           int, int, float, hipStream_t);                                         \
-  template hipError_t launch_qs<D, QS_DQ>(const void*, const void*, const void*, const void*,           \
-                                          const void*, float*, float*, void*, int, int, int, int, int,  \
-                                          int, int, float, hipStream_t);
-SDPA_INST_QS(64)
-SDPA_INST_QS(128)
-SDPA_INST_QS(256)
-SDPA_INST_QS(512)
+#define SDPA_INST_QS(D, E)                                                                                  \
+  template hipError_t launch_qs<D, QS_FWD, E>(const void*, const void*, const void*, const void*, const void*, \
+                                              float*, float*, void*, int, int, int, int, int, int, int, float,   \
+                                              hipStream_t);                                                    \
+  template hipError_t launch_qs<D, QS_DQ, E>(const void*, const void*, const void*, const void*, const void*,  \
+                                             float*, float*, void*, int, int, int, int, int, int, int, float,    \
+                                             hipStream_t);
+SDPA_INST_QS(64, bf16)
+SDPA_INST_QS(128, bf16)
+SDPA_INST_QS(256, bf16)
+SDPA_INST_QS(512, bf16)
+SDPA_INST_QS(64, f16)
+SDPA_INST_QS(128, f16)
+SDPA_INST_QS(256, f16)
+SDPA_INST_QS(512, f16)
 
 }  // namespace sdpa

@@ -16,11 +16,11 @@
 
 namespace sdpa {
 enum { QS_FWD = 0, QS_DQ = 1 };
-template <int D, int MODE>
+template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
                      float scale, hipStream_t stream);
-template <int D>
+template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
                      int dhi, float scale, hipStream_t stream);
@@ -32,19 +32,19 @@ hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, co
                           void*, void*, void*, float*, int, int, int, int, int, int, int, float, hipStream_t,
                           hipEvent_t, hipEvent_t);
 
-// bf16 backward: dQ pass (also writes Delta), then the dK/dV pass; the
+// 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass; the
 // optional events bracket the dK/dV kernel.
-template <int D>
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+template <int D, typename E>
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream,
                            hipEvent_t ev0, hipEvent_t ev1) {
-  hipError_t e = launch_qs<D, QS_DQ>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, Lq, Lk,
+  hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, Lq, Lk,
                                      dlo, dhi, scale, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream);
+  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -85,7 +85,7 @@ struct Shape {
 };
 
 bool d_supported(int dtype, int D) {
-  if (dtype == SDPA_BF16) return D == 64 || D == 128 || D == 256 || D == 512;
+  if (dtype == SDPA_BF16 || dtype == SDPA_F16) return D == 64 || D == 128 || D == 256 || D == 512;
   return D == 64 || D == 128;
 }
 
@@ -93,7 +93,7 @@ bool windowed(int mask) { return mask == SDPA_MASK_CAUSAL_WINDOW || mask == SDPA
 
 // Shape checks shared by both entry points (pointers are checked by the caller).
 int check_shape(const Shape& s) {
-  if (s.dtype != SDPA_BF16 && s.dtype != SDPA_F32) return SDPA_ERR_INVALID_ARG;
+  if (s.dtype != SDPA_BF16 && s.dtype != SDPA_F32 && s.dtype != SDPA_F16) return SDPA_ERR_INVALID_ARG;
   if (s.mask != SDPA_MASK_NONE && s.mask != SDPA_MASK_CAUSAL && !windowed(s.mask)) return SDPA_ERR_INVALID_ARG;
   if (s.B < 0 || s.Hq < 0 || s.Lq < 0 || s.Lk < 0 || s.D <= 0 || s.group <= 0) return SDPA_ERR_INVALID_ARG;
   if (s.Hq % s.group != 0) return SDPA_ERR_INVALID_ARG;
@@ -157,23 +157,24 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
     return SDPA_ERR_INVALID_ARG;
   int dlo, dhi;
   s.band(dlo, dhi);
-  if (dtype == SDPA_BF16) {
-    switch (D) {
-#define SDPA_FWD_CASE(DD)                                                                                     \
-  case DD:                                                                                                    \
-    return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD>(q, k, v, nullptr, nullptr, lse, nullptr, o, B, Hq,     \
-                                                       group, Lq, Lk, dlo, dhi, scale, stream));
-      SDPA_FWD_CASE(64)
-      SDPA_FWD_CASE(128)
-      SDPA_FWD_CASE(256)
-      SDPA_FWD_CASE(512)
+  switch (dtype * 1000 + D) {
+#define SDPA_FWD_CASE(DT, E, DD)                                                                          \
+  case DT * 1000 + DD:                                                                                    \
+    return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, B,  \
+                                                          Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+    SDPA_FWD_CASE(SDPA_BF16, bf16, 64)
+    SDPA_FWD_CASE(SDPA_BF16, bf16, 128)
+    SDPA_FWD_CASE(SDPA_BF16, bf16, 256)
+    SDPA_FWD_CASE(SDPA_BF16, bf16, 512)
+    SDPA_FWD_CASE(SDPA_F16, f16, 64)
+    SDPA_FWD_CASE(SDPA_F16, f16, 128)
+    SDPA_FWD_CASE(SDPA_F16, f16, 256)
+    SDPA_FWD_CASE(SDPA_F16, f16, 512)
 #undef SDPA_FWD_CASE
-    }
-  } else {
-    switch (D) {
-      case 64: return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
-      case 128: return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
-    }
+    case SDPA_F32 * 1000 + 64:
+      return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+    case SDPA_F32 * 1000 + 128:
+      return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
   }
   return SDPA_ERR_UNSUPPORTED;
 }
@@ -197,27 +198,26 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
   float* delta = static_cast<float*>(workspace);
   int dlo, dhi;
   s.band(dlo, dhi);
-  if (dtype == SDPA_BF16) {
-    switch (D) {
-#define SDPA_BWD_CASE(DD)                                                                                   \
-  case DD:                                                                                                  \
-    return to_status(sdpa::launch_bwd_bf16<DD>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, \
-                                               dlo, dhi, scale, stream, main_begin, main_end));
-      SDPA_BWD_CASE(64)
-      SDPA_BWD_CASE(128)
-      SDPA_BWD_CASE(256)
-      SDPA_BWD_CASE(512)
+  switch (dtype * 1000 + D) {
+#define SDPA_BWD_CASE(DT, E, DD)                                                                           \
+  case DT * 1000 + DD:                                                                                     \
+    return to_status(sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, \
+                                                  Lk, dlo, dhi, scale, stream, main_begin, main_end));
+    SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
+    SDPA_BWD_CASE(SDPA_BF16, bf16, 128)
+    SDPA_BWD_CASE(SDPA_BF16, bf16, 256)
+    SDPA_BWD_CASE(SDPA_BF16, bf16, 512)
+    SDPA_BWD_CASE(SDPA_F16, f16, 64)
+    SDPA_BWD_CASE(SDPA_F16, f16, 128)
+    SDPA_BWD_CASE(SDPA_F16, f16, 256)
+    SDPA_BWD_CASE(SDPA_F16, f16, 512)
 #undef SDPA_BWD_CASE
-    }
-  } else {
-    switch (D) {
-      case 64:
-        return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                  dlo, dhi, scale, stream, main_begin, main_end));
-      case 128:
-        return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                   dlo, dhi, scale, stream, main_begin, main_end));
-    }
+    case SDPA_F32 * 1000 + 64:
+      return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
+                                                dlo, dhi, scale, stream, main_begin, main_end));
+    case SDPA_F32 * 1000 + 128:
+      return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
+                                                 dlo, dhi, scale, stream, main_begin, main_end));
   }
   return SDPA_ERR_UNSUPPORTED;
 }

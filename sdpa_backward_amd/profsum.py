@@ -24,7 +24,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_bf16.hip", "sdpa_backward_amd/csrc/common.h"]
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
 COPY_KERNEL = "copyBuffer"   # the 1 GiB device copy bench.py --copy-probe runs
 COPY_BYTES = 1 << 30
 
@@ -44,8 +44,10 @@ def tag(w) -> str:
 
 
 def short(name: str) -> str:
+    """Kernel name without its signature and element type: sdpa::kv_kernel<256, 0>."""
     name = name.replace("void ", "")
     name = re.sub(r"\(.*", "", name)
+    name = re.sub(r"<(\d+), (\d+), [^<>]+>", r"<\1, \2>", name)  # the workloads here are bf16
     return name
 
 

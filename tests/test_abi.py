@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sdpa.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 NONE, CAUSAL, WINDOW, TWO_SIDED = 0, 1, 2, 3
 FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before any launch
 
@@ -75,6 +75,7 @@ def test_workspace_is_linear_in_L(lib):
     assert lib.sdpa_bwd_workspace_bytes(0, 32, 16384, 256, BF16) == 0
     assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 100, BF16) == 0   # unsupported D
     assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, 7) == 0       # unknown dtype
+    assert lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, F16) == 32 * 16384 * 4
 
 
 def fwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
@@ -92,7 +93,8 @@ def bwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, wi
 
 
 @pytest.mark.parametrize("kw,expect", [
-    ({"dtype": 2}, INVALID),
+    ({"dtype": 3}, INVALID),
+    ({"dtype": -1}, INVALID),
     ({"mask": 4}, INVALID),
     ({"mask": -1}, INVALID),
     ({"B": -1}, INVALID),
@@ -112,6 +114,7 @@ def bwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, wi
     ({"D": 96}, UNSUPPORTED),
     ({"D": 1024}, UNSUPPORTED),
     ({"dtype": F32, "D": 256}, UNSUPPORTED),
+    ({"dtype": F16, "D": 96}, UNSUPPORTED),
     ({"Hq": 70000, "group": 1}, UNSUPPORTED),
     ({"Lq": 1 << 29, "Lk": (1 << 29) + 1}, UNSUPPORTED),   # row / key indices plus offsets must fit int32
 ])

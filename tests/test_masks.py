@@ -4,7 +4,8 @@ positions (Lq < Lk), plus more queries than keys (Lq > Lk), where the first
 rows see no key at all.
 
 Each case runs through the C ABI and is compared with the fp64 oracle on the
-same inputs: relative Frobenius error per tensor (1e-2 bf16, 1e-5 fp32), lse
+same inputs: relative Frobenius error per tensor (1e-2 bf16, 2e-3 fp16, 1e-5
+fp32), lse
 max-abs 1e-4 on rows that have keys; rows with no key must hold exactly
 O = 0, lse = -inf, dQ = 0, and keys that no row sees exactly dK = dV = 0
 (page "Lab 028 lab detail: Off NVIDIA, you fix the platform yourself",
@@ -49,6 +50,10 @@ CASES = [
     ("f32_two_w9_D128", 2, 2, 90, 90, 128, "f32", MASK_TWO_SIDED, 9),
     ("f32_suffix_w17_D64", 2, 1, 50, 130, 64, "f32", MASK_WINDOW, 17),
     ("f32_prefix_causal_D64", 2, 1, 90, 40, 64, "f32", MASK_CAUSAL, 0),
+    ("f16_none_D128", 2, 1, 300, 300, 128, "f16", MASK_NONE, 0),
+    ("f16_two_w80_D256", 2, 1, 400, 400, 256, "f16", MASK_TWO_SIDED, 80),
+    ("f16_suffix_w64_D512", 2, 1, 150, 700, 512, "f16", MASK_WINDOW, 64),
+    ("f16_prefix_causal_D64", 2, 2, 300, 120, 64, "f16", MASK_CAUSAL, 0),
 ]
 
 

@@ -39,7 +39,7 @@ class Workload:
     Hkv: int
     L: int
     D: int
-    dtype: str          # "bf16" or "f32"
+    dtype: str          # "bf16", "f16" or "f32"
     mask: str           # MASK_NONE, MASK_CAUSAL, MASK_WINDOW or MASK_TWO_SIDED
     window: int = 0     # window size (diagonal included); 0 without a window
     seed: int = 1000
@@ -59,7 +59,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[self.dtype]
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
