@@ -46,7 +46,8 @@
  * Layout and ownership
  * --------------------
  * Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
- * contiguous row-major: Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
+ * contiguous row-major (the *_strided entry points take any batch / head /
+ * row strides instead): Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
  * [B, Hq/group, Lk, D]; lse [B, Hq, Lq] float32. Element type: bfloat16
  * (SDPA_BF16), float16 (SDPA_F16) or float32 (SDPA_F32) for Q, K, V, O, dO,
  * dQ, dK, dV; lse is always float32. The 16-bit types run on the matrix
@@ -109,6 +110,26 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t dtype, int32_t mask, int32_t window, float scale,
                  hipStream_t stream);
 
+/* Element strides of one tensor seen as [B, H, L, D]: batch, head and row
+ * (sequence position). The D elements of a row must be contiguous. */
+typedef struct {
+  int64_t b, h, l;
+} sdpa_strides;
+
+/* sdpa_fwd_lse for tensors in any strided layout, e.g. [B, L, H, D] projection
+ * outputs or views into a fused QKV buffer. `strides` points to 4 entries, for
+ * q, k, v and o in that order (NULL: all contiguous [B, H, L, D]); lse stays
+ * contiguous [B, Hq, Lq]. Each stride must be >= 0 and a multiple of
+ * 16 bytes' worth of elements, each row stride at least D and below 2^23;
+ * otherwise SDPA_ERR_INVALID_ARG. K and V must have the same row stride (and,
+ * in the backward, Q and dO), else SDPA_ERR_UNSUPPORTED: true of [B, L, H, D]
+ * tensors of one shape and of views into one fused QKV buffer. Rows of the
+ * outputs must not overlap. */
+int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                         int32_t dtype, int32_t mask, int32_t window, float scale,
+                         const sdpa_strides* strides, hipStream_t stream);
+
 /* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
  * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, Lq]),
  * rounded up to 256 bytes. Linear in Lq. Returns 0 for empty shapes and for
@@ -129,6 +150,16 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t dtype, int32_t mask, int32_t window, float scale,
              hipStream_t stream);
 
+/* sdpa_bwd for strided tensors: `strides` points to 8 entries, for q, k, v,
+ * o, dO, dq, dk and dv in that order (NULL: all contiguous), with the rules
+ * of sdpa_fwd_lse_strided. */
+int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                     int32_t dtype, int32_t mask, int32_t window, float scale,
+                     const sdpa_strides* strides, hipStream_t stream);
+
 /* Measurement variant of sdpa_bwd: identical arguments and results, plus two
  * caller-created HIP events. When both are non-null, `main_begin` and
  * `main_end` are recorded on `stream` immediately before and after the main
@@ -146,7 +177,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 200. */
+/* ABI version of this header (major * 100 + minor): 201. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -5,5 +5,6 @@ last Lq of Lk key positions. The compute lives in the HIP library libsdpa.so (C 
 include/sdpa.h); this package is its thin Python binding.
 """
 from ._lib import SdpaError, load, sdpa_bwd, sdpa_fwd_lse, workspace_bytes  # noqa: F401
+from .autograd import SDPAFunction, attention  # noqa: F401
 
-__all__ = ["sdpa_fwd_lse", "sdpa_bwd", "workspace_bytes", "load", "SdpaError"]
+__all__ = ["sdpa_fwd_lse", "sdpa_bwd", "workspace_bytes", "load", "SdpaError", "attention", "SDPAFunction"]

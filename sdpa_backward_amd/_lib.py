@@ -1,10 +1,18 @@
 """ctypes binding of libsdpa.so: argument marshalling only.
 
 Every step of the attention forward and backward runs in the HIP library.
-This module checks tensor dtypes, shapes, devices and contiguity, allocates
+This module checks tensor dtypes, shapes, devices and strides, allocates
 outputs and the backward workspace with torch (torch owns device memory and
-streams), and passes raw device pointers plus the current HIP stream. There is
-no CPU path: if the library is missing or a call fails, it raises.
+streams), and passes raw device pointers, element strides and the current HIP
+stream. There is no CPU path: if the library is missing or a call fails, it
+raises.
+
+Tensors are seen as [B, H, L, D] and may be strided views (for example
+``x.view(B, L, H, D).transpose(1, 2)`` of a projection output, or slices of a
+fused QKV buffer); the D elements of a row must be contiguous. The kernels
+read K and V (and Q and dO) with one set of row offsets, so when the two of a
+pair have different row strides the binding hands the library contiguous
+copies of both (the only copies it ever makes).
 """
 from __future__ import annotations
 
@@ -22,10 +30,15 @@ STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", 
 DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
-EXPORTS = ("sdpa_fwd_lse", "sdpa_bwd", "sdpa_bwd_timed", "sdpa_bwd_workspace_bytes", "sdpa_status_string",
-           "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_strided", "sdpa_bwd", "sdpa_bwd_strided", "sdpa_bwd_timed",
+           "sdpa_bwd_workspace_bytes", "sdpa_status_string", "sdpa_abi_version")
 
 _lib = None
+
+
+class SdpaStrides(ctypes.Structure):
+    """sdpa_strides: element strides of one [B, H, L, D] tensor."""
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64)]
 
 
 class SdpaError(RuntimeError):
@@ -43,13 +56,15 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is missing: build it with `python -m sdpa_backward_amd.build`")
     lib = ctypes.CDLL(path)
     p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-    shape = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, p]  # B Hq group Lq Lk D dtype mask window scale stream
-    lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + shape
-    lib.sdpa_fwd_lse.restype = ctypes.c_int
-    lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape
-    lib.sdpa_bwd.restype = ctypes.c_int
-    lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + shape + [p, p]
-    lib.sdpa_bwd_timed.restype = ctypes.c_int
+    dims = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]  # B Hq group Lq Lk D dtype mask window scale
+    st = ctypes.POINTER(SdpaStrides)
+    lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + dims + [p]
+    lib.sdpa_fwd_lse_strided.argtypes = [p, p, p, p, p] + dims + [st, p]
+    lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
+    lib.sdpa_bwd_strided.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [st, p]
+    lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, p]
+    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_strided", "sdpa_bwd", "sdpa_bwd_strided", "sdpa_bwd_timed"):
+        getattr(lib, f).restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
@@ -74,19 +89,29 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _strides(*ts):
+    arr = (SdpaStrides * len(ts))()
+    for a, t in zip(arr, ts):
+        a.b, a.h, a.l = t.stride(0), t.stride(1), t.stride(2)
+    return arr
+
+
+def _rows_ok(t):
+    """The D elements of a row are contiguous (any stride is fine for a single element)."""
+    return t.dim() == 4 and (t.stride(3) == 1 or t.shape[3] <= 1)
+
+
 def _validate(q, k, v, extra=()):
     """(B, Hq, group, Lq, Lk, D) of q [B, Hq, Lq, D] and k, v [B, Hkv, Lk, D]."""
     for name, t in (("q", q), ("k", k), ("v", v), *extra):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, H, L, D]")
         if t.dtype != q.dtype:
             raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+        if not _rows_ok(t):
+            raise ValueError(f"{name} must be [B, H, L, D] with contiguous rows (stride 1 along D)")
     if q.dtype not in DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, L, D]")
     B, Hq, Lq, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
@@ -94,6 +119,13 @@ def _validate(q, k, v, extra=()):
     if Hkv == 0 or Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     return B, Hq, Hq // Hkv, Lq, Lk, D
+
+
+def _same_rows(a, b):
+    """a, b with one row stride (the library reads the pair with shared offsets)."""
+    if a.stride(2) == b.stride(2):
+        return a, b
+    return a.contiguous(), b.contiguous()
 
 
 def _mask_args(mask, window):
@@ -106,24 +138,31 @@ def default_scale(D):
     return 1.0 / math.sqrt(D)
 
 
+def _out_like(t, out):
+    o = torch.empty_like(t) if out is None else out   # keeps t's strides when t is dense
+    if o.shape != t.shape or o.dtype != t.dtype or not _rows_ok(o):
+        raise ValueError("output buffer must match its input's shape and dtype, rows contiguous")
+    return o
+
+
 def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None):
     """O [B,Hq,Lq,D] (q.dtype) and lse [B,Hq,Lq] (float32, natural log).
 
     k, v are [B, Hkv, Lk, D]; with Lk != Lq the queries are the last Lq key
     positions. mask: "none", "causal", "causal_window" (window keys up to the
-    diagonal) or "window" (window - 1 keys either side of it)."""
+    diagonal) or "window" (window - 1 keys either side of it). O takes q's
+    strides when q is dense (e.g. a [B, L, H, D] layout stays one)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v)
+    k, v = _same_rows(k, v)
     scale = default_scale(D) if scale is None else float(scale)
     m, w = _mask_args(mask, window)
-    o = torch.empty_like(q) if out is None else out
+    o = _out_like(q, out)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("out must match q")
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, L]")
-    st = load().sdpa_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
-                             DTYPE[q.dtype], m, w, scale, _stream(q.device))
-    _check("sdpa_fwd_lse", st)
+    st = load().sdpa_fwd_lse_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
+                                     DTYPE[q.dtype], m, w, scale, _strides(q, k, v, o), _stream(q.device))
+    _check("sdpa_fwd_lse_strided", st)
     return o, lse
 
 
@@ -135,8 +174,9 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
              main_events=None):
     """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse).
 
-    ``main_events``: optional pair of raw hipEvent_t handles recorded around the
-    main backward kernel (sdpa_bwd_timed)."""
+    Gradients take the strides of q, k, v when those are dense. ``main_events``:
+    optional pair of raw hipEvent_t handles recorded around the main backward
+    kernel (sdpa_bwd_timed; contiguous tensors only)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v, (("o", o), ("do", do)))
     if o.shape != q.shape or do.shape != q.shape:
         raise ValueError("o and do must match q")
@@ -148,15 +188,19 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dq, dk, dv = _out_like(q, None), _out_like(k, None), _out_like(v, None)
     else:
-        dq, dk, dv = out
+        dq, dk, dv = (_out_like(t, x) for t, x in zip((q, k, v), out))
+    k, v = _same_rows(k, v)
+    q, do = _same_rows(q, do)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-            _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale,
-            _stream(q.device))
+            _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale)
     if main_events is None:
-        _check("sdpa_bwd", load().sdpa_bwd(*args))
+        strides = _strides(q, k, v, o, do, dq, dk, dv)
+        _check("sdpa_bwd_strided", load().sdpa_bwd_strided(*args, strides, _stream(q.device)))
     else:
+        if not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
+            raise ValueError("the timed backward takes contiguous tensors")
         ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
-        _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, ev0, ev1))
+        _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), ev0, ev1))
     return dq, dk, dv

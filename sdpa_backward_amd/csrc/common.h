@@ -244,53 +244,103 @@ SDPA_DEV typename Vec<E>::x8 op_direct(const E* T, const LaneAddr<D>& a, int k0,
   return *(const typename Vec<E>::x8*)p;
 }
 
+// Element strides of a [B, H, L, D] tensor: batch, head and row (sequence
+// position); the D elements of a row are contiguous.
+struct Strides {
+  long long b, h;
+  int l;  // < 2^23 (checked by the host)
+};
+
+// Strides of every tensor of a forward / backward call (a kernel reads those
+// of the tensors it touches). lse and Delta are always contiguous [B, Hq, Lq].
+struct AllStrides {
+  Strides q, k, v, o, dO, dq, dk, dv;
+};
+
+// The strides of contiguous [B, H, L, D] tensors. The kernels come in a dense
+// instantiation that uses these (row stride D known at compile time, so tile
+// offsets fold to constants and no stride occupies a register) and a strided
+// one that reads the caller's.
+template <int D>
+__host__ __device__ inline AllStrides dense_strides(int Hq, int Hkv, int Lq, int Lk) {
+  const Strides q{(long long)Hq * Lq * D, (long long)Lq * D, D}, kv{(long long)Hkv * Lk * D, (long long)Lk * D, D};
+  return {q, kv, kv, q, q, q, kv, kv};
+}
+
+inline bool same(const Strides& a, const Strides& b) { return a.b == b.b && a.h == b.h && a.l == b.l; }
+
+// Whether a call's tensors are all contiguous (the dense instantiation applies).
+template <int D>
+inline bool is_dense(const AllStrides& s, int Hq, int Hkv, int Lq, int Lk) {
+  const AllStrides d = dense_strides<D>(Hq, Hkv, Lq, Lk);
+  return same(s.q, d.q) && same(s.k, d.k) && same(s.v, d.v) && same(s.o, d.o) && same(s.dO, d.dO) &&
+         same(s.dq, d.dq) && same(s.dk, d.dk) && same(s.dv, d.dv);
+}
+
 // Asynchronous global->LDS tile loads through a buffer resource. A wave
 // issues whole 1 KB blocks (buffer_load_dwordx4 ... lds: lane l's 16 bytes land
-// at the block's LDS base + 16 l); the lane's source offset inside the tile is
-// fixed, so it is computed once (voff) and every load needs no address
-// arithmetic. The resource of each tile covers only its valid rows: lanes whose
-// offset falls beyond them are range-checked by the hardware and read nothing
-// from memory (rows past the end of the sequence are masked downstream; the
-// buffers are zeroed once at kernel start, so such rows only ever hold zeros
-// or finite data of an earlier tile).
-template <int D, int R, int NW>
+// at the block's LDS base + 16 l). Block j of a tile covers RPB = 64 / CPR
+// whole rows, so lane l of a wave's jj-th block reads row
+// r = (jj NW + w) RPB + l / CPR at byte r * row_bytes + 16 slot(r, l % CPR).
+// DENSE (row stride D, the contiguous layout): every offset is computed once
+// and loads need no address arithmetic. Otherwise (any row stride) the
+// swizzled slot depends on r only through r mod 16, which repeats every
+// VP = 16 / gcd(16, NW RPB) blocks (1 for D <= 128, 2 for D = 256, 4 for
+// D = 512): each lane keeps VP offsets and a load adds the uniform rest, a
+// multiple of the row stride. The resource of each tile ends with its last
+// valid row: lanes whose offset falls beyond it are range-checked by the
+// hardware and read nothing from memory (rows past the end of the sequence are
+// masked downstream; the buffers are zeroed once at kernel start, so such rows
+// only ever hold zeros or finite data of an earlier tile).
+template <int D, int R, int NW, bool DENSE>
 struct TileLoader {
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;             // rows per 1 KB block
   static constexpr int PER = R * CPR / 64;         // 1 KB blocks per tile
   static constexpr int NJ = (PER + NW - 1) / NW;   // blocks issued by one wave
-  static_assert((R * CPR) % 64 == 0, "tile must be a whole number of 1 KB blocks");
-  uint32_t voff[NJ];
-  SDPA_DEV void init(int w, int lane) {
+  static constexpr int G = (NW * RPB) % 16 == 0 ? 16 : (NW * RPB) % 8 == 0 ? 8 : (NW * RPB) % 4 == 0 ? 4 : 2;
+  static constexpr int VP0 = 16 / G;               // period of the lane offsets in jj
+  static constexpr int NOFF = DENSE ? NJ : (VP0 < NJ ? VP0 : NJ);
+  static_assert(CPR <= 64 && (R * CPR) % 64 == 0, "tile must be a whole number of 1 KB blocks of whole rows");
+  uint32_t lane_off[NOFF];
+  uint32_t row_bytes;  // source row stride in bytes (uniform)
+  // sl: the source's row stride in elements (D when DENSE; else >= D, bounded
+  // by the host so every offset inside a tile fits 32 bits)
+  SDPA_DEV void init(int w, int lane, long long sl) {
+    row_bytes = DENSE ? D * 2 : (uint32_t)(sl * 2);
 #pragma unroll
-    for (int jj = 0; jj < NJ; jj++) {
-      const int p = (jj * NW + w) * 64 + lane;
-      const int r = p / CPR;
-      voff[jj] = (uint32_t)(r * D + Tile<D>::slot(r, p % CPR) * 8) * 2;  // the slot map is an involution
+    for (int v = 0; v < NOFF; v++) {
+      const int r = (v * NW + w) * RPB + lane / CPR;
+      lane_off[v] = (uint32_t)r * row_bytes + (uint32_t)(Tile<D>::slot(r, lane % CPR) * 16);
     }
   }
-  // Resource covering rows [0, min(valid, R)) of the [R][D] tile starting at
-  // src (row stride D); valid <= 0 gives an empty range (loads read nothing).
-  SDPA_DEV static __amdgpu_buffer_rsrc_t rsrc_of(const void* src, int valid) {
+  // Source offset of this lane in the wave's block jj.
+  SDPA_DEV uint32_t voff(int jj) const {
+    if constexpr (DENSE) return lane_off[jj];
+    else return lane_off[jj % NOFF] + (uint32_t)((jj / NOFF) * NOFF * NW * RPB) * row_bytes;
+  }
+  // Resource covering rows [0, min(valid, R)) of the tile whose row 0 starts at
+  // src; valid <= 0 gives an empty range (loads read nothing).
+  SDPA_DEV __amdgpu_buffer_rsrc_t rsrc(const void* src, int valid) const {
     const int rows = __builtin_amdgcn_readfirstlane(valid < 0 ? 0 : valid < R ? valid : R);  // uniform
-    return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
+    const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, bytes, 0x00020000);
   }
   // This wave's block jj of a tile (jj < NJ, and jj * NW + w < PER).
-  SDPA_DEV void issue_one(void* lds, __amdgpu_buffer_rsrc_t rsrc, int jj, int w) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+  SDPA_DEV void issue_one(void* lds, __amdgpu_buffer_rsrc_t rs, int jj, int w) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs,
                                              (__attribute__((address_space(3))) void*)((char*)lds + (jj * NW + w) * 1024),
-                                             16, (int)voff[jj], 0, 0, 0);
+                                             16, (int)voff(jj), 0, 0, 0);
   }
-  // Rows [0, min(valid, R)) of the [R][D] tile starting at src (row stride D).
+  // Rows [0, min(valid, R)) of the tile whose row 0 starts at src.
   SDPA_DEV void issue(void* lds, const void* src, int valid, int w) const {
-    const int rows = valid < R ? valid : R;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(src, valid);
 #pragma unroll
     for (int jj = 0; jj < NJ; jj++) {
       const int j = jj * NW + w;
       if (PER % NW != 0 && j >= PER) break;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)((char*)lds + j * 1024), 16,
-                                               (int)voff[jj], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)((char*)lds + j * 1024), 16,
+                                               (int)voff(jj), 0, 0, 0);
     }
   }
 };

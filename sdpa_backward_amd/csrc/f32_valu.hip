@@ -16,14 +16,14 @@ template <int D>
 __global__ void __launch_bounds__(128)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                float* __restrict__ O, float* __restrict__ LSE, int Hq, int group, int Lq, int Lk, int dlo,
-               int dhi, float scale) {
+               int dhi, float scale, AllStrides st) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= Lq) return;
   const int Hkv = Hq / group, g = h / group;
-  const float* q = Q + ((size_t)b * Hq + h) * Lq * D + (size_t)i * D;
-  const float* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const float* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const float* q = Q + b * st.q.b + h * st.q.h + (long long)i * st.q.l;
+  const float* Kg = K + b * st.k.b + g * st.k.h;
+  const float* Vg = V + b * st.v.b + g * st.v.h;
   float qr[D];
 #pragma unroll
   for (int d = 0; d < D; d++) qr[d] = q[d];
@@ -33,14 +33,14 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
     m = fmaxf(m, s * scale);
   }
   float l = 0.f;
   for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
     l += expf(s * scale - m);
   }
   const float lse = jlo <= jhi ? m + logf(l) : -INFINITY;
@@ -50,12 +50,12 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
     const float p = expf(s * scale - lse);
 #pragma unroll
-    for (int d = 0; d < D; d++) acc[d] = fmaf(p, Vg[(size_t)j * D + d], acc[d]);
+    for (int d = 0; d < D; d++) acc[d] = fmaf(p, Vg[(long long)j * st.v.l + d], acc[d]);
   }
-  float* o = O + ((size_t)b * Hq + h) * Lq * D + (size_t)i * D;
+  float* o = O + b * st.o.b + h * st.o.h + (long long)i * st.o.l;
 #pragma unroll
   for (int d = 0; d < D; d++) o[d] = acc[d];
   LSE[((size_t)b * Hq + h) * Lq + i] = lse;
@@ -67,17 +67,17 @@ __global__ void __launch_bounds__(128)
 bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                   const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
                   float* __restrict__ dQ, float* __restrict__ Delta, int Hq, int group, int Lq, int Lk,
-                  int dlo, int dhi, float scale) {
+                  int dlo, int dhi, float scale, AllStrides st) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= Lq) return;
   const int Hkv = Hq / group, g = h / group;
-  const size_t row = ((size_t)b * Hq + h) * Lq + i;
-  const float* q = Q + row * D;
-  const float* o = O + row * D;
-  const float* dor = dO + row * D;
-  const float* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const float* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const size_t row = ((size_t)b * Hq + h) * Lq + i;  // lse / Delta index
+  const float* q = Q + b * st.q.b + h * st.q.h + (long long)i * st.q.l;
+  const float* o = O + b * st.o.b + h * st.o.h + (long long)i * st.o.l;
+  const float* dor = dO + b * st.dO.b + h * st.dO.h + (long long)i * st.dO.l;
+  const float* Kg = K + b * st.k.b + g * st.k.h;
+  const float* Vg = V + b * st.v.b + g * st.v.h;
   float qr[D], dr[D], acc[D];
   float delta = 0.f;
 #pragma unroll
@@ -92,16 +92,17 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      s = fmaf(qr[d], Kg[(size_t)j * D + d], s);
-      dp = fmaf(dr[d], Vg[(size_t)j * D + d], dp);
+      s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
+      dp = fmaf(dr[d], Vg[(long long)j * st.v.l + d], dp);
     }
     const float p = expf(s * scale - lse);
     const float ds = p * (dp - delta);
 #pragma unroll
-    for (int d = 0; d < D; d++) acc[d] = fmaf(ds, Kg[(size_t)j * D + d], acc[d]);
+    for (int d = 0; d < D; d++) acc[d] = fmaf(ds, Kg[(long long)j * st.k.l + d], acc[d]);
   }
+  float* dq = dQ + b * st.dq.b + h * st.dq.h + (long long)i * st.dq.l;
 #pragma unroll
-  for (int d = 0; d < D; d++) dQ[row * D + d] = acc[d] * scale;
+  for (int d = 0; d < D; d++) dq[d] = acc[d] * scale;
   Delta[row] = delta;
 }
 
@@ -111,27 +112,28 @@ __global__ void __launch_bounds__(128)
 bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                    const float* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV, int Hq,
-                   int group, int Lq, int Lk, int dlo, int dhi, float scale) {
+                   int group, int Lq, int Lk, int dlo, int dhi, float scale, AllStrides st) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
   if (j >= Lk) return;
   const int Hkv = Hq / group;
-  const size_t krow = ((size_t)b * Hkv + g) * Lk + j;
+  const float* kp = K + b * st.k.b + g * st.k.h + (long long)j * st.k.l;
+  const float* vp = V + b * st.v.b + g * st.v.h + (long long)j * st.v.l;
   float kr[D], vr[D], dk[D], dv[D];
 #pragma unroll
   for (int d = 0; d < D; d++) {
-    kr[d] = K[krow * D + d];
-    vr[d] = V[krow * D + d];
+    kr[d] = kp[d];
+    vr[d] = vp[d];
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
   // rows that see key j: dlo <= j - i <= dhi, 0 <= i < Lq
   const int ilo = max(0, j - dhi), ihi = min(Lq - 1, j - dlo);
   for (int h = g * group; h < (g + 1) * group; h++) {
-    const size_t hrow = ((size_t)b * Hq + h) * Lq;
+    const size_t hrow = ((size_t)b * Hq + h) * Lq;  // lse / Delta row block
     for (int i = ilo; i <= ihi; i++) {
-      const float* q = Q + (hrow + i) * D;
-      const float* dor = dO + (hrow + i) * D;
+      const float* q = Q + b * st.q.b + h * st.q.h + (long long)i * st.q.l;
+      const float* dor = dO + b * st.dO.b + h * st.dO.h + (long long)i * st.dO.l;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int d = 0; d < D; d++) {
@@ -147,27 +149,30 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
       }
     }
   }
+  float* dkp = dK + b * st.dk.b + g * st.dk.h + (long long)j * st.dk.l;
+  float* dvp = dV + b * st.dv.b + g * st.dv.h + (long long)j * st.dv.l;
 #pragma unroll
   for (int d = 0; d < D; d++) {
-    dK[krow * D + d] = dk[d] * scale;
-    dV[krow * D + d] = dv[d];
+    dkp[d] = dk[d] * scale;
+    dvp[d] = dv[d];
   }
 }
 
 template <int D>
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream) {
+                          int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
+                          hipStream_t stream) {
   dim3 grid((Lq + 127) / 128, Hq, B);
   hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (float*)o, lse, Hq, group, Lq, Lk, dlo, dhi, scale);
+                     (const float*)v, (float*)o, lse, Hq, group, Lq, Lk, dlo, dhi, scale, st);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                          int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream,
-                          hipEvent_t ev0, hipEvent_t ev1) {
+                          int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
+                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   hipError_t e;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
@@ -175,7 +180,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     dim3 grid((Lq + 127) / 128, Hq, B);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
-                       Lq, Lk, dlo, dhi, scale);
+                       Lq, Lk, dlo, dhi, scale, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -183,7 +188,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     dim3 grid2((Lk + 127) / 128, Hq / group, B);
     hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
-                       group, Lq, Lk, dlo, dhi, scale);
+                       group, Lq, Lk, dlo, dhi, scale, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -193,10 +198,11 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
 
 #define SDPA_INST_F32(D)                                                                                    \
   template hipError_t launch_fwd_f32<D>(const void*, const void*, const void*, void*, float*, int, int, int, \
-                                        int, int, int, int, float, hipStream_t);                            \
+                                        int, int, int, int, float, const AllStrides&, hipStream_t);         \
   template hipError_t launch_bwd_f32<D>(const void*, const void*, const void*, const void*, const void*,     \
                                         const float*, void*, void*, void*, float*, int, int, int, int, int,  \
-                                        int, int, float, hipStream_t, hipEvent_t, hipEvent_t);
+                                        int, int, float, const AllStrides&, hipStream_t, hipEvent_t,         \
+                                        hipEvent_t);
 SDPA_INST_F32(64)
 SDPA_INST_F32(128)
 

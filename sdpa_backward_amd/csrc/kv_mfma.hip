@@ -59,12 +59,12 @@ SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
   lds_barrier();
 }
 
-template <int D, int PASS, typename E>
+template <int D, int PASS, typename E, bool DENSE>
 __global__ void __launch_bounds__(256, 1)
 kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
           E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-          float scale, float scale_log2) {
+          float scale, float scale_log2, AllStrides st_arg) {
   using C = KvCfg<D>;
   using ex8 = typename Vec<E>::x8;
   constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
@@ -83,14 +83,15 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   la.init(lane);
   const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
+  const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
   const int nkt = (Lk + C::BKT - 1) / C::BKT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
   const int k0 = kt * C::BKT;
   const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
-  const E* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const E* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const E* Kg = K + b * st.k.b + g * st.k.h;
+  const E* Vg = V + b * st.v.b + g * st.v.h;
   // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist)
   const int ihi = min(Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
   const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
@@ -104,17 +105,21 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
   lds_barrier();
   {
-    TileLoader<D, C::BKT, C::NW> kld;
-    kld.init(w, lane);
-    kld.issue(ks, Kg + (size_t)k0 * D, Lk - k0, w);
+    TileLoader<D, C::BKT, C::NW, DENSE> kld;
+    kld.init(w, lane, st.k.l);
+    kld.issue(ks, Kg + (long long)k0 * st.k.l, Lk - k0, w);
   }
-  TileLoader<D, C::BQ, C::NW> ld;  // per-lane source offsets of the Q/dO tile loads
-  ld.init(w, lane);
+  // per-lane source offsets of the Q and dO tile loads (the two share their row
+  // stride: the host checks it)
+  TileLoader<D, C::BQ, C::NW, DENSE> ldq;
+  ldq.init(w, lane, st.q.l);
+  const auto& ldd = ldq;
+  using LD = decltype(ldq);
   // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
   constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
   ex8 vreg[WANT_DK ? NKS : 1];
   if constexpr (WANT_DK) {
-    const E* vrow = Vg + (size_t)(kj < Lk ? kj : 0) * D;
+    const E* vrow = Vg + (long long)(kj < Lk ? kj : 0) * st.v.l;
 #pragma unroll
     for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const ex8*)(vrow + dw0 + 16 * s + 8 * hh) : zero8<E>();
   }
@@ -138,9 +143,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   auto tile_src = [&](int it, const E*& qs, const E*& ds, int& q0) {
     const int hq = g * group + it / nq;
     q0 = (qt_lo + it % nq) * C::BQ;
-    const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
-    qs = Q + off;
-    ds = dO + off;
+    qs = Q + b * st.q.b + hq * st.q.h + (long long)q0 * st.q.l;
+    ds = dO + b * st.dO.b + hq * st.dO.h + (long long)q0 * st.dO.l;
   };
   // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta of them (rows
   // clamped to Lq-1); one 4-byte global->LDS load per lane (wave 0 only)
@@ -156,8 +160,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     const E *qs, *ds;
     int q0;
     tile_src(it, qs, ds, q0);
-    ld.issue(qd, qs, Lq - q0, w);
-    ld.issue(dd, ds, Lq - q0, w);
+    ldq.issue(qd, qs, Lq - q0, w);
+    ldd.issue(dd, ds, Lq - q0, w);
     if (w == 0) load_rows(it, rv);
   };
 
@@ -238,17 +242,17 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       const E *qs, *ds;
       int q0n;
       tile_src(more ? it + 1 : it, qs, ds, q0n);
-      qrs = decltype(ld)::rsrc_of(qs, more ? Lq - q0n : 0);
-      drs = decltype(ld)::rsrc_of(ds, more ? Lq - q0n : 0);
+      qrs = ldq.rsrc(qs, more ? Lq - q0n : 0);
+      drs = ldd.rsrc(ds, more ? Lq - q0n : 0);
       if (w == 0) load_rows(more ? it + 1 : it, rvn);
     }
-    constexpr int NJ = decltype(ld)::NJ;
+    constexpr int NJ = LD::NJ;
     auto load_one = [&, qrs, drs](int j) {  // j in [0, 2 NJ): Q blocks, then dO blocks
-      if constexpr (decltype(ld)::PER % C::NW != 0) {
-        if ((j % NJ) * C::NW + w >= decltype(ld)::PER) return;
+      if constexpr (LD::PER % C::NW != 0) {
+        if ((j % NJ) * C::NW + w >= LD::PER) return;
       }
-      if (j < NJ) ld.issue_one(qn, qrs, j, w);
-      else ld.issue_one(dn, drs, j - NJ, w);
+      if (j < NJ) ldq.issue_one(qn, qrs, j, w);
+      else ldd.issue_one(dn, drs, j - NJ, w);
     };
 
     // S (all of it first, so exp(S) can start while the dP MFMAs run), then
@@ -316,19 +320,19 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // A wave's loads complete in order, so "Q landed, dO may still be in
     // flight" is vmcnt(NJ): at most one tile's worth of this wave's loads
     // outstanding (wave 0's extra lse/Delta load rides with the Q tile).
-    constexpr int NJ = decltype(ld)::NJ;
+    constexpr int NJ = LD::NJ;
     auto issue_q = [&](int it, bool more, E* dst, float* rvd) {
       const E *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
-      ld.issue(dst, qs, more ? Lq - q0n : 0, w);
+      ldq.issue(dst, qs, more ? Lq - q0n : 0, w);
       if (w == 0) load_rows(it, rvd);
     };
     auto issue_do = [&](int it, bool more, E* dst) {
       const E *qs, *ds;
       int q0n;
       tile_src(it, qs, ds, q0n);
-      ld.issue(dst, ds, more ? Lq - q0n : 0, w);
+      ldd.issue(dst, ds, more ? Lq - q0n : 0, w);
     };
     // S, then (dK pass) dP once dO has landed; operand reads pipelined by hand
     auto sdp = [&](const E* Qc, const E* dOc, f32x16& s_acc, f32x16& dp_acc) {
@@ -391,8 +395,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
-  E* dKg = dK + ((size_t)b * Hkv + g) * Lk * D;
-  E* dVg = dV + ((size_t)b * Hkv + g) * Lk * D;
+  E* dKg = dK + b * st.dk.b + g * st.dk.h;
+  E* dVg = dV + b * st.dv.b + g * st.dv.h;
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
     const int col = dw0 + 32 * d + (lane & 31);
@@ -400,8 +404,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     for (int i = 0; i < 16; i++) {
       const int key = kb0 + c_row(i, hh);
       if (key < Lk) {
-        if constexpr (WANT_DK) dKg[(size_t)key * D + col] = (E)(dkacc[d][i] * scale);
-        if constexpr (WANT_DV) dVg[(size_t)key * D + col] = (E)dvacc[d][i];
+        if constexpr (WANT_DK) dKg[(long long)key * st.dk.l + col] = (E)(dkacc[d][i] * scale);
+        if constexpr (WANT_DV) dVg[(long long)key * st.dv.l + col] = (E)dvacc[d][i];
       }
     }
   }
@@ -410,30 +414,32 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, float scale, hipStream_t stream) {
+                     int dhi, float scale, const AllStrides& st, hipStream_t stream) {
   using C = KvCfg<D>;
   const long nwg = (long)((Lk + C::BKT - 1) / C::BKT) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  auto run = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k,
-                       (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk,
-                       dlo, dhi, scale, scale * kLog2e);
+  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk);
+  auto run = [&](auto dense_kernel, auto strided_kernel) {
+    auto kernel = dense ? dense_kernel : strided_kernel;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
+                       Lq, Lk, dlo, dhi, scale, scale * kLog2e, st);
     return hipGetLastError();
   };
   if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
-    const hipError_t e = run(kv_kernel<D, KV_DV, E>);
+    const hipError_t e = run(kv_kernel<D, KV_DV, E, true>, kv_kernel<D, KV_DV, E, false>);
     if (e != hipSuccess) return e;
-    return run(kv_kernel<D, KV_DK, E>);
+    return run(kv_kernel<D, KV_DK, E, true>, kv_kernel<D, KV_DK, E, false>);
   } else {
-    return run(kv_kernel<D, KV_BOTH, E>);
+    return run(kv_kernel<D, KV_BOTH, E, true>, kv_kernel<D, KV_BOTH, E, false>);
   }
 }
 
 #define SDPA_INST_KV(D, E)                                                                                \
   template hipError_t launch_kv<D, E>(const void*, const void*, const void*, const void*, const float*,    \
                                       const float*, void*, void*, int, int, int, int, int, int, int, float, \
-                                      hipStream_t);
+                                      const AllStrides&, hipStream_t);
 SDPA_INST_KV(64, bf16)
 SDPA_INST_KV(128, bf16)
 SDPA_INST_KV(256, bf16)

@@ -73,12 +73,12 @@ SDPA_DEV void exchange_add(f32x16 (&c)[N], float* xbuf, int w, int lane) {
     for (int i = 0; i < 16; i++) c[t][i] += xbuf[((p * N + t) * 16 + i) * 64 + lane];
 }
 
-template <int D, int MODE, typename E>
+template <int D, int MODE, typename E, bool DENSE>
 __global__ void __launch_bounds__(256, 1)
 qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ LSE,
           float* __restrict__ Delta, E* __restrict__ Out, int Hq, int group, int Lq, int Lk, int dlo,
-          int dhi, float scale, float scale_log2) {
+          int dhi, float scale, float scale_log2, AllStrides st_arg) {
   using C = QsCfg<D>;
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
@@ -94,17 +94,21 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
   la.init(lane);
-  TileLoader<D, C::BK, C::NW> ld;  // per-lane source offsets of the K/V tile loads
-  ld.init(w, lane);
+  const AllStrides st = DENSE ? dense_strides<D>(Hq, Hq / group, Lq, Lk) : st_arg;
+  // per-lane source offsets of the K and V tile loads (the two share their row
+  // stride: the host checks it)
+  TileLoader<D, C::BK, C::NW, DENSE> ldk;
+  ldk.init(w, lane, st.k.l);
+  const auto& ldv = ldk;
   const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int nqt = (Lq + C::BQ - 1) / C::BQ;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = nqt - 1 - logical % nqt;  // longest causal rows first within a head
   const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
   const int Hkv = Hq / group, g = h / group;
-  const size_t hrow = (size_t)b * Hq + h;
-  const E* Kg = K + ((size_t)b * Hkv + g) * Lk * D;
-  const E* Vg = V + ((size_t)b * Hkv + g) * Lk * D;
+  const size_t hrow = (size_t)b * Hq + h;  // lse / Delta row block
+  const E* Kg = K + b * st.k.b + g * st.k.h;
+  const E* Vg = V + b * st.v.b + g * st.v.h;
 
   const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
   const int qi = iw0 + (lane & 31);  // this lane's query row
@@ -115,15 +119,15 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 
   // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
   ex8 qreg[NKS];
-  const E* qrow = Q + (hrow * Lq + (qok ? qi : 0)) * D;
+  const E* qrow = Q + b * st.q.b + h * st.q.h + (long long)(qok ? qi : 0) * st.q.l;
 #pragma unroll
   for (int s = 0; s < NKS; s++) qreg[s] = qok ? *(const ex8*)(qrow + dw0 + 16 * s + 8 * hh) : zero8<E>();
 
   ex8 dreg[MODE == QS_DQ ? NKS : 1];
   float lse2 = 0.f, dlt = 0.f;
   if constexpr (MODE == QS_DQ) {
-    const E* drow = dO + (hrow * Lq + (qok ? qi : 0)) * D;
-    const E* orow = O + (hrow * Lq + (qok ? qi : 0)) * D;
+    const E* drow = dO + b * st.dO.b + h * st.dO.h + (long long)(qok ? qi : 0) * st.dO.l;
+    const E* orow = O + b * st.o.b + h * st.o.h + (long long)(qok ? qi : 0) * st.o.l;
 #pragma unroll
     for (int s = 0; s < NKS; s++) dreg[s] = qok ? *(const ex8*)(drow + dw0 + 16 * s + 8 * hh) : zero8<E>();
     // Delta_i = <dO_i, O_i> over the whole head dimension, fp32
@@ -163,15 +167,16 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // rows and the loads read nothing.
     const bool more = kt + 1 <= kt_hi;
     const int jn = more ? (kt + 1) * BK : 0;
-    const auto krs = decltype(ld)::rsrc_of(Kg + (size_t)jn * D, more ? Lk - jn : 0);
-    const auto vrs = decltype(ld)::rsrc_of(Vg + (size_t)jn * D, more ? Lk - jn : 0);
-    constexpr int NJ = decltype(ld)::NJ;
+    const auto krs = ldk.rsrc(Kg + (long long)jn * st.k.l, more ? Lk - jn : 0);
+    const auto vrs = ldv.rsrc(Vg + (long long)jn * st.v.l, more ? Lk - jn : 0);
+    using LD = decltype(ldk);
+    constexpr int NJ = LD::NJ;
     auto load_one = [&, krs, vrs](int j) {  // j in [0, 2 NJ): K blocks, then V blocks
-      if constexpr (decltype(ld)::PER % C::NW != 0) {
-        if ((j % NJ) * C::NW + w >= decltype(ld)::PER) return;
+      if constexpr (LD::PER % C::NW != 0) {
+        if ((j % NJ) * C::NW + w >= LD::PER) return;
       }
-      if (j < NJ) ld.issue_one(Kn, krs, j, w);
-      else ld.issue_one(Vn, vrs, j - NJ, w);
+      if (j < NJ) ldk.issue_one(Kn, krs, j, w);
+      else ldv.issue_one(Vn, vrs, j - NJ, w);
     };
 #pragma unroll
     for (int s = 0; s < NKS; s++) keep_in_agpr(qreg[s]);
@@ -304,8 +309,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     zero_lds(vb0, C::TILE, tid);
     zero_lds(vb1, C::TILE, tid);
     lds_barrier();
-    ld.issue(kb0, Kg + (size_t)j0 * D, Lk - j0, w);
-    ld.issue(vb0, Vg + (size_t)j0 * D, Lk - j0, w);
+    ldk.issue(kb0, Kg + (long long)j0 * st.k.l, Lk - j0, w);
+    ldv.issue(vb0, Vg + (long long)j0 * st.v.l, Lk - j0, w);
     wait_all_and_barrier();
   }
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
@@ -317,7 +322,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
 
   if (!qok) return;
-  E* orow = Out + (hrow * Lq + qi) * D;
+  const Strides so = MODE == QS_FWD ? st.o : st.dq;
+  E* orow = Out + b * so.b + h * so.h + (long long)qi * so.l;
   if constexpr (MODE == QS_FWD) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
@@ -346,24 +352,25 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-                     float scale, hipStream_t stream) {
+                     float scale, const AllStrides& st, hipStream_t stream) {
   using C = QsCfg<D>;
   const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((qs_kernel<D, MODE, E>), dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q,
-                     (const E*)k, (const E*)v, (const E*)o, (const E*)dO, lse, delta, (E*)out,
-                     Hq, group, Lq, Lk, dlo, dhi, scale, scale * kLog2e);
+  auto kernel = is_dense<D>(st, Hq, Hq / group, Lq, Lk) ? qs_kernel<D, MODE, E, true> : qs_kernel<D, MODE, E, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                     (const E*)o, (const E*)dO, lse, delta, (E*)out, Hq, group, Lq, Lk, dlo, dhi, scale,
+                     scale * kLog2e, st);
   return hipGetLastError();
 }
 
 #define SDPA_INST_QS(D, E)                                                                                  \
   template hipError_t launch_qs<D, QS_FWD, E>(const void*, const void*, const void*, const void*, const void*, \
                                               float*, float*, void*, int, int, int, int, int, int, int, float,   \
-                                              hipStream_t);                                                    \
+                                              const AllStrides&, hipStream_t);                                 \
   template hipError_t launch_qs<D, QS_DQ, E>(const void*, const void*, const void*, const void*, const void*,  \
                                              float*, float*, void*, int, int, int, int, int, int, int, float,    \
-                                             hipStream_t);
+                                             const AllStrides&, hipStream_t);
 SDPA_INST_QS(64, bf16)
 SDPA_INST_QS(128, bf16)
 SDPA_INST_QS(256, bf16)

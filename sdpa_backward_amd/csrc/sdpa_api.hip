@@ -19,32 +19,32 @@ enum { QS_FWD = 0, QS_DQ = 1 };
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-                     float scale, hipStream_t stream);
+                     float scale, const AllStrides& st, hipStream_t stream);
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, float scale, hipStream_t stream);
+                     int dhi, float scale, const AllStrides& st, hipStream_t stream);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
-                          int, float, hipStream_t);
+                          int, float, const AllStrides&, hipStream_t);
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
-                          void*, void*, void*, float*, int, int, int, int, int, int, int, float, hipStream_t,
-                          hipEvent_t, hipEvent_t);
+                          void*, void*, void*, float*, int, int, int, int, int, int, int, float,
+                          const AllStrides&, hipStream_t, hipEvent_t, hipEvent_t);
 
 // 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass; the
 // optional events bracket the dK/dV kernel.
 template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                           int group, int Lq, int Lk, int dlo, int dhi, float scale, hipStream_t stream,
-                           hipEvent_t ev0, hipEvent_t ev1) {
+                           int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
+                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, Lq, Lk,
-                                     dlo, dhi, scale, stream);
+                                        dlo, dhi, scale, st, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream);
+  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, st, stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -118,6 +118,40 @@ size_t workspace_for(const Shape& s) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
 
+int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
+
+// Strides of a contiguous [B, H, L, D] tensor.
+sdpa::Strides dense(int H, int L, int D) { return {(long long)H * L * D, (long long)L * D, D}; }
+
+sdpa::AllStrides dense_all(const Shape& s) {
+  const int Hkv = s.Hq / s.group;
+  const sdpa::Strides q = dense(s.Hq, s.Lq, s.D), kv = dense(Hkv, s.Lk, s.D);
+  return {q, kv, kv, q, q, q, kv, kv};
+}
+
+// Caller strides (n tensors, in the AllStrides order q, k, v, o, dO, dq, dk, dv),
+// or the contiguous layout when st is null. Every stride must be non-negative,
+// a whole number of 16-byte units (so rows stay 16-byte aligned), and a row
+// stride at least D and below 2^23 elements (tile offsets then fit 32 bits).
+// K and V must share their row stride, and so must Q and dO.
+int take_strides(const Shape& s, const sdpa_strides* st, int n, sdpa::AllStrides& out) {
+  out = dense_all(s);
+  if (st == nullptr) return SDPA_OK;
+  sdpa::Strides* dst[] = {&out.q, &out.k, &out.v, &out.o, &out.dO, &out.dq, &out.dk, &out.dv};
+  const long long unit = 16 / elem_bytes(s.dtype);
+  for (int t = 0; t < n; t++) {
+    const sdpa_strides& x = st[t];
+    for (long long v : {(long long)x.b, (long long)x.h, (long long)x.l})
+      if (v < 0 || v % unit != 0 || v > (1LL << 40)) return SDPA_ERR_INVALID_ARG;
+    if (x.l < s.D || x.l >= (1LL << 23)) return SDPA_ERR_INVALID_ARG;
+    *dst[t] = {(long long)x.b, (long long)x.h, (int)x.l};
+  }
+  // the tile loaders of the matrix-core kernels serve K and V (and Q and dO)
+  // with one set of per-lane offsets
+  if (out.k.l != out.v.l || (n > 4 && out.q.l != out.dO.l)) return SDPA_ERR_UNSUPPORTED;
+  return SDPA_OK;
+}
+
 // Pointers of tensors that hold elements must be set and 16-byte aligned;
 // those of empty tensors are not used.
 bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned16(p)); }
@@ -126,7 +160,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 200; }
+int sdpa_abi_version(void) { return 201; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -145,9 +179,9 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
   return workspace_for(s);
 }
 
-int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
-                 int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
-                 float scale, hipStream_t stream) {
+int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                         int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask,
+                         int32_t window, float scale, const sdpa_strides* strides, hipStream_t stream) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -155,13 +189,15 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
   const bool rows = true, keys = !s.no_keys();
   if (!ptr_ok(q, rows) || !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(o, rows) || !ptr_ok(lse, rows))
     return SDPA_ERR_INVALID_ARG;
+  sdpa::AllStrides str;
+  if ((st = take_strides(s, strides, 4, str)) != SDPA_OK) return st;
   int dlo, dhi;
   s.band(dlo, dhi);
   switch (dtype * 1000 + D) {
 #define SDPA_FWD_CASE(DT, E, DD)                                                                          \
   case DT * 1000 + DD:                                                                                    \
     return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, B,  \
-                                                          Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+                                                          Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
     SDPA_FWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 256)
@@ -172,18 +208,31 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
     SDPA_FWD_CASE(SDPA_F16, f16, 512)
 #undef SDPA_FWD_CASE
     case SDPA_F32 * 1000 + 64:
-      return to_status(sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+      return to_status(
+          sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
     case SDPA_F32 * 1000 + 128:
-      return to_status(sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, stream));
+      return to_status(
+          sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
   }
   return SDPA_ERR_UNSUPPORTED;
 }
 
-int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                   int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
-                   int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
-                   hipEvent_t main_end) {
+int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                 int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                 float scale, hipStream_t stream) {
+  return sdpa_fwd_lse_strided(q, k, v, o, lse, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr,
+                              stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+             int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+             float scale, const sdpa_strides* strides, hipStream_t stream, hipEvent_t main_begin,
+             hipEvent_t main_end) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -192,6 +241,8 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
   if (!ptr_ok(q, rows) || !ptr_ok(o, rows) || !ptr_ok(dO, rows) || !ptr_ok(lse, rows) || !ptr_ok(dq, rows) ||
       !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(dk, keys) || !ptr_ok(dv, keys))
     return SDPA_ERR_INVALID_ARG;
+  sdpa::AllStrides str;
+  if ((st = take_strides(s, strides, 8, str)) != SDPA_OK) return st;
   const size_t need = workspace_for(s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return SDPA_ERR_WORKSPACE;
@@ -202,7 +253,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 #define SDPA_BWD_CASE(DT, E, DD)                                                                           \
   case DT * 1000 + DD:                                                                                     \
     return to_status(sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, \
-                                                  Lk, dlo, dhi, scale, stream, main_begin, main_end));
+                                                  Lk, dlo, dhi, scale, str, stream, main_begin, main_end));
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 256)
@@ -214,20 +265,42 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 #undef SDPA_BWD_CASE
     case SDPA_F32 * 1000 + 64:
       return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                dlo, dhi, scale, stream, main_begin, main_end));
+                                                dlo, dhi, scale, str, stream, main_begin, main_end));
     case SDPA_F32 * 1000 + 128:
       return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                 dlo, dhi, scale, stream, main_begin, main_end));
+                                                 dlo, dhi, scale, str, stream, main_begin, main_end));
   }
   return SDPA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
+                     int32_t mask, int32_t window, float scale, const sdpa_strides* strides,
+                     hipStream_t stream) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
+                  mask, window, scale, strides, stream, nullptr, nullptr);
+}
+
+int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                   int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
+                   int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
+                   hipEvent_t main_end) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
+                  mask, window, scale, nullptr, stream, main_begin, main_end);
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
              float scale, hipStream_t stream) {
-  return sdpa_bwd_timed(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D,
-                        dtype, mask, window, scale, stream, nullptr, nullptr);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
+                  mask, window, scale, nullptr, stream, nullptr, nullptr);
 }
 
 }  // extern "C"
