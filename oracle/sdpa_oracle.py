@@ -24,6 +24,10 @@ What is computed, and where the pages define it
   non-causal window also drops the tiles wholly ahead). With queries a suffix of the keys,
   ``diag_off = Lk - Lq`` (same page, item 5(b), and the parity cases with
   ``qL < kL``). No mask: every key.
+* Sinks: the backward the pages patch also takes attention sinks as a
+  parameter (Lab 028 page, "What I changed", item 2). Reading: one logit per
+  query head that joins every row's softmax normalizer as an extra score
+  with a zero value row (see head_rows).
 * GQA: query head h reads kv head ``h // group`` (page "MiniCPM5 Decode
   Megakernel - end-to-end build plan (handoff)", section 4.1, per-layer stage 5).
 
@@ -124,19 +128,30 @@ def _softmax_rows(S: np.ndarray, ok: np.ndarray):
     return P, lse
 
 
-def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True):
+def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True, sink=None):
     """Forward (and, with ``do_h``, backward) for one q-head and a set of query rows.
 
     q_h, do_h: [Lq, D]; k_g, v_g: [Lk, D] (fp64). Returns a dict with
     O[rows], lse[rows], Delta[rows] and, if want_grad, dQ[rows] plus the
     additive contributions of these rows to dK and dV ([Lk, D] each).
+
+    ``sink``: this head's sink logit, or None. It is one more score column,
+    allowed for every row, whose value row is zero: it enters every row's
+    softmax normalizer and takes probability mass without adding to O. Its
+    gradient is the chain rule through that column, dS_sink = P_sink (0 - Delta),
+    returned summed over the rows as "dSink".
     """
     Lq, Lk = q_h.shape[0], k_g.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
     ok = allowed_block(rows, Lq, Lk, mask, window)
     qb = q_h[rows]
     S = scale * (qb @ k_g.T)
+    if sink is not None:
+        S = np.concatenate([S, np.full((len(rows), 1), float(sink))], axis=1)
+        ok = np.concatenate([ok, np.ones((len(rows), 1), dtype=bool)], axis=1)
     P, lse = _softmax_rows(S, ok)
+    if sink is not None:
+        P, P_sink = P[:, :Lk], P[:, Lk]
     O = P @ v_g
     out = {"O": O, "lse": lse}
     if not want_grad:
@@ -149,6 +164,8 @@ def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True):
     out["dQ"] = scale * (dS @ k_g)
     out["dK"] = scale * (dS.T @ qb)
     out["dV"] = P.T @ dob
+    if sink is not None:
+        out["dSink"] = float(np.sum(P_sink * (0.0 - delta)))
     return out
 
 
@@ -160,9 +177,12 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024):
-    """O [B,Hq,Lq,D] and lse [B,Hq,Lq] for inputs [B,H,L,D] (any float dtype, upcast to fp64)."""
+def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024, sinks=None):
+    """O [B,Hq,Lq,D] and lse [B,Hq,Lq] for inputs [B,H,L,D] (any float dtype, upcast to fp64).
+
+    sinks: optional [Hq] sink logits (see head_rows)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
+    sinks = None if sinks is None else _f64(sinks)
     B, Hq, Lq, D = q.shape
     Hkv = k.shape[1]
     if Hq % Hkv:
@@ -175,15 +195,18 @@ def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024):
             g = h // group
             for r0 in range(0, Lq, row_block):
                 rows = np.arange(r0, min(Lq, r0 + row_block))
-                res = head_rows(q[b, h], k[b, g], v[b, g], None, scale, mask, window, rows, want_grad=False)
+                res = head_rows(q[b, h], k[b, g], v[b, g], None, scale, mask, window, rows, want_grad=False,
+                                sink=None if sinks is None else sinks[h])
                 O[b, h, rows] = res["O"]
                 lse[b, h, rows] = res["lse"]
     return O, lse
 
 
-def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024):
-    """Forward and closed-form backward. Returns dict O, lse, Delta, dQ, dK, dV (fp64 numpy)."""
+def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024, sinks=None):
+    """Forward and closed-form backward. Returns dict O, lse, Delta, dQ, dK, dV (fp64 numpy),
+    and dSinks [Hq] when sinks [Hq] are given."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    sinks = None if sinks is None else _f64(sinks)
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     if Hq % Hkv:
@@ -195,31 +218,38 @@ def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024):
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
+    dSinks = np.zeros(Hq)
     for b in range(B):
         for h in range(Hq):
             g = h // group
             for r0 in range(0, Lq, row_block):
                 rows = np.arange(r0, min(Lq, r0 + row_block))
-                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h], scale, mask, window, rows)
+                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h], scale, mask, window, rows,
+                                sink=None if sinks is None else sinks[h])
                 O[b, h, rows] = res["O"]
                 lse[b, h, rows] = res["lse"]
                 delta[b, h, rows] = res["Delta"]
                 dQ[b, h, rows] = res["dQ"]
                 dK[b, g] += res["dK"]
                 dV[b, g] += res["dV"]
-    return {"O": O, "lse": lse, "Delta": delta, "dQ": dQ, "dK": dK, "dV": dV}
+                if sinks is not None:
+                    dSinks[h] += res["dSink"]
+    out = {"O": O, "lse": lse, "Delta": delta, "dQ": dQ, "dK": dK, "dV": dV}
+    if sinks is not None:
+        out["dSinks"] = dSinks
+    return out
 
 
-def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows):
+def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows, sinks=None):
     """O, lse and dQ of selected query rows of head (b, h), from the full key range."""
     group = q.shape[1] // k.shape[1]
     g = h // group
     qh, kg, vg, doh = _f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g]), _f64(do[b, h])
-    res = head_rows(qh, kg, vg, doh, scale, mask, window, rows)
+    res = head_rows(qh, kg, vg, doh, scale, mask, window, rows, sink=None if sinks is None else _f64(sinks)[h])
     return {"O": res["O"], "lse": res["lse"], "dQ": res["dQ"]}
 
 
-def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024):
+def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024, sinks=None):
     """dK, dV of selected keys of kv head (b, g): every row that attends them, every q-head of the group."""
     Hq, Lq = q.shape[1], q.shape[2]
     Lk = k.shape[2]
@@ -232,7 +262,8 @@ def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024):
         qh, doh = _f64(q[b, h]), _f64(do[b, h])
         for r0 in range(0, len(rows), row_block):
             rr = rows[r0:r0 + row_block]
-            res = head_rows(qh, kg, vg, doh, scale, mask, window, rr)
+            res = head_rows(qh, kg, vg, doh, scale, mask, window, rr,
+                            sink=None if sinks is None else _f64(sinks)[h])
             dK += res["dK"]
             dV += res["dV"]
     keys = np.asarray(keys)

@@ -5,7 +5,7 @@ checks can be run against deliberately broken copies of it (mutation tests).
 Pins:
   golden       hand-derived worked example (tests/golden/worked_L2_D1.json)
   brute        pure-Python loops over the definition (forward: O, lse)
-  fd           central finite differences of l = sum(dO * O) (dQ, dK, dV)
+  fd           central finite differences of l = sum(dO * O) (dQ, dK, dV, dSinks)
   autograd     torch float64 autograd of a plain matmul/softmax forward
 """
 from __future__ import annotations
@@ -48,11 +48,13 @@ def pin_golden(mod, tol=1e-14):
     return worst
 
 
-def brute_forward(q, k, v, scale, mask, window):
+def brute_forward(q, k, v, scale, mask, window, sinks=None):
     """O and lse from the definition with Python loops and math.exp (no numpy linear algebra).
 
     Query row i sits at key position i + Lk - Lq (queries are the last Lq of
-    the Lk positions); a row with no allowed key gets O = 0, lse = -inf."""
+    the Lk positions); a row with no allowed key gets O = 0, lse = -inf (or
+    lse = its head's sink logit when sinks are given: the sink adds exp(sink)
+    to every row's normalizer and nothing to O)."""
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     group = Hq // Hkv
@@ -71,12 +73,13 @@ def brute_forward(q, k, v, scale, mask, window):
                     keys = [j for j in range(Lk) if pos - window < j <= pos]
                 else:  # "window": both sides of the diagonal
                     keys = [j for j in range(Lk) if abs(j - pos) < window]
+                sink = None if sinks is None else float(sinks[h])
                 if not keys:
-                    lse[b, h, i] = -math.inf
+                    lse[b, h, i] = -math.inf if sink is None else sink
                     continue
                 s = [scale * sum(float(q[b, h, i, d]) * float(k[b, g, j, d]) for d in range(D)) for j in keys]
-                mx = max(s)
-                z = sum(math.exp(x - mx) for x in s)
+                mx = max(s) if sink is None else max(max(s), sink)
+                z = sum(math.exp(x - mx) for x in s) + (0.0 if sink is None else math.exp(sink - mx))
                 lse[b, h, i] = mx + math.log(z)
                 for d in range(D):
                     O[b, h, i, d] = sum(math.exp(x - lse[b, h, i]) * float(v[b, g, j, d]) for x, j in zip(s, keys))
@@ -109,16 +112,25 @@ BRUTE_CASES = [
     (2, 1, 9, 4, 3, 0.8, "causal", 0),          # more queries than keys: the first rows see nothing
     (2, 2, 8, 5, 2, 1.3, "window", 2),
 ]
+# the same kind of cases with sink logits (per head)
+BRUTE_SINK_CASES = [
+    ((2, 1, 7, 7, 3, 0.7, "causal", 0), (0.5, -1.0)),
+    ((2, 2, 6, 9, 2, 1.1, "window", 2), (2.0, -0.3)),
+    ((2, 1, 9, 4, 3, 0.8, "causal", 0), (1.5, 0.0)),      # rows with no key: lse = sink
+]
 
 
 def pin_brute(mod, cases=None):
     """Max abs error of oracle O/lse against brute force over a few tiny cases (lse -inf must match)."""
-    cases = cases or BRUTE_CASES
+    cases = cases or [(c, None) for c in BRUTE_CASES] + BRUTE_SINK_CASES
     worst = 0.0
-    for n, (Hq, Hkv, Lq, Lk, D, s, mask, W) in enumerate(cases):
+    for n, (case, sinks) in enumerate(cases):
+        Hq, Hkv, Lq, Lk, D, s, mask, W = case
         q, k, v, _ = tiny_inputs(Hq, Hkv, Lq, D, 100 + n, Lk)
-        O, lse = mod.sdpa_forward(q, k, v, s, mask, W)
-        Ob, lb = brute_forward(q, k, v, s, mask, W)
+        sinks = None if sinks is None else np.array(sinks, dtype=np.float64)
+        O, lse = (mod.sdpa_forward(q, k, v, s, mask, W) if sinks is None else
+                  mod.sdpa_forward(q, k, v, s, mask, W, sinks=sinks))
+        Ob, lb = brute_forward(q, k, v, s, mask, W, sinks)
         if not np.all(np.isfinite(O)):
             return math.inf
         fin = np.isfinite(lb)
@@ -128,20 +140,25 @@ def pin_brute(mod, cases=None):
     return worst
 
 
-def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None):
-    """max|FD - analytic| / max|analytic| over every coordinate of Q, K and V."""
+def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None, sinks=None):
+    """max|FD - analytic| / max|analytic| over every coordinate of Q, K and V (and the sinks)."""
     q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed, Lk)
-    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
+    kw = {} if sinks is None else {"sinks": np.asarray(sinks, dtype=np.float64)}
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, **kw)
     grads = {"q": res["dQ"], "k": res["dK"], "v": res["dV"]}
+    base = {"q": q, "k": k, "v": v}
+    if sinks is not None:
+        grads["sinks"] = res["dSinks"]
+        base["sinks"] = kw["sinks"]
 
-    def loss(qq, kk, vv):
-        O, _ = mod.sdpa_forward(qq, kk, vv, scale, mask, window)
+    def loss(a):
+        extra = {} if sinks is None else {"sinks": a["sinks"]}
+        O, _ = mod.sdpa_forward(a["q"], a["k"], a["v"], scale, mask, window, **extra)
         return float(np.sum(do * O))
 
     worst = 0.0
     scale_ref = max(float(np.max(np.abs(g))) for g in grads.values())
-    for name in ("q", "k", "v"):
-        base = {"q": q, "k": k, "v": v}
+    for name in base:
         x = base[name]
         fd = np.zeros_like(x)
         it = np.nditer(x, flags=["multi_index"])
@@ -153,9 +170,7 @@ def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None):
             xp[idx] = x0 + h
             xm = x.copy()
             xm[idx] = x0 - h
-            args_p = dict(base, **{name: xp})
-            args_m = dict(base, **{name: xm})
-            fd[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            fd[idx] = (loss(dict(base, **{name: xp})) - loss(dict(base, **{name: xm}))) / (2 * h)
         worst = max(worst, float(np.max(np.abs(fd - grads[name]))))
     return worst / scale_ref
 
@@ -202,9 +217,10 @@ def torch_mask(Lq, Lk, mask, window):
     raise ValueError(mask)
 
 
-def torch_plain(q, k, v, do, scale, mask, window):
+def torch_plain(q, k, v, do, scale, mask, window, sinks=None):
     """float64 autograd of the plain forward: matmul -> -inf mask -> softmax -> matmul
-    (every row must have an allowed key)."""
+    (every row must have an allowed key, or a sink). Sinks: one more score
+    column per head, concatenated after masking, whose value row is zero."""
     q = torch.tensor(q, dtype=torch.float64, requires_grad=True)
     k = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     v = torch.tensor(v, dtype=torch.float64, requires_grad=True)
@@ -212,14 +228,23 @@ def torch_plain(q, k, v, do, scale, mask, window):
     kk = k.repeat_interleave(group, dim=1)
     vv = v.repeat_interleave(group, dim=1)
     ok = torch_mask(q.shape[2], k.shape[2], mask, window)
-    assert bool(ok.any(dim=1).all()), "a row with no allowed key"
     S = scale * torch.matmul(q, kk.transpose(-1, -2).contiguous())
     S = S.masked_fill(~ok, float("-inf"))
+    if sinks is not None:
+        sk = torch.tensor(sinks, dtype=torch.float64, requires_grad=True)
+        col = sk.view(1, -1, 1, 1).expand(S.shape[0], S.shape[1], S.shape[2], 1)
+        S = torch.cat([S, col], dim=-1)
+        vv = torch.cat([vv, torch.zeros_like(vv[:, :, :1])], dim=2)
+    else:
+        assert bool(ok.any(dim=1).all()), "a row with no allowed key"
     lse = torch.logsumexp(S, dim=-1)
     O = torch.matmul(torch.softmax(S, dim=-1), vv)
     O.backward(torch.tensor(do, dtype=torch.float64))
-    return {"O": O.detach().numpy(), "lse": lse.detach().numpy(), "dQ": q.grad.numpy(),
-            "dK": k.grad.numpy(), "dV": v.grad.numpy()}
+    out = {"O": O.detach().numpy(), "lse": lse.detach().numpy(), "dQ": q.grad.numpy(),
+           "dK": k.grad.numpy(), "dV": v.grad.numpy()}
+    if sinks is not None:
+        out["dSinks"] = sk.grad.numpy()
+    return out
 
 
 def rel_fro(x, ref):
@@ -228,7 +253,11 @@ def rel_fro(x, ref):
     return num / den if den > 0 else num
 
 
-def autograd_error(mod, q, k, v, do, scale, mask, window):
-    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
-    ref = torch_plain(q, k, v, do, scale, mask, window)
-    return max(rel_fro(res[n], ref[n]) for n in ("O", "lse", "dQ", "dK", "dV"))
+def autograd_error(mod, q, k, v, do, scale, mask, window, sinks=None):
+    if sinks is None:
+        res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
+    else:
+        res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, sinks=np.asarray(sinks, dtype=np.float64))
+    ref = torch_plain(q, k, v, do, scale, mask, window, sinks)
+    names = ("O", "lse", "dQ", "dK", "dV") + (() if sinks is None else ("dSinks",))
+    return max(rel_fro(res[n], ref[n]) for n in names)

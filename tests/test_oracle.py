@@ -160,6 +160,52 @@ def test_library_sdpa_no_mask_and_lower_right_causal():
             assert pins.rel_fro(O, ref.numpy()) <= 1e-12
 
 
+# ---------------------------------------------------------------- sinks
+SINK_FD = [
+    # Hq, Hkv, Lq, Lk, D, scale, mask, window, sinks
+    (2, 1, 7, 7, 4, 0.7, "causal", 0, (0.4, -1.2)),
+    (2, 2, 9, 9, 4, 1.0, "causal_window", 3, (2.5, 0.0)),
+    (2, 1, 5, 11, 4, 0.9, "window", 2, (-0.5, 1.0)),
+    (2, 1, 9, 4, 4, 0.8, "causal", 0, (1.0, 0.2)),       # rows with no key
+    (2, 1, 6, 6, 4, 0.6, "none", 0, (3.0, -3.0)),
+]
+
+
+@pytest.mark.parametrize("case", SINK_FD, ids=[str(c) for c in SINK_FD])
+def test_sinks_finite_differences(case):
+    Hq, Hkv, Lq, Lk, D, s, mask, W, sinks = case
+    assert pins.fd_error(sdpa_oracle, Hq, Hkv, Lq, D, s, mask, W, Lk=Lk, sinks=sinks) <= 1e-7
+
+
+@pytest.mark.parametrize("mask,window,Lq,Lk", [("causal_window", 64, 300, 300), ("none", 0, 200, 350),
+                                               ("causal", 0, 400, 150)])
+def test_sinks_autograd_independent(mask, window, Lq, Lk):
+    q, k, v, do = pins.tiny_inputs(4, 2, Lq, 32, 79, Lk)
+    sinks = np.array([0.5, -2.0, 3.0, 1.25])
+    err = pins.autograd_error(sdpa_oracle, q, k, v, do, 32 ** -0.5, mask, window, sinks)
+    assert err <= 1e-12, err
+
+
+def test_sink_at_minus_infinity_is_no_sink_bitwise():
+    q, k, v, do = pins.tiny_inputs(4, 2, 30, 8, 80, 41)
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, "window", 5)
+    b = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, "window", 5, sinks=np.full(4, -np.inf))
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+    assert np.all(b["dSinks"] == 0)
+
+
+def test_sink_takes_mass_without_value():
+    # with sinks, lse = log(exp(lse0) + exp(sink)) and O = O0 * exp(lse0 - lse)
+    q, k, v, do = pins.tiny_inputs(2, 1, 25, 8, 81, 25)
+    sinks = np.array([1.0, -0.5])
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 0.9, "causal", 0)
+    b = oracle.sdpa_fwd_bwd(q, k, v, do, 0.9, "causal", 0, sinks=sinks)
+    lse = np.logaddexp(a["lse"], sinks[None, :, None])
+    assert np.max(np.abs(b["lse"] - lse)) <= 1e-13
+    assert np.max(np.abs(b["O"] - a["O"] * np.exp(a["lse"] - lse)[..., None])) <= 1e-13
+
+
 # ---------------------------------------------------------------- invariants
 def _rand(Hq=4, Hkv=2, L=37, D=8, seed=5, Lk=None):
     return pins.tiny_inputs(Hq, Hkv, L, D, seed, Lk)
@@ -373,6 +419,10 @@ MUTATIONS = [
     ("d = i + (Lk - Lq) - j", "d = i + (Lq - Lk) - j"),                              # diagonal offset sign
     ("d = i + (Lk - Lq) - j", "d = i - j"),                                          # top-left alignment
     ("nonempty = tot > 0", "nonempty = tot >= 0"),                                   # empty rows -> NaN
+    ('out["dSink"] = float(np.sum(P_sink * (0.0 - delta)))', 'out["dSink"] = float(np.sum(P_sink * delta))'),  # sink sign
+    ("np.full((len(rows), 1), float(sink))", "np.full((len(rows), 1), 2 * float(sink))"),  # sink logit scaled
+    ("ok = np.concatenate([ok, np.ones((len(rows), 1), dtype=bool)], axis=1)",
+     "ok = np.concatenate([ok, np.zeros((len(rows), 1), dtype=bool)], axis=1)"),      # sink dropped
     ("g = h // group\n            for r0 in range(0, Lq, row_block):\n                rows = np.arange(r0, min(Lq, r0 + row_block))\n                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h]",
      "g = h % Hkv\n            for r0 in range(0, Lq, row_block):\n                rows = np.arange(r0, min(Lq, r0 + row_block))\n                res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h]"),  # GQA map
     ("lse = m_safe + np.log(tot)", "lse = m_safe + np.log(tot + 1e-3)"),          # wrong normaliser
@@ -407,6 +457,11 @@ def _pins_catch(mod):
                 failures.append(f"fd{case}")
         except Exception:
             failures.append("fd-raised")
+    try:
+        if not pins.fd_error(mod, 2, 1, 6, 3, 0.8, "causal", 0, sinks=(0.5, -1.0)) <= 1e-7:
+            failures.append("fd-sinks")
+    except Exception:
+        failures.append("fd-sinks-raised")
     return failures
 
 
