@@ -117,9 +117,17 @@ typedef struct {
 } sdpa_strides;
 
 /* sdpa_fwd_lse for tensors in any strided layout, e.g. [B, L, H, D] projection
- * outputs or views into a fused QKV buffer. `strides` points to 4 entries, for
- * q, k, v and o in that order (NULL: all contiguous [B, H, L, D]); lse stays
- * contiguous [B, Hq, Lq]. Each stride must be >= 0 and a multiple of
+ * outputs or views into a fused QKV buffer, and with optional attention
+ * sinks. `strides` points to 4 entries, for q, k, v and o in that order
+ * (NULL: all contiguous [B, H, L, D]); lse stays contiguous [B, Hq, Lq].
+ * `sinks` (NULL: none) is a DEVICE array of Hq float32 logits, one per query
+ * head, 16-byte aligned: sink h joins every row's softmax normalizer as one
+ * more score with a zero value row, lse_i = log(exp(sinks[h]) + sum_j
+ * exp(S_ij)), so it takes probability mass without adding to O (the pages
+ * list sinks among the backward's parameters: page "Lab 028 lab detail: Off
+ * NVIDIA, you fix the platform yourself", "What I changed, in plain terms",
+ * item 2). -INFINITY is no sink; a row with no allowed key gets lse =
+ * sinks[h] and O = 0. Each stride must be >= 0 and a multiple of
  * 16 bytes' worth of elements, each row stride at least D and below 2^23;
  * otherwise SDPA_ERR_INVALID_ARG. K and V must have the same row stride (and,
  * in the backward, Q and dO), else SDPA_ERR_UNSUPPORTED: true of [B, L, H, D]
@@ -128,7 +136,7 @@ typedef struct {
 int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                          int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                          int32_t dtype, int32_t mask, int32_t window, float scale,
-                         const sdpa_strides* strides, hipStream_t stream);
+                         const float* sinks, const sdpa_strides* strides, hipStream_t stream);
 
 /* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
  * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, Lq]),
@@ -150,15 +158,19 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t dtype, int32_t mask, int32_t window, float scale,
              hipStream_t stream);
 
-/* sdpa_bwd for strided tensors: `strides` points to 8 entries, for q, k, v,
- * o, dO, dq, dk and dv in that order (NULL: all contiguous), with the rules
- * of sdpa_fwd_lse_strided. */
+/* sdpa_bwd for strided tensors and sinks: `strides` points to 8 entries, for
+ * q, k, v, o, dO, dq, dk and dv in that order (NULL: all contiguous), with
+ * the rules of sdpa_fwd_lse_strided. With `sinks` (the forward's, and lse
+ * from that forward), `dsinks` is a DEVICE array of Hq float32 that receives
+ * d sinks[h] = -sum over batches and rows of exp(sinks[h] - lse_i) Delta_i,
+ * Delta_i = <dO_i, O_i> (fully overwritten; reduced in a fixed order). sinks
+ * and dsinks are both NULL or both set (else SDPA_ERR_INVALID_ARG). */
 int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes,
                      int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                      int32_t dtype, int32_t mask, int32_t window, float scale,
-                     const sdpa_strides* strides, hipStream_t stream);
+                     const float* sinks, float* dsinks, const sdpa_strides* strides, hipStream_t stream);
 
 /* Measurement variant of sdpa_bwd: identical arguments and results, plus two
  * caller-created HIP events. When both are non-null, `main_begin` and
@@ -177,7 +189,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 201. */
+/* ABI version of this header (major * 100 + minor): 202. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

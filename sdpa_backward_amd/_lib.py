@@ -59,9 +59,9 @@ def load(path: str = LIB_PATH):
     dims = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]  # B Hq group Lq Lk D dtype mask window scale
     st = ctypes.POINTER(SdpaStrides)
     lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + dims + [p]
-    lib.sdpa_fwd_lse_strided.argtypes = [p, p, p, p, p] + dims + [st, p]
+    lib.sdpa_fwd_lse_strided.argtypes = [p, p, p, p, p] + dims + [p, st, p]
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
-    lib.sdpa_bwd_strided.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [st, p]
+    lib.sdpa_bwd_strided.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, st, p]
     lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, p]
     for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_strided", "sdpa_bwd", "sdpa_bwd_strided", "sdpa_bwd_timed"):
         getattr(lib, f).restype = ctypes.c_int
@@ -128,6 +128,17 @@ def _same_rows(a, b):
     return a.contiguous(), b.contiguous()
 
 
+def _sinks_arg(sinks, q, Hq):
+    """Sink logits as a 16-byte-aligned float32 [Hq] device tensor (or None)."""
+    if sinks is None:
+        return None
+    if sinks.device != q.device or sinks.dtype != torch.float32 or sinks.shape != (Hq,):
+        raise ValueError(f"sinks must be float32 [Hq={Hq}] on {q.device}")
+    if not sinks.is_contiguous() or sinks.data_ptr() % 16:
+        sinks = sinks.clone()
+    return sinks
+
+
 def _mask_args(mask, window):
     if mask not in MASK:
         raise ValueError(f"mask must be one of {tuple(MASK)}")
@@ -145,14 +156,16 @@ def _out_like(t, out):
     return o
 
 
-def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None):
+def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None, sinks=None):
     """O [B,Hq,Lq,D] (q.dtype) and lse [B,Hq,Lq] (float32, natural log).
 
     k, v are [B, Hkv, Lk, D]; with Lk != Lq the queries are the last Lq key
     positions. mask: "none", "causal", "causal_window" (window keys up to the
-    diagonal) or "window" (window - 1 keys either side of it). O takes q's
+    diagonal) or "window" (window - 1 keys either side of it). sinks: optional
+    float32 [Hq] logits that join every row's softmax normalizer. O takes q's
     strides when q is dense (e.g. a [B, L, H, D] layout stays one)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v)
+    sinks = _sinks_arg(sinks, q, Hq)
     k, v = _same_rows(k, v)
     scale = default_scale(D) if scale is None else float(scale)
     m, w = _mask_args(mask, window)
@@ -161,7 +174,8 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, L]")
     st = load().sdpa_fwd_lse_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
-                                     DTYPE[q.dtype], m, w, scale, _strides(q, k, v, o), _stream(q.device))
+                                     DTYPE[q.dtype], m, w, scale, _ptr(sinks), _strides(q, k, v, o),
+                                     _stream(q.device))
     _check("sdpa_fwd_lse_strided", st)
     return o, lse
 
@@ -171,13 +185,16 @@ def workspace_bytes(B, Hq, L, D, dtype):
 
 
 def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None,
-             main_events=None):
-    """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse).
+             main_events=None, sinks=None):
+    """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse);
+    with ``sinks`` (the forward's), also d sinks: (dq, dk, dv, dsinks).
 
     Gradients take the strides of q, k, v when those are dense. ``main_events``:
     optional pair of raw hipEvent_t handles recorded around the main backward
-    kernel (sdpa_bwd_timed; contiguous tensors only)."""
+    kernel (sdpa_bwd_timed; contiguous tensors, no sinks)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v, (("o", o), ("do", do)))
+    sinks = _sinks_arg(sinks, q, Hq)
+    dsinks = None if sinks is None else torch.empty(Hq, dtype=torch.float32, device=q.device)
     if o.shape != q.shape or do.shape != q.shape:
         raise ValueError("o and do must match q")
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -197,10 +214,11 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
             _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale)
     if main_events is None:
         strides = _strides(q, k, v, o, do, dq, dk, dv)
-        _check("sdpa_bwd_strided", load().sdpa_bwd_strided(*args, strides, _stream(q.device)))
+        _check("sdpa_bwd_strided", load().sdpa_bwd_strided(*args, _ptr(sinks), _ptr(dsinks), strides,
+                                                             _stream(q.device)))
     else:
-        if not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
-            raise ValueError("the timed backward takes contiguous tensors")
+        if sinks is not None or not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
+            raise ValueError("the timed backward takes contiguous tensors and no sinks")
         ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
         _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), ev0, ev1))
-    return dq, dk, dv
+    return (dq, dk, dv) if sinks is None else (dq, dk, dv, dsinks)

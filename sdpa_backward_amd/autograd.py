@@ -14,23 +14,26 @@ from ._lib import sdpa_bwd, sdpa_fwd_lse
 
 
 class SDPAFunction(torch.autograd.Function):
-    """O = softmax(scale * Q K^T + mask) V with the library's forward and backward."""
+    """O = softmax(scale * Q K^T + mask) V with the library's forward and backward
+    (and optional per-head sink logits in every row's normalizer)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask="causal", window=0, scale=None):
-        o, lse = sdpa_fwd_lse(q, k, v, mask, window, scale)
-        ctx.save_for_backward(q, k, v, o, lse)
+    def forward(ctx, q, k, v, mask="causal", window=0, scale=None, sinks=None):
+        o, lse = sdpa_fwd_lse(q, k, v, mask, window, scale, sinks=sinks)
+        ctx.save_for_backward(q, k, v, o, lse, sinks)
         ctx.cfg = (mask, window, scale)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
+        q, k, v, o, lse, sinks = ctx.saved_tensors
         mask, window, scale = ctx.cfg
-        dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale)
-        return dq, dk, dv, None, None, None
+        grads = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale, sinks=sinks)
+        dsinks = grads[3] if sinks is not None else None
+        return grads[0], grads[1], grads[2], None, None, None, dsinks
 
 
-def attention(q, k, v, mask="causal", window=0, scale=None):
-    """Differentiable attention over [B, H, L, D] tensors (q: Hq heads, k/v: Hkv heads, Hq % Hkv == 0)."""
-    return SDPAFunction.apply(q, k, v, mask, window, scale)
+def attention(q, k, v, mask="causal", window=0, scale=None, sinks=None):
+    """Differentiable attention over [B, H, L, D] tensors (q: Hq heads, k/v: Hkv heads, Hq % Hkv == 0);
+    sinks: optional float32 [Hq] logits (differentiable)."""
+    return SDPAFunction.apply(q, k, v, mask, window, scale, sinks)

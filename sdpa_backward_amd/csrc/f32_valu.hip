@@ -15,8 +15,8 @@ namespace sdpa {
 template <int D>
 __global__ void __launch_bounds__(128)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-               float* __restrict__ O, float* __restrict__ LSE, int Hq, int group, int Lq, int Lk, int dlo,
-               int dhi, float scale, AllStrides st) {
+               float* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ Sinks, int Hq,
+               int group, int Lq, int Lk, int dlo, int dhi, float scale, AllStrides st) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= Lq) return;
@@ -29,21 +29,22 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   for (int d = 0; d < D; d++) qr[d] = q[d];
   // allowed keys of row i: dlo <= j - i <= dhi, 0 <= j < Lk (empty: O = 0, lse = -inf)
   const int jlo = max(0, i + dlo), jhi = min(Lk - 1, i + dhi);
-  float m = -INFINITY;
+  const float sink = Sinks != nullptr ? Sinks[h] : -INFINITY;  // one more score, with a zero value row
+  float m = sink;
   for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
     m = fmaxf(m, s * scale);
   }
-  float l = 0.f;
+  float l = sink != -INFINITY ? expf(sink - m) : 0.f;
   for (int j = jlo; j <= jhi; j++) {
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
     l += expf(s * scale - m);
   }
-  const float lse = jlo <= jhi ? m + logf(l) : -INFINITY;
+  const float lse = l > 0.f ? m + logf(l) : -INFINITY;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; d++) acc[d] = 0.f;
@@ -160,11 +161,11 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
 
 template <int D>
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
-                          hipStream_t stream) {
+                          const float* sinks, int group, int Lq, int Lk, int dlo, int dhi, float scale,
+                          const AllStrides& st, hipStream_t stream) {
   dim3 grid((Lq + 127) / 128, Hq, B);
   hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (float*)o, lse, Hq, group, Lq, Lk, dlo, dhi, scale, st);
+                     (const float*)v, (float*)o, lse, sinks, Hq, group, Lq, Lk, dlo, dhi, scale, st);
   return hipGetLastError();
 }
 
@@ -197,8 +198,9 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
 }
 
 #define SDPA_INST_F32(D)                                                                                    \
-  template hipError_t launch_fwd_f32<D>(const void*, const void*, const void*, void*, float*, int, int, int, \
-                                        int, int, int, int, float, const AllStrides&, hipStream_t);         \
+  template hipError_t launch_fwd_f32<D>(const void*, const void*, const void*, void*, float*, int, int,      \
+                                        const float*, int, int, int, int, int, float, const AllStrides&,    \
+                                        hipStream_t);                                                       \
   template hipError_t launch_bwd_f32<D>(const void*, const void*, const void*, const void*, const void*,     \
                                         const float*, void*, void*, void*, float*, int, int, int, int, int,  \
                                         int, int, float, const AllStrides&, hipStream_t, hipEvent_t,         \

@@ -77,8 +77,8 @@ template <int D, int MODE, typename E, bool DENSE>
 __global__ void __launch_bounds__(256, 1)
 qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ LSE,
-          float* __restrict__ Delta, E* __restrict__ Out, int Hq, int group, int Lq, int Lk, int dlo,
-          int dhi, float scale, float scale_log2, AllStrides st_arg) {
+          float* __restrict__ Delta, E* __restrict__ Out, const float* __restrict__ Sinks, int Hq, int group,
+          int Lq, int Lk, int dlo, int dhi, float scale, float scale_log2, AllStrides st_arg) {
   using C = QsCfg<D>;
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
@@ -150,6 +150,14 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 #pragma unroll
   for (int d = 0; d < NDB; d++) acc[d] = zero16();
   float m = -INFINITY, lsum = 0.f;  // forward: running (used) max in log2 units and row sum
+  if constexpr (MODE == QS_FWD) {
+    // a sink logit joins the normalizer from the start: it becomes the used
+    // max, contributing exp2(m - m) = 1 to the sum (and nothing to O)
+    if (Sinks != nullptr) {
+      const float sg = Sinks[h] * kLog2e;
+      if (sg != -INFINITY) m = sg, lsum = 1.f;
+    }
+  }
 
   // key tiles that a row of this workgroup can see (none: kt_hi < kt_lo)
   const int i1 = min(i0 + C::BQ - 1, Lq - 1);
@@ -351,26 +359,26 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
-                     float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-                     float scale, const AllStrides& st, hipStream_t stream) {
+                     float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk,
+                     int dlo, int dhi, float scale, const AllStrides& st, hipStream_t stream) {
   using C = QsCfg<D>;
   const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   auto kernel = is_dense<D>(st, Hq, Hq / group, Lq, Lk) ? qs_kernel<D, MODE, E, true> : qs_kernel<D, MODE, E, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)o, (const E*)dO, lse, delta, (E*)out, Hq, group, Lq, Lk, dlo, dhi, scale,
+                     (const E*)o, (const E*)dO, lse, delta, (E*)out, sinks, Hq, group, Lq, Lk, dlo, dhi, scale,
                      scale * kLog2e, st);
   return hipGetLastError();
 }
 
 #define SDPA_INST_QS(D, E)                                                                                  \
   template hipError_t launch_qs<D, QS_FWD, E>(const void*, const void*, const void*, const void*, const void*, \
-                                              float*, float*, void*, int, int, int, int, int, int, int, float,   \
-                                              const AllStrides&, hipStream_t);                                 \
+                                              float*, float*, void*, const float*, int, int, int, int, int, int, \
+                                              int, float, const AllStrides&, hipStream_t);                     \
   template hipError_t launch_qs<D, QS_DQ, E>(const void*, const void*, const void*, const void*, const void*,  \
-                                             float*, float*, void*, int, int, int, int, int, int, int, float,    \
-                                             const AllStrides&, hipStream_t);
+                                             float*, float*, void*, const float*, int, int, int, int, int, int,  \
+                                             int, float, const AllStrides&, hipStream_t);
 SDPA_INST_QS(64, bf16)
 SDPA_INST_QS(128, bf16)
 SDPA_INST_QS(256, bf16)

@@ -18,15 +18,17 @@ namespace sdpa {
 enum { QS_FWD = 0, QS_DQ = 1 };
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
-                     float* delta, void* out, int B, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-                     float scale, const AllStrides& st, hipStream_t stream);
+                     float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                     int dhi, float scale, const AllStrides& st, hipStream_t stream);
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
                      int dhi, float scale, const AllStrides& st, hipStream_t stream);
 template <int D>
-hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
-                          int, float, const AllStrides&, hipStream_t);
+hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, const float*, int, int,
+                          int, int, int, float, const AllStrides&, hipStream_t);
+hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks, int B, int Hq,
+                         int Lq, hipStream_t stream);
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
                           void*, void*, void*, float*, int, int, int, int, int, int, int, float,
@@ -39,8 +41,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
                            hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, B, Hq, group, Lq, Lk,
-                                        dlo, dhi, scale, st, stream);
+  hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group,
+                                        Lq, Lk, dlo, dhi, scale, st, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
@@ -160,7 +162,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 201; }
+int sdpa_abi_version(void) { return 202; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -181,7 +183,8 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
 
 int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
                          int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask,
-                         int32_t window, float scale, const sdpa_strides* strides, hipStream_t stream) {
+                         int32_t window, float scale, const float* sinks, const sdpa_strides* strides,
+                         hipStream_t stream) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -196,8 +199,8 @@ int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, f
   switch (dtype * 1000 + D) {
 #define SDPA_FWD_CASE(DT, E, DD)                                                                          \
   case DT * 1000 + DD:                                                                                    \
-    return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, B,  \
-                                                          Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
+    return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, sinks, \
+                                                          B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
     SDPA_FWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 256)
@@ -209,10 +212,10 @@ int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, f
 #undef SDPA_FWD_CASE
     case SDPA_F32 * 1000 + 64:
       return to_status(
-          sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
+          sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, scale, str, stream));
     case SDPA_F32 * 1000 + 128:
       return to_status(
-          sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
+          sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, scale, str, stream));
   }
   return SDPA_ERR_UNSUPPORTED;
 }
@@ -221,7 +224,7 @@ int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* ls
                  int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
                  float scale, hipStream_t stream) {
   return sdpa_fwd_lse_strided(q, k, v, o, lse, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr,
-                              stream);
+                              nullptr, stream);
 }
 
 }  // extern "C"
@@ -231,12 +234,17 @@ namespace {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
-             float scale, const sdpa_strides* strides, hipStream_t stream, hipEvent_t main_begin,
-             hipEvent_t main_end) {
+             float scale, const float* sinks, float* dsinks, const sdpa_strides* strides, hipStream_t stream,
+             hipEvent_t main_begin, hipEvent_t main_end) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
-  if (s.no_rows() && s.no_keys()) return SDPA_OK;
+  if ((sinks == nullptr) != (dsinks == nullptr)) return SDPA_ERR_INVALID_ARG;
+  if (s.B == 0 || s.Hq == 0) return SDPA_OK;
+  if (sinks != nullptr && (!aligned16(sinks) || !aligned16(dsinks))) return SDPA_ERR_INVALID_ARG;
+  if (s.no_rows() && s.no_keys()) return sinks ? to_status(sdpa::launch_dsinks(nullptr, nullptr, sinks, dsinks, B,
+                                                                               Hq, 0, stream))
+                                               : SDPA_OK;
   const bool rows = !s.no_rows(), keys = !s.no_keys();
   if (!ptr_ok(q, rows) || !ptr_ok(o, rows) || !ptr_ok(dO, rows) || !ptr_ok(lse, rows) || !ptr_ok(dq, rows) ||
       !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(dk, keys) || !ptr_ok(dv, keys))
@@ -249,11 +257,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   float* delta = static_cast<float*>(workspace);
   int dlo, dhi;
   s.band(dlo, dhi);
+  hipError_t e;
   switch (dtype * 1000 + D) {
-#define SDPA_BWD_CASE(DT, E, DD)                                                                           \
-  case DT * 1000 + DD:                                                                                     \
-    return to_status(sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, \
-                                                  Lk, dlo, dhi, scale, str, stream, main_begin, main_end));
+#define SDPA_BWD_CASE(DT, E, DD)                                                                              \
+  case DT * 1000 + DD:                                                                                        \
+    e = sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi,   \
+                                     scale, str, stream, main_begin, main_end);                               \
+    break;
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 256)
@@ -264,13 +274,20 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     SDPA_BWD_CASE(SDPA_F16, f16, 512)
 #undef SDPA_BWD_CASE
     case SDPA_F32 * 1000 + 64:
-      return to_status(sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                dlo, dhi, scale, str, stream, main_begin, main_end));
+      e = sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, scale,
+                                   str, stream, main_begin, main_end);
+      break;
     case SDPA_F32 * 1000 + 128:
-      return to_status(sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk,
-                                                 dlo, dhi, scale, str, stream, main_begin, main_end));
+      e = sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, scale,
+                                    str, stream, main_begin, main_end);
+      break;
+    default:
+      return SDPA_ERR_UNSUPPORTED;
   }
-  return SDPA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return SDPA_ERR_LAUNCH;
+  // d sigma_h from lse and Delta (the dQ pass wrote Delta into the workspace)
+  if (sinks != nullptr) e = sdpa::launch_dsinks(lse, delta, sinks, dsinks, B, Hq, Lq, stream);
+  return to_status(e);
 }
 
 }  // namespace
@@ -280,10 +297,10 @@ extern "C" {
 int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                      int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
-                     int32_t mask, int32_t window, float scale, const sdpa_strides* strides,
-                     hipStream_t stream) {
+                     int32_t mask, int32_t window, float scale, const float* sinks, float* dsinks,
+                     const sdpa_strides* strides, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, strides, stream, nullptr, nullptr);
+                  mask, window, scale, sinks, dsinks, strides, stream, nullptr, nullptr);
 }
 
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -292,7 +309,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
                    int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
                    hipEvent_t main_end) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, stream, main_begin, main_end);
+                  mask, window, scale, nullptr, nullptr, nullptr, stream, main_begin, main_end);
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -300,7 +317,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
              float scale, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, stream, nullptr, nullptr);
+                  mask, window, scale, nullptr, nullptr, nullptr, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

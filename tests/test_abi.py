@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 201
+    assert lib.sdpa_abi_version() == 202
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -199,19 +199,25 @@ def test_stride_errors(lib):
     p0[0] = 0
     good = _st(blhd_q, blhd_kv, blhd_kv, blhd_q)
     args = (B, Hq, 2, L, L, D, BF16, CAUSAL, 0, 0.125)
-    assert lib.sdpa_fwd_lse_strided(*[ctypes.c_void_p(x) for x in p0], *args, good, None) == INVALID
+    assert lib.sdpa_fwd_lse_strided(*[ctypes.c_void_p(x) for x in p0], *args, None, good, None) == INVALID
     p = [ctypes.c_void_p(FAKE)] * 5
     for bad in (_st(blhd_q, blhd_kv, blhd_kv, (0, D, D - 8)),          # row stride below D
                 _st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 4)),     # not a 16-byte multiple
                 _st(blhd_q, (-64, D, Hkv * D), blhd_kv, blhd_q),       # negative
                 _st(blhd_q, blhd_kv, blhd_kv, (0, D, 1 << 23))):       # row stride too large
-        assert lib.sdpa_fwd_lse_strided(*p, *args, bad, None) == INVALID
+        assert lib.sdpa_fwd_lse_strided(*p, *args, None, bad, None) == INVALID
     # K and V with different row strides: not built
-    assert lib.sdpa_fwd_lse_strided(*p, *args, _st(blhd_q, blhd_kv, (0, L * D, D), blhd_q), None) == UNSUPPORTED
+    assert lib.sdpa_fwd_lse_strided(*p, *args, None, _st(blhd_q, blhd_kv, (0, L * D, D), blhd_q), None) == UNSUPPORTED
     # backward: Q and dO must share their row stride too
     pb = [ctypes.c_void_p(FAKE)] * 9
     bad8 = _st(blhd_q, blhd_kv, blhd_kv, blhd_q, (0, L * D, D), blhd_q, blhd_kv, blhd_kv)
-    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, bad8, None) == UNSUPPORTED
+    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, None, None, bad8, None) == UNSUPPORTED
+    # sinks and their gradient come together
+    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, ctypes.c_void_p(FAKE), None, None,
+                                None) == INVALID
+    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, None, ctypes.c_void_p(FAKE), None,
+                                None) == INVALID
     # fp32 rows need 16-byte multiples too: 4 elements
     args32 = (B, Hq, 2, L, L, D, F32, CAUSAL, 0, 0.125)
-    assert lib.sdpa_fwd_lse_strided(*p, *args32, _st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)), None) == INVALID
+    assert lib.sdpa_fwd_lse_strided(*p, *args32, None, _st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)),
+                                    None) == INVALID
