@@ -24,6 +24,12 @@ What is computed, and where the pages define it
   non-causal window also drops the tiles wholly ahead). With queries a suffix of the keys,
   ``diag_off = Lk - Lq`` (same page, item 5(b), and the parity cases with
   ``qL < kL``). No mask: every key.
+* Block-sparse cut: the prefix-sharing forward runs one pass over
+  [prompt; chosen; rejected] under a mask that is causal except that the
+  rejected rows never see the chosen tokens (page "Training - design (ORPO,
+  flash-CCE head, prefix sharing, segmented backward)", section 5.4); here a
+  cut (r0, c0, c1) removes keys [c0, c1) from rows r0 onwards, on top of any
+  mask.
 * Sinks: the backward the pages patch also takes attention sinks as a
   parameter (Lab 028 page, "What I changed", item 2). Reading: one logit per
   query head that joins every row's softmax normalizer as an extra score
@@ -70,7 +76,7 @@ import numpy as np
 MASKS = ("none", "causal", "causal_window", "window")
 
 
-def allowed(i, j, Lq: int, Lk: int, mask: str, window: int):
+def allowed(i, j, Lq: int, Lk: int, mask: str, window: int, cut=None):
     """True where query row i may attend key j (numpy broadcasting over i, j).
 
     With d = i + diag_off - j, diag_off = Lk - Lq (the query's diagonal sits
@@ -80,6 +86,11 @@ def allowed(i, j, Lq: int, Lk: int, mask: str, window: int):
       causal_window: 0 <= d < window
       window:        -window < d < window   (both sides, diagonal included)
     Keys outside [0, Lk) and rows outside [0, Lq) do not exist.
+
+    cut = (r0, c0, c1): additionally, rows i >= r0 do not see keys
+    c0 <= j < c1 (the block-sparse prefix-sharing mask: with the sequence
+    [prompt; chosen; rejected], r0 = c1 = start of rejected and c0 = start of
+    chosen, so the rejected rows never see the chosen tokens).
     """
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
@@ -95,20 +106,23 @@ def allowed(i, j, Lq: int, Lk: int, mask: str, window: int):
         ok = ok & (d >= 0) & (d < window)
     elif mask == "window":
         ok = ok & (d > -window) & (d < window)
+    if cut is not None:
+        r0, c0, c1 = cut
+        ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))
     return ok
 
 
-def allowed_block(rows: np.ndarray, Lq: int, Lk: int, mask: str, window: int) -> np.ndarray:
+def allowed_block(rows: np.ndarray, Lq: int, Lk: int, mask: str, window: int, cut=None) -> np.ndarray:
     """Boolean [len(rows), Lk]: the allowed pairs of these query rows."""
-    return allowed(np.asarray(rows)[:, None], np.arange(Lk)[None, :], Lq, Lk, mask, window)
+    return allowed(np.asarray(rows)[:, None], np.arange(Lk)[None, :], Lq, Lk, mask, window, cut)
 
 
-def rows_attending(keys, Lq: int, Lk: int, mask: str, window: int) -> np.ndarray:
+def rows_attending(keys, Lq: int, Lk: int, mask: str, window: int, cut=None) -> np.ndarray:
     """Sorted query rows that attend at least one of ``keys`` (for sampled key gradients)."""
     rows = np.arange(Lq)
     hit = np.zeros(Lq, dtype=bool)
     for j in np.asarray(keys):
-        hit |= allowed(rows, int(j), Lq, Lk, mask, window)
+        hit |= allowed(rows, int(j), Lq, Lk, mask, window, cut)
     return rows[hit]
 
 
@@ -128,7 +142,7 @@ def _softmax_rows(S: np.ndarray, ok: np.ndarray):
     return P, lse
 
 
-def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True, sink=None):
+def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True, sink=None, cut=None):
     """Forward (and, with ``do_h``, backward) for one q-head and a set of query rows.
 
     q_h, do_h: [Lq, D]; k_g, v_g: [Lk, D] (fp64). Returns a dict with
@@ -143,7 +157,7 @@ def head_rows(q_h, k_g, v_g, do_h, scale, mask, window, rows, want_grad=True, si
     """
     Lq, Lk = q_h.shape[0], k_g.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    ok = allowed_block(rows, Lq, Lk, mask, window)
+    ok = allowed_block(rows, Lq, Lk, mask, window, cut)
     qb = q_h[rows]
     S = scale * (qb @ k_g.T)
     if sink is not None:
@@ -177,7 +191,7 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024, sinks=None):
+def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024, sinks=None, cut=None):
     """O [B,Hq,Lq,D] and lse [B,Hq,Lq] for inputs [B,H,L,D] (any float dtype, upcast to fp64).
 
     sinks: optional [Hq] sink logits (see head_rows)."""
@@ -196,13 +210,13 @@ def sdpa_forward(q, k, v, scale, mask="causal", window=0, row_block=1024, sinks=
             for r0 in range(0, Lq, row_block):
                 rows = np.arange(r0, min(Lq, r0 + row_block))
                 res = head_rows(q[b, h], k[b, g], v[b, g], None, scale, mask, window, rows, want_grad=False,
-                                sink=None if sinks is None else sinks[h])
+                                sink=None if sinks is None else sinks[h], cut=cut)
                 O[b, h, rows] = res["O"]
                 lse[b, h, rows] = res["lse"]
     return O, lse
 
 
-def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024, sinks=None):
+def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024, sinks=None, cut=None):
     """Forward and closed-form backward. Returns dict O, lse, Delta, dQ, dK, dV (fp64 numpy),
     and dSinks [Hq] when sinks [Hq] are given."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -225,7 +239,7 @@ def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024, si
             for r0 in range(0, Lq, row_block):
                 rows = np.arange(r0, min(Lq, r0 + row_block))
                 res = head_rows(q[b, h], k[b, g], v[b, g], do[b, h], scale, mask, window, rows,
-                                sink=None if sinks is None else sinks[h])
+                                sink=None if sinks is None else sinks[h], cut=cut)
                 O[b, h, rows] = res["O"]
                 lse[b, h, rows] = res["lse"]
                 delta[b, h, rows] = res["Delta"]
@@ -240,21 +254,22 @@ def sdpa_fwd_bwd(q, k, v, do, scale, mask="causal", window=0, row_block=1024, si
     return out
 
 
-def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows, sinks=None):
+def sampled_rows(q, k, v, do, scale, mask, window, b, h, rows, sinks=None, cut=None):
     """O, lse and dQ of selected query rows of head (b, h), from the full key range."""
     group = q.shape[1] // k.shape[1]
     g = h // group
     qh, kg, vg, doh = _f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g]), _f64(do[b, h])
-    res = head_rows(qh, kg, vg, doh, scale, mask, window, rows, sink=None if sinks is None else _f64(sinks)[h])
+    res = head_rows(qh, kg, vg, doh, scale, mask, window, rows, sink=None if sinks is None else _f64(sinks)[h],
+                    cut=cut)
     return {"O": res["O"], "lse": res["lse"], "dQ": res["dQ"]}
 
 
-def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024, sinks=None):
+def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024, sinks=None, cut=None):
     """dK, dV of selected keys of kv head (b, g): every row that attends them, every q-head of the group."""
     Hq, Lq = q.shape[1], q.shape[2]
     Lk = k.shape[2]
     group = Hq // k.shape[1]
-    rows = rows_attending(keys, Lq, Lk, mask, window)
+    rows = rows_attending(keys, Lq, Lk, mask, window, cut)
     kg, vg = _f64(k[b, g]), _f64(v[b, g])
     dK = np.zeros_like(kg)
     dV = np.zeros_like(vg)
@@ -263,7 +278,7 @@ def sampled_keys(q, k, v, do, scale, mask, window, b, g, keys, row_block=1024, s
         for r0 in range(0, len(rows), row_block):
             rr = rows[r0:r0 + row_block]
             res = head_rows(qh, kg, vg, doh, scale, mask, window, rr,
-                            sink=None if sinks is None else _f64(sinks)[h])
+                            sink=None if sinks is None else _f64(sinks)[h], cut=cut)
             dK += res["dK"]
             dV += res["dV"]
     keys = np.asarray(keys)

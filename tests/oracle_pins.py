@@ -48,7 +48,7 @@ def pin_golden(mod, tol=1e-14):
     return worst
 
 
-def brute_forward(q, k, v, scale, mask, window, sinks=None):
+def brute_forward(q, k, v, scale, mask, window, sinks=None, cut=None):
     """O and lse from the definition with Python loops and math.exp (no numpy linear algebra).
 
     Query row i sits at key position i + Lk - Lq (queries are the last Lq of
@@ -73,6 +73,8 @@ def brute_forward(q, k, v, scale, mask, window, sinks=None):
                     keys = [j for j in range(Lk) if pos - window < j <= pos]
                 else:  # "window": both sides of the diagonal
                     keys = [j for j in range(Lk) if abs(j - pos) < window]
+                if cut is not None and i >= cut[0]:   # rows from cut[0] on skip keys [cut[1], cut[2])
+                    keys = [j for j in keys if not cut[1] <= j < cut[2]]
                 sink = None if sinks is None else float(sinks[h])
                 if not keys:
                     lse[b, h, i] = -math.inf if sink is None else sink
@@ -112,6 +114,12 @@ BRUTE_CASES = [
     (2, 1, 9, 4, 3, 0.8, "causal", 0),          # more queries than keys: the first rows see nothing
     (2, 2, 8, 5, 2, 1.3, "window", 2),
 ]
+# [prompt 3; chosen 4; rejected 3] and a cut inside a suffix-query problem
+BRUTE_CUT_CASES = [
+    ((2, 1, 10, 10, 3, 0.8, "causal", 0), (7, 3, 7)),
+    ((2, 2, 6, 11, 2, 1.2, "causal_window", 4), (3, 2, 6)),
+    ((2, 1, 8, 8, 3, 0.6, "none", 0), (4, 0, 3)),
+]
 # the same kind of cases with sink logits (per head)
 BRUTE_SINK_CASES = [
     ((2, 1, 7, 7, 3, 0.7, "causal", 0), (0.5, -1.0)),
@@ -122,15 +130,19 @@ BRUTE_SINK_CASES = [
 
 def pin_brute(mod, cases=None):
     """Max abs error of oracle O/lse against brute force over a few tiny cases (lse -inf must match)."""
-    cases = cases or [(c, None) for c in BRUTE_CASES] + BRUTE_SINK_CASES
+    cases = cases or ([(c, None, None) for c in BRUTE_CASES] + [(c, sk, None) for c, sk in BRUTE_SINK_CASES] +
+                      [(c, None, cut) for c, cut in BRUTE_CUT_CASES])
     worst = 0.0
-    for n, (case, sinks) in enumerate(cases):
+    for n, (case, sinks, cut) in enumerate(cases):
         Hq, Hkv, Lq, Lk, D, s, mask, W = case
         q, k, v, _ = tiny_inputs(Hq, Hkv, Lq, D, 100 + n, Lk)
-        sinks = None if sinks is None else np.array(sinks, dtype=np.float64)
-        O, lse = (mod.sdpa_forward(q, k, v, s, mask, W) if sinks is None else
-                  mod.sdpa_forward(q, k, v, s, mask, W, sinks=sinks))
-        Ob, lb = brute_forward(q, k, v, s, mask, W, sinks)
+        kw = {}
+        if sinks is not None:
+            kw["sinks"] = np.array(sinks, dtype=np.float64)
+        if cut is not None:
+            kw["cut"] = cut
+        O, lse = mod.sdpa_forward(q, k, v, s, mask, W, **kw)
+        Ob, lb = brute_forward(q, k, v, s, mask, W, kw.get("sinks"), cut)
         if not np.all(np.isfinite(O)):
             return math.inf
         fin = np.isfinite(lb)
@@ -140,11 +152,12 @@ def pin_brute(mod, cases=None):
     return worst
 
 
-def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None, sinks=None):
+def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None, sinks=None, cut=None):
     """max|FD - analytic| / max|analytic| over every coordinate of Q, K and V (and the sinks)."""
     q, k, v, do = tiny_inputs(Hq, Hkv, L, D, seed, Lk)
     kw = {} if sinks is None else {"sinks": np.asarray(sinks, dtype=np.float64)}
-    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, **kw)
+    ckw = {} if cut is None else {"cut": cut}
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, **kw, **ckw)
     grads = {"q": res["dQ"], "k": res["dK"], "v": res["dV"]}
     base = {"q": q, "k": k, "v": v}
     if sinks is not None:
@@ -153,7 +166,7 @@ def fd_error(mod, Hq, Hkv, L, D, scale, mask, window, seed=0, Lk=None, sinks=Non
 
     def loss(a):
         extra = {} if sinks is None else {"sinks": a["sinks"]}
-        O, _ = mod.sdpa_forward(a["q"], a["k"], a["v"], scale, mask, window, **extra)
+        O, _ = mod.sdpa_forward(a["q"], a["k"], a["v"], scale, mask, window, **extra, **ckw)
         return float(np.sum(do * O))
 
     worst = 0.0
@@ -200,24 +213,29 @@ def fd_directional_error(mod, Hq, Hkv, L, D, scale, mask, window, ndir=16, seed=
     return worst
 
 
-def torch_mask(Lq, Lk, mask, window):
+def torch_mask(Lq, Lk, mask, window, cut=None):
     """Allowed pairs [Lq, Lk] built from torch's own band routines: tril keeps
     j <= i + diagonal and triu keeps j >= i + diagonal, with the diagonal moved
     Lk - Lq to the right (queries are the last Lq key positions)."""
     ones = torch.ones(Lq, Lk, dtype=torch.bool)
     off = Lk - Lq
     if mask == "none":
-        return ones
-    if mask == "causal":
-        return torch.tril(ones, diagonal=off)
-    if mask == "causal_window":
-        return torch.tril(ones, diagonal=off) & torch.triu(ones, diagonal=off - window + 1)
-    if mask == "window":
-        return torch.tril(ones, diagonal=off + window - 1) & torch.triu(ones, diagonal=off - window + 1)
-    raise ValueError(mask)
+        ok = ones
+    elif mask == "causal":
+        ok = torch.tril(ones, diagonal=off)
+    elif mask == "causal_window":
+        ok = torch.tril(ones, diagonal=off) & torch.triu(ones, diagonal=off - window + 1)
+    elif mask == "window":
+        ok = torch.tril(ones, diagonal=off + window - 1) & torch.triu(ones, diagonal=off - window + 1)
+    else:
+        raise ValueError(mask)
+    if cut is not None:   # a zeroed block: rows cut[0].. against keys cut[1]..cut[2]-1
+        ok = ok.clone()
+        ok[cut[0]:, cut[1]:cut[2]] = False
+    return ok
 
 
-def torch_plain(q, k, v, do, scale, mask, window, sinks=None):
+def torch_plain(q, k, v, do, scale, mask, window, sinks=None, cut=None):
     """float64 autograd of the plain forward: matmul -> -inf mask -> softmax -> matmul
     (every row must have an allowed key, or a sink). Sinks: one more score
     column per head, concatenated after masking, whose value row is zero."""
@@ -227,7 +245,7 @@ def torch_plain(q, k, v, do, scale, mask, window, sinks=None):
     group = q.shape[1] // k.shape[1]
     kk = k.repeat_interleave(group, dim=1)
     vv = v.repeat_interleave(group, dim=1)
-    ok = torch_mask(q.shape[2], k.shape[2], mask, window)
+    ok = torch_mask(q.shape[2], k.shape[2], mask, window, cut)
     S = scale * torch.matmul(q, kk.transpose(-1, -2).contiguous())
     S = S.masked_fill(~ok, float("-inf"))
     if sinks is not None:
@@ -253,11 +271,11 @@ def rel_fro(x, ref):
     return num / den if den > 0 else num
 
 
-def autograd_error(mod, q, k, v, do, scale, mask, window, sinks=None):
-    if sinks is None:
-        res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window)
-    else:
-        res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, sinks=np.asarray(sinks, dtype=np.float64))
-    ref = torch_plain(q, k, v, do, scale, mask, window, sinks)
+def autograd_error(mod, q, k, v, do, scale, mask, window, sinks=None, cut=None):
+    kw = {} if sinks is None else {"sinks": np.asarray(sinks, dtype=np.float64)}
+    if cut is not None:
+        kw["cut"] = cut
+    res = mod.sdpa_fwd_bwd(q, k, v, do, scale, mask, window, **kw)
+    ref = torch_plain(q, k, v, do, scale, mask, window, sinks, cut)
     names = ("O", "lse", "dQ", "dK", "dV") + (() if sinks is None else ("dSinks",))
     return max(rel_fro(res[n], ref[n]) for n in names)

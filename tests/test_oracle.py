@@ -206,6 +206,46 @@ def test_sink_takes_mass_without_value():
     assert np.max(np.abs(b["O"] - a["O"] * np.exp(a["lse"] - lse)[..., None])) <= 1e-13
 
 
+# ---------------------------------------------------------------- prefix-sharing cut
+@pytest.mark.parametrize("case", [(2, 1, 10, 4, 0.8, "causal", 0, (7, 3, 7)),
+                                  (2, 2, 12, 4, 1.0, "causal_window", 4, (8, 4, 8)),
+                                  (2, 1, 9, 4, 0.6, "none", 0, (5, 1, 4))], ids=["causal", "cwin", "none"])
+def test_cut_finite_differences(case):
+    Hq, Hkv, L, D, s, mask, W, cut = case
+    assert pins.fd_error(sdpa_oracle, Hq, Hkv, L, D, s, mask, W, cut=cut) <= 1e-7
+
+
+def test_cut_autograd_independent():
+    q, k, v, do = pins.tiny_inputs(4, 2, 300, 32, 82)
+    err = pins.autograd_error(sdpa_oracle, q, k, v, do, 32 ** -0.5, "causal", 0, cut=(220, 100, 220))
+    assert err <= 1e-12, err
+
+
+@pytest.mark.parametrize("P,Rc,Rr", [(40, 25, 30), (1, 7, 9), (50, 1, 1)])
+def test_prefix_sharing_equals_two_branches(P, Rc, Rr):
+    # One pass over [prompt; chosen; rejected] with the rejected rows cut off
+    # from the chosen keys equals two causal passes, [prompt; chosen] and
+    # [prompt; rejected], row for row; the prompt's keys collect the gradient
+    # of both branches (dO of the prompt rows counted once, in the first).
+    L = P + Rc + Rr
+    q, k, v, do = pins.tiny_inputs(4, 2, L, 8, 83)
+    cut = (P + Rc, P, P + Rc)
+    sh = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, "causal", 0, cut=cut)
+    a_idx = np.arange(P + Rc)
+    b_idx = np.concatenate([np.arange(P), np.arange(P + Rc, L)])
+    br_a = oracle.sdpa_fwd_bwd(q[:, :, a_idx], k[:, :, a_idx], v[:, :, a_idx], do[:, :, a_idx], 0.7, "causal", 0)
+    do_b = do[:, :, b_idx].copy()
+    do_b[:, :, :P] = 0.0
+    br_b = oracle.sdpa_fwd_bwd(q[:, :, b_idx], k[:, :, b_idx], v[:, :, b_idx], do_b, 0.7, "causal", 0)
+    for n in ("O", "lse", "dQ"):
+        assert np.max(np.abs(sh[n][:, :, :P + Rc] - br_a[n])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P + Rc:] - br_b[n][:, :, P:])) <= 1e-13, n
+    for n in ("dK", "dV"):
+        assert np.max(np.abs(sh[n][:, :, :P] - br_a[n][:, :, :P] - br_b[n][:, :, :P])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P:P + Rc] - br_a[n][:, :, P:])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P + Rc:] - br_b[n][:, :, P:])) <= 1e-13, n
+
+
 # ---------------------------------------------------------------- invariants
 def _rand(Hq=4, Hkv=2, L=37, D=8, seed=5, Lk=None):
     return pins.tiny_inputs(Hq, Hkv, L, D, seed, Lk)
@@ -419,6 +459,8 @@ MUTATIONS = [
     ("d = i + (Lk - Lq) - j", "d = i + (Lq - Lk) - j"),                              # diagonal offset sign
     ("d = i + (Lk - Lq) - j", "d = i - j"),                                          # top-left alignment
     ("nonempty = tot > 0", "nonempty = tot >= 0"),                                   # empty rows -> NaN
+    ("ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))", "ok = ok & ~((i > r0) & (j >= c0) & (j < c1))"),  # cut rows off by one
+    ("ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))", "ok = ok & ~((i >= r0) & (j >= c0) & (j <= c1))"),  # cut keys too wide
     ('out["dSink"] = float(np.sum(P_sink * (0.0 - delta)))', 'out["dSink"] = float(np.sum(P_sink * delta))'),  # sink sign
     ("np.full((len(rows), 1), float(sink))", "np.full((len(rows), 1), 2 * float(sink))"),  # sink logit scaled
     ("ok = np.concatenate([ok, np.ones((len(rows), 1), dtype=bool)], axis=1)",
