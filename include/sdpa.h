@@ -46,8 +46,8 @@
  * Layout and ownership
  * --------------------
  * Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
- * contiguous row-major (the *_strided entry points take any batch / head /
- * row strides instead): Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
+ * contiguous row-major (the *_ex entry points take any batch / head / row
+ * strides instead): Q, O, dO, dQ [B, Hq, Lq, D]; K, V, dK, dV
  * [B, Hq/group, Lk, D]; lse [B, Hq, Lq] float32. Element type: bfloat16
  * (SDPA_BF16), float16 (SDPA_F16) or float32 (SDPA_F32) for Q, K, V, O, dO,
  * dQ, dK, dV; lse is always float32. The 16-bit types run on the matrix
@@ -116,27 +116,52 @@ typedef struct {
   int64_t b, h, l;
 } sdpa_strides;
 
-/* sdpa_fwd_lse for tensors in any strided layout, e.g. [B, L, H, D] projection
- * outputs or views into a fused QKV buffer, and with optional attention
- * sinks. `strides` points to 4 entries, for q, k, v and o in that order
- * (NULL: all contiguous [B, H, L, D]); lse stays contiguous [B, Hq, Lq].
- * `sinks` (NULL: none) is a DEVICE array of Hq float32 logits, one per query
- * head, 16-byte aligned: sink h joins every row's softmax normalizer as one
- * more score with a zero value row, lse_i = log(exp(sinks[h]) + sum_j
- * exp(S_ij)), so it takes probability mass without adding to O (the pages
- * list sinks among the backward's parameters: page "Lab 028 lab detail: Off
- * NVIDIA, you fix the platform yourself", "What I changed, in plain terms",
- * item 2). -INFINITY is no sink; a row with no allowed key gets lse =
- * sinks[h] and O = 0. Each stride must be >= 0 and a multiple of
- * 16 bytes' worth of elements, each row stride at least D and below 2^23;
- * otherwise SDPA_ERR_INVALID_ARG. K and V must have the same row stride (and,
- * in the backward, Q and dO), else SDPA_ERR_UNSUPPORTED: true of [B, L, H, D]
- * tensors of one shape and of views into one fused QKV buffer. Rows of the
- * outputs must not overlap. */
-int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
-                         int32_t dtype, int32_t mask, int32_t window, float scale,
-                         const float* sinks, const sdpa_strides* strides, hipStream_t stream);
+/* Extensions of the *_ex entry points; a NULL extension pointer, or zeroed
+ * fields, mean none of them.
+ *
+ * strides: NULL (every tensor contiguous [B, H, L, D]) or 4 entries for the
+ *   forward (q, k, v, o) / 8 for the backward (q, k, v, o, dO, dq, dk, dv), in
+ *   that order, for tensors in any layout (e.g. [B, L, H, D] projection
+ *   outputs, views into a fused QKV buffer). lse stays contiguous [B, Hq, Lq].
+ *   Each stride must be >= 0 and a multiple of 16 bytes' worth of elements,
+ *   each row stride at least D and below 2^23 (else SDPA_ERR_INVALID_ARG). K
+ *   and V must have the same row stride, and in the backward Q and dO too
+ *   (else SDPA_ERR_UNSUPPORTED): true of [B, L, H, D] tensors of one shape and
+ *   of views into one fused QKV buffer. Output rows must not overlap.
+ * sinks: NULL or a DEVICE array of Hq float32 logits, one per query head,
+ *   16-byte aligned: sink h joins every row's softmax normalizer as one more
+ *   score with a zero value row, lse_i = log(exp(sinks[h]) + sum_j exp(S_ij)),
+ *   so it takes probability mass without adding to O (the pages list sinks
+ *   among the backward's parameters: page "Lab 028 lab detail: Off NVIDIA,
+ *   you fix the platform yourself", "What I changed, in plain terms", item 2).
+ *   -INFINITY is no sink; a row with no allowed key gets lse = sinks[h] and
+ *   O = 0. The backward needs the forward's sinks (and its lse).
+ * dsinks: backward only, set exactly when sinks is: a DEVICE array of Hq
+ *   float32 that receives d sinks[h] = -sum over batches and rows of
+ *   exp(sinks[h] - lse_i) Delta_i, Delta_i = <dO_i, O_i> (fully overwritten,
+ *   reduced in a fixed order); else SDPA_ERR_INVALID_ARG.
+ * cut_row, cut_key_lo, cut_key_hi: a block-sparse cut on top of the mask:
+ *   rows i >= cut_row do not see keys cut_key_lo <= j < cut_key_hi
+ *   (cut_key_lo == cut_key_hi: no cut; else 0 <= cut_row <= Lq and
+ *   0 <= cut_key_lo <= cut_key_hi <= Lk, or SDPA_ERR_INVALID_ARG). With the
+ *   sequence [prompt; chosen; rejected], causal mask, cut_row = cut_key_hi =
+ *   start of rejected and cut_key_lo = start of chosen, this is the
+ *   prefix-sharing mask: the rejected rows never see the chosen tokens, and
+ *   one pass equals the two passes [prompt; chosen] and [prompt; rejected]
+ *   (page "Training - design (ORPO, flash-CCE head, prefix sharing,
+ *   segmented backward)", section 5.4). */
+typedef struct {
+  const sdpa_strides* strides;
+  const float* sinks;
+  float* dsinks;
+  int32_t cut_row, cut_key_lo, cut_key_hi;
+} sdpa_ext;
+
+/* sdpa_fwd_lse with extensions (strided tensors, sinks, block-sparse cut). */
+int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                    int32_t dtype, int32_t mask, int32_t window, float scale,
+                    const sdpa_ext* ext, hipStream_t stream);
 
 /* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
  * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, Lq]),
@@ -158,19 +183,14 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t dtype, int32_t mask, int32_t window, float scale,
              hipStream_t stream);
 
-/* sdpa_bwd for strided tensors and sinks: `strides` points to 8 entries, for
- * q, k, v, o, dO, dq, dk and dv in that order (NULL: all contiguous), with
- * the rules of sdpa_fwd_lse_strided. With `sinks` (the forward's, and lse
- * from that forward), `dsinks` is a DEVICE array of Hq float32 that receives
- * d sinks[h] = -sum over batches and rows of exp(sinks[h] - lse_i) Delta_i,
- * Delta_i = <dO_i, O_i> (fully overwritten; reduced in a fixed order). sinks
- * and dsinks are both NULL or both set (else SDPA_ERR_INVALID_ARG). */
-int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                     const float* lse, void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes,
-                     int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
-                     int32_t dtype, int32_t mask, int32_t window, float scale,
-                     const float* sinks, float* dsinks, const sdpa_strides* strides, hipStream_t stream);
+/* sdpa_bwd with extensions: the same sdpa_ext as the forward (with dsinks
+ * when there are sinks, and the cut and mask the forward used). */
+int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes,
+                int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                int32_t dtype, int32_t mask, int32_t window, float scale,
+                const sdpa_ext* ext, hipStream_t stream);
 
 /* Measurement variant of sdpa_bwd: identical arguments and results, plus two
  * caller-created HIP events. When both are non-null, `main_begin` and
@@ -189,7 +209,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 202. */
+/* ABI version of this header (major * 100 + minor): 300. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

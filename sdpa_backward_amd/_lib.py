@@ -30,7 +30,7 @@ STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", 
 DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
-EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_strided", "sdpa_bwd", "sdpa_bwd_strided", "sdpa_bwd_timed",
+EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed",
            "sdpa_bwd_workspace_bytes", "sdpa_status_string", "sdpa_abi_version")
 
 _lib = None
@@ -39,6 +39,12 @@ _lib = None
 class SdpaStrides(ctypes.Structure):
     """sdpa_strides: element strides of one [B, H, L, D] tensor."""
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64)]
+
+
+class SdpaExt(ctypes.Structure):
+    """sdpa_ext: strides, sinks / d sinks and the block-sparse cut of the *_ex calls."""
+    _fields_ = [("strides", ctypes.POINTER(SdpaStrides)), ("sinks", ctypes.c_void_p), ("dsinks", ctypes.c_void_p),
+                ("cut_row", ctypes.c_int32), ("cut_key_lo", ctypes.c_int32), ("cut_key_hi", ctypes.c_int32)]
 
 
 class SdpaError(RuntimeError):
@@ -57,13 +63,13 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     dims = [i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]  # B Hq group Lq Lk D dtype mask window scale
-    st = ctypes.POINTER(SdpaStrides)
+    ext = ctypes.POINTER(SdpaExt)
     lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + dims + [p]
-    lib.sdpa_fwd_lse_strided.argtypes = [p, p, p, p, p] + dims + [p, st, p]
+    lib.sdpa_fwd_lse_ex.argtypes = [p, p, p, p, p] + dims + [ext, p]
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
-    lib.sdpa_bwd_strided.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, st, p]
+    lib.sdpa_bwd_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [ext, p]
     lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, p]
-    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_strided", "sdpa_bwd", "sdpa_bwd_strided", "sdpa_bwd_timed"):
+    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
@@ -139,6 +145,16 @@ def _sinks_arg(sinks, q, Hq):
     return sinks
 
 
+def _ext(strides, sinks=None, dsinks=None, cut=None):
+    e = SdpaExt()
+    e.strides = strides
+    e.sinks = None if sinks is None else sinks.data_ptr()
+    e.dsinks = None if dsinks is None else dsinks.data_ptr()
+    if cut is not None:
+        e.cut_row, e.cut_key_lo, e.cut_key_hi = (int(x) for x in cut)
+    return ctypes.byref(e), e   # (the struct stays referenced until the call returns)
+
+
 def _mask_args(mask, window):
     if mask not in MASK:
         raise ValueError(f"mask must be one of {tuple(MASK)}")
@@ -156,14 +172,16 @@ def _out_like(t, out):
     return o
 
 
-def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None, sinks=None):
+def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None, sinks=None, cut=None):
     """O [B,Hq,Lq,D] (q.dtype) and lse [B,Hq,Lq] (float32, natural log).
 
     k, v are [B, Hkv, Lk, D]; with Lk != Lq the queries are the last Lq key
     positions. mask: "none", "causal", "causal_window" (window keys up to the
     diagonal) or "window" (window - 1 keys either side of it). sinks: optional
-    float32 [Hq] logits that join every row's softmax normalizer. O takes q's
-    strides when q is dense (e.g. a [B, L, H, D] layout stays one)."""
+    float32 [Hq] logits that join every row's softmax normalizer. cut:
+    optional (r0, c0, c1), rows from r0 on do not see keys [c0, c1) (the
+    prefix-sharing mask). O takes q's strides when q is dense (e.g. a
+    [B, L, H, D] layout stays one)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v)
     sinks = _sinks_arg(sinks, q, Hq)
     k, v = _same_rows(k, v)
@@ -173,10 +191,10 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, L]")
-    st = load().sdpa_fwd_lse_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
-                                     DTYPE[q.dtype], m, w, scale, _ptr(sinks), _strides(q, k, v, o),
-                                     _stream(q.device))
-    _check("sdpa_fwd_lse_strided", st)
+    ext, _keep = _ext(_strides(q, k, v, o), sinks, cut=cut)
+    st = load().sdpa_fwd_lse_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
+                                DTYPE[q.dtype], m, w, scale, ext, _stream(q.device))
+    _check("sdpa_fwd_lse_ex", st)
     return o, lse
 
 
@@ -185,7 +203,7 @@ def workspace_bytes(B, Hq, L, D, dtype):
 
 
 def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None,
-             main_events=None, sinks=None):
+             main_events=None, sinks=None, cut=None):
     """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse);
     with ``sinks`` (the forward's), also d sinks: (dq, dk, dv, dsinks).
 
@@ -213,12 +231,11 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale)
     if main_events is None:
-        strides = _strides(q, k, v, o, do, dq, dk, dv)
-        _check("sdpa_bwd_strided", load().sdpa_bwd_strided(*args, _ptr(sinks), _ptr(dsinks), strides,
-                                                             _stream(q.device)))
+        ext, _keep = _ext(_strides(q, k, v, o, do, dq, dk, dv), sinks, dsinks, cut)
+        _check("sdpa_bwd_ex", load().sdpa_bwd_ex(*args, ext, _stream(q.device)))
     else:
-        if sinks is not None or not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
-            raise ValueError("the timed backward takes contiguous tensors and no sinks")
+        if sinks is not None or cut is not None or not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
+            raise ValueError("the timed backward takes contiguous tensors, no sinks and no cut")
         ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
         _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), ev0, ev1))
     return (dq, dk, dv) if sinks is None else (dq, dk, dv, dsinks)

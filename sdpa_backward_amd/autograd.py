@@ -18,22 +18,24 @@ class SDPAFunction(torch.autograd.Function):
     (and optional per-head sink logits in every row's normalizer)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, mask="causal", window=0, scale=None, sinks=None):
-        o, lse = sdpa_fwd_lse(q, k, v, mask, window, scale, sinks=sinks)
+    def forward(ctx, q, k, v, mask="causal", window=0, scale=None, sinks=None, cut=None):
+        o, lse = sdpa_fwd_lse(q, k, v, mask, window, scale, sinks=sinks, cut=cut)
         ctx.save_for_backward(q, k, v, o, lse, sinks)
-        ctx.cfg = (mask, window, scale)
+        ctx.cfg = (mask, window, scale, cut)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, sinks = ctx.saved_tensors
-        mask, window, scale = ctx.cfg
-        grads = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale, sinks=sinks)
+        mask, window, scale, cut = ctx.cfg
+        grads = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale, sinks=sinks, cut=cut)
         dsinks = grads[3] if sinks is not None else None
-        return grads[0], grads[1], grads[2], None, None, None, dsinks
+        return grads[0], grads[1], grads[2], None, None, None, dsinks, None
 
 
-def attention(q, k, v, mask="causal", window=0, scale=None, sinks=None):
+def attention(q, k, v, mask="causal", window=0, scale=None, sinks=None, cut=None):
     """Differentiable attention over [B, H, L, D] tensors (q: Hq heads, k/v: Hkv heads, Hq % Hkv == 0);
-    sinks: optional float32 [Hq] logits (differentiable)."""
-    return SDPAFunction.apply(q, k, v, mask, window, scale, sinks)
+    sinks: optional float32 [Hq] logits (differentiable); cut: optional (r0, c0, c1), rows from r0 on do
+    not see keys [c0, c1) (prefix sharing: [prompt; chosen; rejected] with r0 = c1 = start of rejected,
+    c0 = start of chosen)."""
+    return SDPAFunction.apply(q, k, v, mask, window, scale, sinks, cut)

@@ -257,10 +257,22 @@ struct AllStrides {
   Strides q, k, v, o, dO, dq, dk, dv;
 };
 
+// Block-sparse cut on top of the mask: rows i >= r0 do not see keys
+// c0 <= j < c1 (c0 == c1: no cut). With [prompt; chosen; rejected] and
+// r0 = c1 = start of rejected, c0 = start of chosen, this is the
+// prefix-sharing mask (page "Training - design (ORPO, flash-CCE head, prefix
+// sharing, segmented backward)", section 5.4). A key's rows stay one range
+// (keys in [c0, c1) just end at row r0 - 1); a row from r0 on loses one key
+// range, tested with a second compare on edge tiles.
+struct Cut {
+  int r0, c0, c1;
+};
+
 // The strides of contiguous [B, H, L, D] tensors. The kernels come in a dense
-// instantiation that uses these (row stride D known at compile time, so tile
-// offsets fold to constants and no stride occupies a register) and a strided
-// one that reads the caller's.
+// instantiation that uses these and no cut (row stride D known at compile
+// time, so tile offsets fold to constants, no stride occupies a register and
+// the cut's tests vanish) and a general one that reads the caller's strides
+// and cut.
 template <int D>
 __host__ __device__ inline AllStrides dense_strides(int Hq, int Hkv, int Lq, int Lk) {
   const Strides q{(long long)Hq * Lq * D, (long long)Lq * D, D}, kv{(long long)Hkv * Lk * D, (long long)Lk * D, D};
@@ -323,7 +335,9 @@ struct TileLoader {
   // src; valid <= 0 gives an empty range (loads read nothing).
   SDPA_DEV __amdgpu_buffer_rsrc_t rsrc(const void* src, int valid) const {
     const int rows = __builtin_amdgcn_readfirstlane(valid < 0 ? 0 : valid < R ? valid : R);  // uniform
-    const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0;
+    uint32_t bytes;
+    if constexpr (DENSE) bytes = rows * D * 2;
+    else bytes = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, bytes, 0x00020000);
   }
   // This wave's block jj of a tile (jj < NJ, and jj * NW + w < PER).
@@ -334,7 +348,13 @@ struct TileLoader {
   }
   // Rows [0, min(valid, R)) of the tile whose row 0 starts at src.
   SDPA_DEV void issue(void* lds, const void* src, int valid, int w) const {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(src, valid);
+    __amdgpu_buffer_rsrc_t rs;
+    if constexpr (DENSE) {  // valid is uniform and positive here
+      const int rows = valid < R ? valid : R;
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * D * 2, 0x00020000);
+    } else {
+      rs = rsrc(src, valid);
+    }
 #pragma unroll
     for (int jj = 0; jj < NJ; jj++) {
       const int j = jj * NW + w;

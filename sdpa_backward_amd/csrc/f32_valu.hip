@@ -16,7 +16,7 @@ template <int D>
 __global__ void __launch_bounds__(128)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                float* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ Sinks, int Hq,
-               int group, int Lq, int Lk, int dlo, int dhi, float scale, AllStrides st) {
+               int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, AllStrides st) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= Lq) return;
@@ -30,8 +30,10 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   // allowed keys of row i: dlo <= j - i <= dhi, 0 <= j < Lk (empty: O = 0, lse = -inf)
   const int jlo = max(0, i + dlo), jhi = min(Lk - 1, i + dhi);
   const float sink = Sinks != nullptr ? Sinks[h] : -INFINITY;  // one more score, with a zero value row
+  const bool cr = i >= cut.r0;  // this row skips the cut's keys
   float m = sink;
   for (int j = jlo; j <= jhi; j++) {
+    if (cr && j >= cut.c0 && j < cut.c1) continue;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
@@ -39,6 +41,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   }
   float l = sink != -INFINITY ? expf(sink - m) : 0.f;
   for (int j = jlo; j <= jhi; j++) {
+    if (cr && j >= cut.c0 && j < cut.c1) continue;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
@@ -49,6 +52,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 #pragma unroll
   for (int d = 0; d < D; d++) acc[d] = 0.f;
   for (int j = jlo; j <= jhi; j++) {
+    if (cr && j >= cut.c0 && j < cut.c1) continue;
     float s = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
@@ -68,7 +72,7 @@ __global__ void __launch_bounds__(128)
 bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                   const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
                   float* __restrict__ dQ, float* __restrict__ Delta, int Hq, int group, int Lq, int Lk,
-                  int dlo, int dhi, float scale, AllStrides st) {
+                  int dlo, int dhi, Cut cut, float scale, AllStrides st) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   if (i >= Lq) return;
@@ -89,7 +93,9 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
     acc[d] = 0.f;
   }
   const float lse = LSE[row];
+  const bool cr = i >= cut.r0;  // this row skips the cut's keys
   for (int j = max(0, i + dlo), jhi = min(Lk - 1, i + dhi); j <= jhi; j++) {
+    if (cr && j >= cut.c0 && j < cut.c1) continue;
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) {
@@ -113,7 +119,7 @@ __global__ void __launch_bounds__(128)
 bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                    const float* __restrict__ dO, const float* __restrict__ LSE,
                    const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV, int Hq,
-                   int group, int Lq, int Lk, int dlo, int dhi, float scale, AllStrides st) {
+                   int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, AllStrides st) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
   if (j >= Lk) return;
@@ -129,7 +135,8 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
     dv[d] = 0.f;
   }
   // rows that see key j: dlo <= j - i <= dhi, 0 <= i < Lq
-  const int ilo = max(0, j - dhi), ihi = min(Lq - 1, j - dlo);
+  const bool kc = j >= cut.c0 && j < cut.c1;  // a cut key is seen only by rows before r0
+  const int ilo = max(0, j - dhi), ihi = min(kc ? cut.r0 - 1 : Lq - 1, j - dlo);
   for (int h = g * group; h < (g + 1) * group; h++) {
     const size_t hrow = ((size_t)b * Hq + h) * Lq;  // lse / Delta row block
     for (int i = ilo; i <= ihi; i++) {
@@ -161,18 +168,18 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
 
 template <int D>
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                          const float* sinks, int group, int Lq, int Lk, int dlo, int dhi, float scale,
+                          const float* sinks, int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale,
                           const AllStrides& st, hipStream_t stream) {
   dim3 grid((Lq + 127) / 128, Hq, B);
   hipLaunchKernelGGL(fwd_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
-                     (const float*)v, (float*)o, lse, sinks, Hq, group, Lq, Lk, dlo, dhi, scale, st);
+                     (const float*)v, (float*)o, lse, sinks, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                          int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
+                          int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   hipError_t e;
@@ -181,7 +188,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     dim3 grid((Lq + 127) / 128, Hq, B);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)o, (const float*)dO, lse, (float*)dq, delta, Hq, group,
-                       Lq, Lk, dlo, dhi, scale, st);
+                       Lq, Lk, dlo, dhi, cut, scale, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -189,7 +196,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     dim3 grid2((Lk + 127) / 128, Hq / group, B);
     hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
                        (const float*)v, (const float*)dO, lse, (const float*)delta, (float*)dk, (float*)dv, Hq,
-                       group, Lq, Lk, dlo, dhi, scale, st);
+                       group, Lq, Lk, dlo, dhi, cut, scale, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -199,11 +206,11 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
 
 #define SDPA_INST_F32(D)                                                                                    \
   template hipError_t launch_fwd_f32<D>(const void*, const void*, const void*, void*, float*, int, int,      \
-                                        const float*, int, int, int, int, int, float, const AllStrides&,    \
-                                        hipStream_t);                                                       \
+                                        const float*, int, int, int, int, int, Cut, float,                  \
+                                        const AllStrides&, hipStream_t);                                    \
   template hipError_t launch_bwd_f32<D>(const void*, const void*, const void*, const void*, const void*,     \
                                         const float*, void*, void*, void*, float*, int, int, int, int, int,  \
-                                        int, int, float, const AllStrides&, hipStream_t, hipEvent_t,         \
+                                        int, int, Cut, float, const AllStrides&, hipStream_t, hipEvent_t,    \
                                         hipEvent_t);
 SDPA_INST_F32(64)
 SDPA_INST_F32(128)

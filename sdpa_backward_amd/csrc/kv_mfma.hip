@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256, 1)
 kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
           E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-          float scale, float scale_log2, AllStrides st_arg) {
+          Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
   using C = KvCfg<D>;
   using ex8 = typename Vec<E>::x8;
   constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
@@ -84,6 +84,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
+  const Cut cut = DENSE ? Cut{0x7fffffff, 0, 0} : cut_arg;  // no cut in the dense instantiation
   const int nkt = (Lk + C::BKT - 1) / C::BKT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
@@ -92,8 +93,10 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
   const E* Kg = K + b * st.k.b + g * st.k.h;
   const E* Vg = V + b * st.v.b + g * st.v.h;
-  // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist)
-  const int ihi = min(Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
+  // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist);
+  // a key inside the cut is seen only by rows before r0
+  const bool kcut = kj >= cut.c0 && kj < cut.c1;
+  const int ihi = min(kcut ? cut.r0 - 1 : Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
   const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
 
   zero_lds(ks, C::BKT * D, tid);
@@ -134,17 +137,26 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // query tiles that can see a key of this workgroup, for each q-head of the group
   // (none: total = 0, and the keys get zero gradients)
   const int klast = min(k0 + C::BKT - 1, Lk - 1);
-  const int rlo = max(0, k0 - dhi), rhi = min(Lq - 1, klast - dlo);
+  const bool all_cut = k0 >= cut.c0 && klast < cut.c1;  // every key of the workgroup inside the cut
+  const int rlo = max(0, k0 - dhi), rhi = min(all_cut ? cut.r0 - 1 : Lq - 1, klast - dlo);
   const int qt_lo = rlo / C::BQ;
   const int nq = rlo <= rhi ? rhi / C::BQ - qt_lo + 1 : 0;
   const int total = group * nq;
   const int kb1 = min(kb0 + 31, Lk - 1);  // this wave's last key (kb1 < kb0: none)
+  const bool wcut = kb0 >= cut.c0 && kb1 < cut.c1;                 // all of the wave's keys inside the cut
+  const int wrhi = wcut ? min(kb1 - dlo, cut.r0 - 1) : kb1 - dlo;  // last row that sees a key of the wave
 
   auto tile_src = [&](int it, const E*& qs, const E*& ds, int& q0) {
     const int hq = g * group + it / nq;
     q0 = (qt_lo + it % nq) * C::BQ;
-    qs = Q + b * st.q.b + hq * st.q.h + (long long)q0 * st.q.l;
-    ds = dO + b * st.dO.b + hq * st.dO.h + (long long)q0 * st.dO.l;
+    if constexpr (DENSE) {  // one offset for both (same layout), as few live scalars as possible
+      const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
+      qs = Q + off;
+      ds = dO + off;
+    } else {
+      qs = Q + b * st.q.b + hq * st.q.h + (long long)q0 * st.q.l;
+      ds = dO + b * st.dO.b + hq * st.dO.h + (long long)q0 * st.dO.l;
+    }
   };
   // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta of them (rows
   // clamped to Lq-1); one 4-byte global->LDS load per lane (wave 0 only)
@@ -233,8 +245,9 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     const int q0 = (qt_lo + it % nq) * C::BQ;
     // some pair of the tile's rows and the wave's keys allowed / every pair allowed
     const int r1 = min(q0 + 31, Lq - 1);
-    const bool active = kb0 <= kb1 && q0 <= kb1 - dlo && r1 >= kb0 - dhi;
-    const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi;
+    const bool active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
+    const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi &&
+                      !(kb0 < cut.c1 && kb1 >= cut.c0 && q0 + 31 >= cut.r0);
 
     __amdgpu_buffer_rsrc_t qrs, drs;
     if constexpr (PF) {
@@ -367,8 +380,9 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     auto tile = [&](int it, E* Qb, E* Db, float* rvc, float* rvn) {
       const int q0 = (qt_lo + it % nq) * C::BQ;
       const int r1 = min(q0 + 31, Lq - 1);
-      const bool active = kb0 <= kb1 && q0 <= kb1 - dlo && r1 >= kb0 - dhi;
-      const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi;
+      const bool active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
+      const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi &&
+                        !(kb0 < cut.c1 && kb1 >= cut.c0 && q0 + 31 >= cut.r0);
       const bool more = it + 1 < total;
       const int itn = more ? it + 1 : it;
       wait_vm_and_barrier<NJ>();  // Q(t) and lse/Delta(t) landed (dO(t) may not have)
@@ -414,17 +428,17 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, float scale, const AllStrides& st, hipStream_t stream) {
+                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
   using C = KvCfg<D>;
   const long nwg = (long)((Lk + C::BKT - 1) / C::BKT) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk);
+  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
   auto run = [&](auto dense_kernel, auto strided_kernel) {
     auto kernel = dense ? dense_kernel : strided_kernel;
     hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
-                       Lq, Lk, dlo, dhi, scale, scale * kLog2e, st);
+                       Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st);
     return hipGetLastError();
   };
   if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
@@ -438,8 +452,8 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
 
 #define SDPA_INST_KV(D, E)                                                                                \
   template hipError_t launch_kv<D, E>(const void*, const void*, const void*, const void*, const float*,    \
-                                      const float*, void*, void*, int, int, int, int, int, int, int, float, \
-                                      const AllStrides&, hipStream_t);
+                                      const float*, void*, void*, int, int, int, int, int, int, int, Cut,   \
+                                      float, const AllStrides&, hipStream_t);
 SDPA_INST_KV(64, bf16)
 SDPA_INST_KV(128, bf16)
 SDPA_INST_KV(256, bf16)

@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256, 1)
 qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ LSE,
           float* __restrict__ Delta, E* __restrict__ Out, const float* __restrict__ Sinks, int Hq, int group,
-          int Lq, int Lk, int dlo, int dhi, float scale, float scale_log2, AllStrides st_arg) {
+          int Lq, int Lk, int dlo, int dhi, Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
   using C = QsCfg<D>;
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
@@ -95,6 +95,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
   la.init(lane);
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hq / group, Lq, Lk) : st_arg;
+  const Cut cut = DENSE ? Cut{0x7fffffff, 0, 0} : cut_arg;  // no cut in the dense instantiation
   // per-lane source offsets of the K and V tile loads (the two share their row
   // stride: the host checks it)
   TileLoader<D, C::BK, C::NW, DENSE> ldk;
@@ -107,8 +108,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
   const int Hkv = Hq / group, g = h / group;
   const size_t hrow = (size_t)b * Hq + h;  // lse / Delta row block
-  const E* Kg = K + b * st.k.b + g * st.k.h;
-  const E* Vg = V + b * st.v.b + g * st.v.h;
+  const E* Kg = DENSE ? K + ((size_t)b * Hkv + g) * Lk * D : K + b * st.k.b + g * st.k.h;
+  const E* Vg = DENSE ? V + ((size_t)b * Hkv + g) * Lk * D : V + b * st.v.b + g * st.v.h;
 
   const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
   const int qi = iw0 + (lane & 31);  // this lane's query row
@@ -116,6 +117,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // this row's keys: [jhi - span + 1, jhi] (span 0: none, or the row does not exist)
   const int jhi = min(Lk - 1, qi + dhi), jlo = max(0, qi + dlo);
   const int span = qok && jhi >= jlo ? jhi - jlo + 1 : 0;
+  // the cut's keys [c0, c1) for rows from r0 on (cspan 0: this row keeps them)
+  const int cspan = qi >= cut.r0 ? cut.c1 - cut.c0 : 0;
 
   // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
   ex8 qreg[NKS];
@@ -192,8 +195,10 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     for (int d = 0; d < NDB; d++) keep_in_agpr(acc[d]);
     const int j0 = kt * BK;
     // some pair of the wave's rows and the tile's keys allowed / every pair allowed
-    const bool active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo;
-    const bool full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk;
+    const bool active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo &&
+                        !(wr0 >= cut.r0 && j0 >= cut.c0 && j0 + BK <= cut.c1);
+    const bool full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk &&
+                      !(wr1 >= cut.r0 && j0 < cut.c1 && j0 + BK > cut.c0);
 
     // Scores of every wave, also of waves whose rows miss this tile (they
     // would only wait at the tile barrier): no branch around the MFMAs.
@@ -233,11 +238,12 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       auto scores = [&](auto masked) {
 #pragma unroll
         for (int mb = 0; mb < NMB; mb++) {
-          const int base = jhi - (j0 + 32 * mb + 4 * hh);
+          const int base = jhi - (j0 + 32 * mb + 4 * hh), cbase = cut.c1 - 1 - (j0 + 32 * mb + 4 * hh);
 #pragma unroll
           for (int i = 0; i < 16; i++) {
+            const int r = 8 * (i >> 2) + (i & 3);
             if constexpr (decltype(masked)::value)
-              st[mb][i] = in_band(base, 8 * (i >> 2) + (i & 3), span) ? st[mb][i] : -INFINITY;
+              st[mb][i] = in_band(base, r, span) && !in_band(cbase, r, cspan) ? st[mb][i] : -INFINITY;
             mx = fmaxf(mx, st[mb][i]);
           }
         }
@@ -282,13 +288,14 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
-        const int base = jhi - (j0 + 32 * mb + 4 * hh);
+        const int base = jhi - (j0 + 32 * mb + 4 * hh), cbase = cut.c1 - 1 - (j0 + 32 * mb + 4 * hh);
         auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, -lse2));
             if constexpr (decltype(masked)::value)
-              p = in_band(base, 8 * (i >> 2) + (i & 3), span) ? p : 0.f;
+              p = in_band(base, 8 * (i >> 2) + (i & 3), span) && !in_band(cbase, 8 * (i >> 2) + (i & 3), cspan)
+                      ? p : 0.f;
             st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
           }
         };
@@ -360,25 +367,25 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk,
-                     int dlo, int dhi, float scale, const AllStrides& st, hipStream_t stream) {
+                     int dlo, int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
   using C = QsCfg<D>;
   const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  auto kernel = is_dense<D>(st, Hq, Hq / group, Lq, Lk) ? qs_kernel<D, MODE, E, true> : qs_kernel<D, MODE, E, false>;
+  auto kernel = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1 ? qs_kernel<D, MODE, E, true> : qs_kernel<D, MODE, E, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
-                     (const E*)o, (const E*)dO, lse, delta, (E*)out, sinks, Hq, group, Lq, Lk, dlo, dhi, scale,
-                     scale * kLog2e, st);
+                     (const E*)o, (const E*)dO, lse, delta, (E*)out, sinks, Hq, group, Lq, Lk, dlo, dhi, cut,
+                     scale, scale * kLog2e, st);
   return hipGetLastError();
 }
 
 #define SDPA_INST_QS(D, E)                                                                                  \
   template hipError_t launch_qs<D, QS_FWD, E>(const void*, const void*, const void*, const void*, const void*, \
                                               float*, float*, void*, const float*, int, int, int, int, int, int, \
-                                              int, float, const AllStrides&, hipStream_t);                     \
+                                              int, Cut, float, const AllStrides&, hipStream_t);                \
   template hipError_t launch_qs<D, QS_DQ, E>(const void*, const void*, const void*, const void*, const void*,  \
                                              float*, float*, void*, const float*, int, int, int, int, int, int,  \
-                                             int, float, const AllStrides&, hipStream_t);
+                                             int, Cut, float, const AllStrides&, hipStream_t);
 SDPA_INST_QS(64, bf16)
 SDPA_INST_QS(128, bf16)
 SDPA_INST_QS(256, bf16)

@@ -19,19 +19,19 @@ enum { QS_FWD = 0, QS_DQ = 1 };
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, float scale, const AllStrides& st, hipStream_t stream);
+                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, float scale, const AllStrides& st, hipStream_t stream);
+                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, const float*, int, int,
-                          int, int, int, float, const AllStrides&, hipStream_t);
+                          int, int, int, Cut, float, const AllStrides&, hipStream_t);
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks, int B, int Hq,
                          int Lq, hipStream_t stream);
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
-                          void*, void*, void*, float*, int, int, int, int, int, int, int, float,
+                          void*, void*, void*, float*, int, int, int, int, int, int, int, Cut, float,
                           const AllStrides&, hipStream_t, hipEvent_t, hipEvent_t);
 
 // 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass; the
@@ -39,14 +39,14 @@ hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, co
 template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                           int group, int Lq, int Lk, int dlo, int dhi, float scale, const AllStrides& st,
+                           int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
                            hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group,
-                                        Lq, Lk, dlo, dhi, scale, st, stream);
+                                        Lq, Lk, dlo, dhi, cut, scale, st, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, scale, st, stream);
+  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -122,6 +122,17 @@ int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH
 
 int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 
+// The block-sparse cut of an extension struct (none: an empty key range).
+int take_cut(const Shape& s, const sdpa_ext* ext, sdpa::Cut& cut) {
+  cut = {s.Lq, 0, 0};
+  if (ext == nullptr || ext->cut_key_lo == ext->cut_key_hi) return SDPA_OK;
+  if (ext->cut_key_lo < 0 || ext->cut_key_lo > ext->cut_key_hi || ext->cut_key_hi > s.Lk || ext->cut_row < 0 ||
+      ext->cut_row > s.Lq)
+    return SDPA_ERR_INVALID_ARG;
+  cut = {ext->cut_row, ext->cut_key_lo, ext->cut_key_hi};
+  return SDPA_OK;
+}
+
 // Strides of a contiguous [B, H, L, D] tensor.
 sdpa::Strides dense(int H, int L, int D) { return {(long long)H * L * D, (long long)L * D, D}; }
 
@@ -162,7 +173,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 202; }
+int sdpa_abi_version(void) { return 300; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -181,10 +192,9 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
   return workspace_for(s);
 }
 
-int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                         int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask,
-                         int32_t window, float scale, const float* sinks, const sdpa_strides* strides,
-                         hipStream_t stream) {
+int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                    int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                    float scale, const sdpa_ext* ext, hipStream_t stream) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -192,15 +202,20 @@ int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, f
   const bool rows = true, keys = !s.no_keys();
   if (!ptr_ok(q, rows) || !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(o, rows) || !ptr_ok(lse, rows))
     return SDPA_ERR_INVALID_ARG;
+  const float* sinks = ext ? ext->sinks : nullptr;
+  if (sinks != nullptr && !aligned16(sinks)) return SDPA_ERR_INVALID_ARG;
   sdpa::AllStrides str;
-  if ((st = take_strides(s, strides, 4, str)) != SDPA_OK) return st;
+  if ((st = take_strides(s, ext ? ext->strides : nullptr, 4, str)) != SDPA_OK) return st;
+  sdpa::Cut cut;
+  if ((st = take_cut(s, ext, cut)) != SDPA_OK) return st;
   int dlo, dhi;
   s.band(dlo, dhi);
   switch (dtype * 1000 + D) {
 #define SDPA_FWD_CASE(DT, E, DD)                                                                          \
   case DT * 1000 + DD:                                                                                    \
     return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, sinks, \
-                                                          B, Hq, group, Lq, Lk, dlo, dhi, scale, str, stream));
+                                                          B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, str,    \
+                                                          stream));
     SDPA_FWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 256)
@@ -212,10 +227,10 @@ int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, f
 #undef SDPA_FWD_CASE
     case SDPA_F32 * 1000 + 64:
       return to_status(
-          sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, scale, str, stream));
+          sdpa::launch_fwd_f32<64>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, cut, scale, str, stream));
     case SDPA_F32 * 1000 + 128:
       return to_status(
-          sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, scale, str, stream));
+          sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, cut, scale, str, stream));
   }
   return SDPA_ERR_UNSUPPORTED;
 }
@@ -223,8 +238,7 @@ int sdpa_fwd_lse_strided(const void* q, const void* k, const void* v, void* o, f
 int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                  int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
                  float scale, hipStream_t stream) {
-  return sdpa_fwd_lse_strided(q, k, v, o, lse, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr,
-                              nullptr, stream);
+  return sdpa_fwd_lse_ex(q, k, v, o, lse, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr, stream);
 }
 
 }  // extern "C"
@@ -234,11 +248,12 @@ namespace {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
-             float scale, const float* sinks, float* dsinks, const sdpa_strides* strides, hipStream_t stream,
-             hipEvent_t main_begin, hipEvent_t main_end) {
+             float scale, const sdpa_ext* ext, hipStream_t stream, hipEvent_t main_begin, hipEvent_t main_end) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
+  const float* sinks = ext ? ext->sinks : nullptr;
+  float* dsinks = ext ? ext->dsinks : nullptr;
   if ((sinks == nullptr) != (dsinks == nullptr)) return SDPA_ERR_INVALID_ARG;
   if (s.B == 0 || s.Hq == 0) return SDPA_OK;
   if (sinks != nullptr && (!aligned16(sinks) || !aligned16(dsinks))) return SDPA_ERR_INVALID_ARG;
@@ -250,7 +265,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
       !ptr_ok(k, keys) || !ptr_ok(v, keys) || !ptr_ok(dk, keys) || !ptr_ok(dv, keys))
     return SDPA_ERR_INVALID_ARG;
   sdpa::AllStrides str;
-  if ((st = take_strides(s, strides, 8, str)) != SDPA_OK) return st;
+  if ((st = take_strides(s, ext ? ext->strides : nullptr, 8, str)) != SDPA_OK) return st;
+  sdpa::Cut cut;
+  if ((st = take_cut(s, ext, cut)) != SDPA_OK) return st;
   const size_t need = workspace_for(s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return SDPA_ERR_WORKSPACE;
@@ -262,7 +279,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 #define SDPA_BWD_CASE(DT, E, DD)                                                                              \
   case DT * 1000 + DD:                                                                                        \
     e = sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi,   \
-                                     scale, str, stream, main_begin, main_end);                               \
+                                     cut, scale, str, stream, main_begin, main_end);                          \
     break;
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)
@@ -274,12 +291,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     SDPA_BWD_CASE(SDPA_F16, f16, 512)
 #undef SDPA_BWD_CASE
     case SDPA_F32 * 1000 + 64:
-      e = sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, scale,
-                                   str, stream, main_begin, main_end);
+      e = sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
+                                   scale, str, stream, main_begin, main_end);
       break;
     case SDPA_F32 * 1000 + 128:
-      e = sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, scale,
-                                    str, stream, main_begin, main_end);
+      e = sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
+                                    scale, str, stream, main_begin, main_end);
       break;
     default:
       return SDPA_ERR_UNSUPPORTED;
@@ -294,13 +311,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 
 extern "C" {
 
-int sdpa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                     int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
-                     int32_t mask, int32_t window, float scale, const float* sinks, float* dsinks,
-                     const sdpa_strides* strides, hipStream_t stream) {
+int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
+                int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                float scale, const sdpa_ext* ext, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, sinks, dsinks, strides, stream, nullptr, nullptr);
+                  mask, window, scale, ext, stream, nullptr, nullptr);
 }
 
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -309,7 +325,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
                    int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
                    hipEvent_t main_end) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, nullptr, nullptr, stream, main_begin, main_end);
+                  mask, window, scale, nullptr, stream, main_begin, main_end);
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -317,7 +333,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
              float scale, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, nullptr, nullptr, stream, nullptr, nullptr);
+                  mask, window, scale, nullptr, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 202
+    assert lib.sdpa_abi_version() == 300
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -190,34 +190,52 @@ def _st(*triples):
     return arr
 
 
-def test_stride_errors(lib):
+def _x(strides=None, sinks=None, dsinks=None, cut=(0, 0, 0)):
+    e = _lib.SdpaExt()
+    e.strides = strides
+    e.sinks, e.dsinks = sinks, dsinks
+    e.cut_row, e.cut_key_lo, e.cut_key_hi = cut
+    return ctypes.byref(e), e
+
+
+def test_extension_errors(lib):
     # q [1, 4, 64, 64], k/v [1, 2, 64, 64]; a dense [B, L, H, D] layout is valid
     # (validated, then rejected here only by a null pointer so nothing launches)
     B, Hq, Hkv, L, D = 1, 4, 2, 64, 64
     blhd_q, blhd_kv = (L * Hq * D, D, Hq * D), (L * Hkv * D, D, Hkv * D)
     p0 = [FAKE] * 5
     p0[0] = 0
-    good = _st(blhd_q, blhd_kv, blhd_kv, blhd_q)
     args = (B, Hq, 2, L, L, D, BF16, CAUSAL, 0, 0.125)
-    assert lib.sdpa_fwd_lse_strided(*[ctypes.c_void_p(x) for x in p0], *args, None, good, None) == INVALID
+    good, _k1 = _x(_st(blhd_q, blhd_kv, blhd_kv, blhd_q))
+    assert lib.sdpa_fwd_lse_ex(*[ctypes.c_void_p(x) for x in p0], *args, good, None) == INVALID
     p = [ctypes.c_void_p(FAKE)] * 5
     for bad in (_st(blhd_q, blhd_kv, blhd_kv, (0, D, D - 8)),          # row stride below D
                 _st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 4)),     # not a 16-byte multiple
                 _st(blhd_q, (-64, D, Hkv * D), blhd_kv, blhd_q),       # negative
                 _st(blhd_q, blhd_kv, blhd_kv, (0, D, 1 << 23))):       # row stride too large
-        assert lib.sdpa_fwd_lse_strided(*p, *args, None, bad, None) == INVALID
+        x, _k = _x(bad)
+        assert lib.sdpa_fwd_lse_ex(*p, *args, x, None) == INVALID
     # K and V with different row strides: not built
-    assert lib.sdpa_fwd_lse_strided(*p, *args, None, _st(blhd_q, blhd_kv, (0, L * D, D), blhd_q), None) == UNSUPPORTED
+    x, _k = _x(_st(blhd_q, blhd_kv, (0, L * D, D), blhd_q))
+    assert lib.sdpa_fwd_lse_ex(*p, *args, x, None) == UNSUPPORTED
     # backward: Q and dO must share their row stride too
     pb = [ctypes.c_void_p(FAKE)] * 9
-    bad8 = _st(blhd_q, blhd_kv, blhd_kv, blhd_q, (0, L * D, D), blhd_q, blhd_kv, blhd_kv)
-    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, None, None, bad8, None) == UNSUPPORTED
+    ws = (ctypes.c_void_p(FAKE), 1 << 40)
+    x, _k = _x(_st(blhd_q, blhd_kv, blhd_kv, blhd_q, (0, L * D, D), blhd_q, blhd_kv, blhd_kv))
+    assert lib.sdpa_bwd_ex(*pb, *ws, *args, x, None) == UNSUPPORTED
     # sinks and their gradient come together
-    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, ctypes.c_void_p(FAKE), None, None,
-                                None) == INVALID
-    assert lib.sdpa_bwd_strided(*pb, ctypes.c_void_p(FAKE), 1 << 40, *args, None, ctypes.c_void_p(FAKE), None,
-                                None) == INVALID
+    for s_, d_ in ((FAKE, None), (None, FAKE)):
+        x, _k = _x(sinks=s_, dsinks=d_)
+        assert lib.sdpa_bwd_ex(*pb, *ws, *args, x, None) == INVALID
+    # misaligned sinks
+    x, _k = _x(sinks=FAKE + 4)
+    assert lib.sdpa_fwd_lse_ex(*[ctypes.c_void_p(v) for v in p0], *args, x, None) == INVALID
+    # a cut outside the rows / keys
+    for cut in ((-1, 0, 5), (10, 5, 3), (10, 0, L + 1), (L + 1, 0, 5), (0, -2, 5)):
+        x, _k = _x(cut=cut)
+        assert lib.sdpa_fwd_lse_ex(*p, *args, x, None) == INVALID, cut
+        assert lib.sdpa_bwd_ex(*pb, *ws, *args, x, None) == INVALID, cut
     # fp32 rows need 16-byte multiples too: 4 elements
     args32 = (B, Hq, 2, L, L, D, F32, CAUSAL, 0, 0.125)
-    assert lib.sdpa_fwd_lse_strided(*p, *args32, None, _st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)),
-                                    None) == INVALID
+    x, _k = _x(_st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)))
+    assert lib.sdpa_fwd_lse_ex(*p, *args32, x, None) == INVALID
