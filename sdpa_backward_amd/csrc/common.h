@@ -25,7 +25,7 @@
 // distinct slots (conflict-free 16-byte reads of one column chunk across rows)
 // and 4 consecutive rows to 4 distinct chunk pairs (transposed reads).
 //
-// Tiles arrive by global_load_lds_dwordx4 (checked on the hardware: the 16
+// Tiles arrive by buffer_load_dwordx4 ... lds (checked on the hardware: the 16
 // bytes a lane fetches land at LDS base + 16 * lane, one 1 KB block per wave
 // instruction), so loads of the next tile run while the current one is used.
 // The two buffers of a double-buffered tile are distinct __shared__ objects

@@ -159,14 +159,22 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
   };
   // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta of them (rows
-  // clamped to Lq-1); one 4-byte global->LDS load per lane (wave 0 only)
+  // clamped to Lq-1); one 4-byte buffer->LDS load per lane (wave 0 only). A
+  // buffer load, not global_load_lds: while one of those is outstanding the
+  // compiler waits for every earlier LDS read (lgkmcnt(0)) before each MFMA,
+  // which undoes the operand look-ahead.
   auto load_rows = [&](int it, float* rv) {
     const int hq = g * group + it / nq;
     const int q0 = (qt_lo + it % nq) * C::BQ;
-    const int row = min(q0 + (lane & 31), Lq - 1);
-    const float* src = (lane < 32 ? LSE : Delta) + ((size_t)b * Hq + hq) * Lq + row;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)rv, 4, 0, 0);
+    const uint32_t off = (uint32_t)min(q0 + (lane & 31), Lq - 1) * 4;
+    const size_t rb = ((size_t)b * Hq + hq) * Lq;
+    auto* dst = (__attribute__((address_space(3))) void*)rv;
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Delta + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
   };
   auto issue = [&](int it, E* qd, E* dd, float* rv) {
     const E *qs, *ds;
