@@ -29,7 +29,12 @@ What is computed, and where the pages define it
   rejected rows never see the chosen tokens (page "Training - design (ORPO,
   flash-CCE head, prefix sharing, segmented backward)", section 5.4); here a
   cut (r0, c0, c1) removes keys [c0, c1) from rows r0 onwards, on top of any
-  mask.
+  mask. The same section cuts its sliding window at logical positions (each
+  response restarts right after the prompt, by its block-wise position
+  reset): with a fourth element ``logical`` true, rows r0 onwards measure
+  their distance to a key before c0 as if the cut keys were not there, i.e.
+  from the key's position plus c1 - c0. With r0 = c1 that makes every
+  rejected row's mask the mask of the pass over [prompt; rejected] alone.
 * Sinks: the backward the pages patch also takes attention sinks as a
   parameter (Lab 028 page, "What I changed", item 2). Reading: one logit per
   query head that joins every row's softmax normalizer as an extra score
@@ -91,6 +96,9 @@ def allowed(i, j, Lq: int, Lk: int, mask: str, window: int, cut=None):
     c0 <= j < c1 (the block-sparse prefix-sharing mask: with the sequence
     [prompt; chosen; rejected], r0 = c1 = start of rejected and c0 = start of
     chosen, so the rejected rows never see the chosen tokens).
+    cut = (r0, c0, c1, logical) with logical true: besides, for rows i >= r0
+    a key j < c0 sits at position j + (c1 - c0) in the distance d above (the
+    cut keys do not count), so a window reaches that far further back.
     """
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
@@ -100,6 +108,9 @@ def allowed(i, j, Lq: int, Lk: int, mask: str, window: int, cut=None):
     j = np.asarray(j, dtype=np.int64)
     ok = (i >= 0) & (i < Lq) & (j >= 0) & (j < Lk)
     d = i + (Lk - Lq) - j
+    if cut is not None and len(cut) > 3 and cut[3]:
+        r0, c0, c1 = cut[:3]
+        d = np.where((i >= r0) & (j < c0), d - (c1 - c0), d)
     if mask == "causal":
         ok = ok & (d >= 0)
     elif mask == "causal_window":
@@ -107,7 +118,7 @@ def allowed(i, j, Lq: int, Lk: int, mask: str, window: int, cut=None):
     elif mask == "window":
         ok = ok & (d > -window) & (d < window)
     if cut is not None:
-        r0, c0, c1 = cut
+        r0, c0, c1 = cut[:3]
         ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))
     return ok
 

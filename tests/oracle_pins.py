@@ -65,14 +65,21 @@ def brute_forward(q, k, v, scale, mask, window, sinks=None, cut=None):
             g = h // group
             for i in range(Lq):
                 pos = i + Lk - Lq
+                # logical cut: a row from cut[0] on and the keys from cut[2] on
+                # move back by the cut's length (the response restarts right
+                # after the prompt); the keys before cut[1] keep their place
+                logical = cut is not None and len(cut) > 3 and cut[3] and i >= cut[0]
+                sh = cut[2] - cut[1] if logical else 0
+                where = (lambda j: j - sh if j >= cut[2] else j) if logical else (lambda j: j)
+                p = pos - sh
                 if mask == "none":
                     keys = list(range(Lk))
                 elif mask == "causal":
-                    keys = [j for j in range(Lk) if j <= pos]
+                    keys = [j for j in range(Lk) if where(j) <= p]
                 elif mask == "causal_window":
-                    keys = [j for j in range(Lk) if pos - window < j <= pos]
+                    keys = [j for j in range(Lk) if p - window < where(j) <= p]
                 else:  # "window": both sides of the diagonal
-                    keys = [j for j in range(Lk) if abs(j - pos) < window]
+                    keys = [j for j in range(Lk) if abs(where(j) - p) < window]
                 if cut is not None and i >= cut[0]:   # rows from cut[0] on skip keys [cut[1], cut[2])
                     keys = [j for j in keys if not cut[1] <= j < cut[2]]
                 sink = None if sinks is None else float(sinks[h])
@@ -119,6 +126,10 @@ BRUTE_CUT_CASES = [
     ((2, 1, 10, 10, 3, 0.8, "causal", 0), (7, 3, 7)),
     ((2, 2, 6, 11, 2, 1.2, "causal_window", 4), (3, 2, 6)),
     ((2, 1, 8, 8, 3, 0.6, "none", 0), (4, 0, 3)),
+    # the window at logical positions: [prompt 3; chosen 4; rejected 4], window 3 and 5
+    ((2, 1, 11, 11, 3, 0.9, "causal_window", 3), (7, 3, 7, True)),
+    ((2, 2, 11, 11, 2, 0.7, "causal_window", 5), (7, 3, 7, True)),
+    ((2, 1, 9, 9, 3, 1.1, "window", 3), (6, 2, 5, True)),
 ]
 # the same kind of cases with sink logits (per head)
 BRUTE_SINK_CASES = [
@@ -231,6 +242,11 @@ def torch_mask(Lq, Lk, mask, window, cut=None):
         raise ValueError(mask)
     if cut is not None:   # a zeroed block: rows cut[0].. against keys cut[1]..cut[2]-1
         ok = ok.clone()
+        if len(cut) > 3 and cut[3]:
+            # logical window: rows cut[0].. see the keys before cut[1] through the
+            # band of a sequence without the cut keys (diagonal cut[2]-cut[1] lower)
+            shifted = torch_mask(Lq, Lk - (cut[2] - cut[1]), mask, window)
+            ok[cut[0]:, :cut[1]] = shifted[cut[0]:, :cut[1]]
         ok[cut[0]:, cut[1]:cut[2]] = False
     return ok
 

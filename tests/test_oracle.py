@@ -246,6 +246,67 @@ def test_prefix_sharing_equals_two_branches(P, Rc, Rr):
         assert np.max(np.abs(sh[n][:, :, P + Rc:] - br_b[n][:, :, P:])) <= 1e-13, n
 
 
+@pytest.mark.parametrize("mask,W,P,Rc,Rr", [("causal_window", 6, 20, 9, 14), ("causal_window", 1, 5, 3, 4),
+                                             ("causal_window", 40, 12, 7, 9), ("causal", 0, 10, 6, 8)])
+def test_logical_window_prefix_sharing_equals_two_branches(mask, W, P, Rc, Rr):
+    # With the window at logical positions, one pass over [prompt; chosen;
+    # rejected] equals the two windowed passes over [prompt; chosen] and
+    # [prompt; rejected] row for row (prompt keys collect both branches'
+    # gradient), for any window: this is what the position reset is for.
+    L = P + Rc + Rr
+    q, k, v, do = pins.tiny_inputs(4, 2, L, 8, 84)
+    sh = oracle.sdpa_fwd_bwd(q, k, v, do, 0.7, mask, W, cut=(P + Rc, P, P + Rc, True))
+    a_idx = np.arange(P + Rc)
+    b_idx = np.concatenate([np.arange(P), np.arange(P + Rc, L)])
+    br_a = oracle.sdpa_fwd_bwd(q[:, :, a_idx], k[:, :, a_idx], v[:, :, a_idx], do[:, :, a_idx], 0.7, mask, W)
+    do_b = do[:, :, b_idx].copy()
+    do_b[:, :, :P] = 0.0
+    br_b = oracle.sdpa_fwd_bwd(q[:, :, b_idx], k[:, :, b_idx], v[:, :, b_idx], do_b, 0.7, mask, W)
+    for n in ("O", "lse", "dQ"):
+        assert np.max(np.abs(sh[n][:, :, :P + Rc] - br_a[n])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P + Rc:] - br_b[n][:, :, P:])) <= 1e-13, n
+    for n in ("dK", "dV"):
+        assert np.max(np.abs(sh[n][:, :, :P] - br_a[n][:, :, :P] - br_b[n][:, :, :P])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P:P + Rc] - br_a[n][:, :, P:])) <= 1e-13, n
+        assert np.max(np.abs(sh[n][:, :, P + Rc:] - br_b[n][:, :, P:])) <= 1e-13, n
+
+
+def test_physical_window_cut_differs_from_the_branches():
+    # the plain cut keeps the window at physical positions: a rejected row
+    # near the start of its block then reaches fewer prompt keys than in its
+    # own branch (the chosen block sits in between), so the two readings differ
+    P, Rc, Rr, W = 20, 9, 14, 12
+    L = P + Rc + Rr
+    q, k, v, _ = pins.tiny_inputs(2, 1, L, 8, 85)
+    phys = oracle.sdpa_forward(q, k, v, 0.7, "causal_window", W, cut=(P + Rc, P, P + Rc))[1]
+    logi = oracle.sdpa_forward(q, k, v, 0.7, "causal_window", W, cut=(P + Rc, P, P + Rc, True))[1]
+    assert np.max(np.abs(phys[:, :, :P + Rc] - logi[:, :, :P + Rc])) == 0.0
+    assert np.max(np.abs(phys[:, :, P + Rc:] - logi[:, :, P + Rc:])) > 1e-3
+
+
+@pytest.mark.parametrize("mask,W", [("causal", 0), ("none", 0)])
+def test_logical_cut_without_window_is_the_plain_cut(mask, W):
+    # without a window the position of a prompt key does not matter to a row
+    # after it (causal) or to any row (no mask): both readings agree exactly
+    q, k, v, do = pins.tiny_inputs(2, 1, 30, 8, 86)
+    a = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, mask, W, cut=(18, 7, 18))
+    b = oracle.sdpa_fwd_bwd(q, k, v, do, 0.8, mask, W, cut=(18, 7, 18, True))
+    for n in ("O", "lse", "dQ", "dK", "dV"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_logical_cut_finite_differences():
+    assert pins.fd_error(sdpa_oracle, 2, 1, 13, 4, 0.9, "causal_window", 3, cut=(8, 3, 8, True)) <= 1e-7
+    assert pins.fd_error(sdpa_oracle, 2, 2, 12, 4, 0.8, "window", 3, cut=(7, 2, 6, True)) <= 1e-7
+
+
+def test_logical_cut_autograd_independent():
+    q, k, v, do = pins.tiny_inputs(4, 2, 260, 32, 87)
+    err = pins.autograd_error(sdpa_oracle, q, k, v, do, 32 ** -0.5, "causal_window", 40,
+                              cut=(180, 90, 180, True))
+    assert err <= 1e-12, err
+
+
 # ---------------------------------------------------------------- invariants
 def _rand(Hq=4, Hkv=2, L=37, D=8, seed=5, Lk=None):
     return pins.tiny_inputs(Hq, Hkv, L, D, seed, Lk)
@@ -461,6 +522,12 @@ MUTATIONS = [
     ("nonempty = tot > 0", "nonempty = tot >= 0"),                                   # empty rows -> NaN
     ("ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))", "ok = ok & ~((i > r0) & (j >= c0) & (j < c1))"),  # cut rows off by one
     ("ok = ok & ~((i >= r0) & (j >= c0) & (j < c1))", "ok = ok & ~((i >= r0) & (j >= c0) & (j <= c1))"),  # cut keys too wide
+    ("d = np.where((i >= r0) & (j < c0), d - (c1 - c0), d)",
+     "d = np.where((i >= r0) & (j < c0), d - (c1 - c0) + 1, d)"),                   # logical shift off by one
+    ("d = np.where((i >= r0) & (j < c0), d - (c1 - c0), d)",
+     "d = np.where((i >= r0) & (j < c0), d + (c1 - c0), d)"),                       # logical shift sign
+    ("d = np.where((i >= r0) & (j < c0), d - (c1 - c0), d)",
+     "d = np.where((i >= r0) & (j >= c1), d - (c1 - c0), d)"),                      # shift on the wrong side
     ('out["dSink"] = float(np.sum(P_sink * (0.0 - delta)))', 'out["dSink"] = float(np.sum(P_sink * delta))'),  # sink sign
     ("np.full((len(rows), 1), float(sink))", "np.full((len(rows), 1), 2 * float(sink))"),  # sink logit scaled
     ("ok = np.concatenate([ok, np.ones((len(rows), 1), dtype=bool)], axis=1)",
