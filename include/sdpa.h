@@ -149,12 +149,20 @@ typedef struct {
  *   prefix-sharing mask: the rejected rows never see the chosen tokens, and
  *   one pass equals the two passes [prompt; chosen] and [prompt; rejected]
  *   (page "Training - design (ORPO, flash-CCE head, prefix sharing,
- *   segmented backward)", section 5.4). */
+ *   segmented backward)", section 5.4).
+ * cut_logical: 0 or 1 (else SDPA_ERR_INVALID_ARG; ignored without a cut).
+ *   1: the mask's distances for rows i >= cut_row count positions without
+ *   the cut keys: a key j < cut_key_lo sits at j + (cut_key_hi - cut_key_lo)
+ *   (the same section's window cut at logical positions, where each
+ *   response restarts right after the prompt). With a window, the prefix-
+ *   sharing pass then equals the two windowed branch passes; without one
+ *   (causal, cut_row >= cut_key_hi) it changes nothing. */
 typedef struct {
   const sdpa_strides* strides;
   const float* sinks;
   float* dsinks;
   int32_t cut_row, cut_key_lo, cut_key_hi;
+  int32_t cut_logical;
 } sdpa_ext;
 
 /* sdpa_fwd_lse with extensions (strided tensors, sinks, block-sparse cut). */
@@ -209,7 +217,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 300. */
+/* ABI version of this header (major * 100 + minor): 301. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

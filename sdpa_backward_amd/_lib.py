@@ -44,7 +44,8 @@ class SdpaStrides(ctypes.Structure):
 class SdpaExt(ctypes.Structure):
     """sdpa_ext: strides, sinks / d sinks and the block-sparse cut of the *_ex calls."""
     _fields_ = [("strides", ctypes.POINTER(SdpaStrides)), ("sinks", ctypes.c_void_p), ("dsinks", ctypes.c_void_p),
-                ("cut_row", ctypes.c_int32), ("cut_key_lo", ctypes.c_int32), ("cut_key_hi", ctypes.c_int32)]
+                ("cut_row", ctypes.c_int32), ("cut_key_lo", ctypes.c_int32), ("cut_key_hi", ctypes.c_int32),
+                ("cut_logical", ctypes.c_int32)]
 
 
 class SdpaError(RuntimeError):
@@ -151,7 +152,10 @@ def _ext(strides, sinks=None, dsinks=None, cut=None):
     e.sinks = None if sinks is None else sinks.data_ptr()
     e.dsinks = None if dsinks is None else dsinks.data_ptr()
     if cut is not None:
-        e.cut_row, e.cut_key_lo, e.cut_key_hi = (int(x) for x in cut)
+        if len(cut) not in (3, 4):
+            raise ValueError("cut is (r0, c0, c1) or (r0, c0, c1, logical)")
+        e.cut_row, e.cut_key_lo, e.cut_key_hi = (int(x) for x in cut[:3])
+        e.cut_logical = int(bool(cut[3])) if len(cut) == 4 else 0
     return ctypes.byref(e), e   # (the struct stays referenced until the call returns)
 
 
@@ -180,7 +184,9 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
     diagonal) or "window" (window - 1 keys either side of it). sinks: optional
     float32 [Hq] logits that join every row's softmax normalizer. cut:
     optional (r0, c0, c1), rows from r0 on do not see keys [c0, c1) (the
-    prefix-sharing mask). O takes q's strides when q is dense (e.g. a
+    prefix-sharing mask), or (r0, c0, c1, True): besides, rows from r0 on
+    place the keys before c0 at their position plus c1 - c0 (the window at
+    logical positions). O takes q's strides when q is dense (e.g. a
     [B, L, H, D] layout stays one)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v)
     sinks = _sinks_arg(sinks, q, Hq)

@@ -37,5 +37,6 @@ def attention(q, k, v, mask="causal", window=0, scale=None, sinks=None, cut=None
     """Differentiable attention over [B, H, L, D] tensors (q: Hq heads, k/v: Hkv heads, Hq % Hkv == 0);
     sinks: optional float32 [Hq] logits (differentiable); cut: optional (r0, c0, c1), rows from r0 on do
     not see keys [c0, c1) (prefix sharing: [prompt; chosen; rejected] with r0 = c1 = start of rejected,
-    c0 = start of chosen)."""
+    c0 = start of chosen); (r0, c0, c1, True) also measures the window of rows from r0 on at logical
+    positions (the cut keys do not count)."""
     return SDPAFunction.apply(q, k, v, mask, window, scale, sinks, cut)

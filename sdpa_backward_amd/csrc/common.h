@@ -261,12 +261,18 @@ struct AllStrides {
 // c0 <= j < c1 (c0 == c1: no cut). With [prompt; chosen; rejected] and
 // r0 = c1 = start of rejected, c0 = start of chosen, this is the
 // prefix-sharing mask (page "Training - design (ORPO, flash-CCE head, prefix
-// sharing, segmented backward)", section 5.4). A key's rows stay one range
-// (keys in [c0, c1) just end at row r0 - 1); a row from r0 on loses one key
-// range, tested with a second compare on edge tiles.
+// sharing, segmented backward)", section 5.4). sh is 0, or c1 - c0 for the
+// window cut at logical positions (same section): rows from r0 on then see a
+// key j < c0 through the band as if it sat at j + sh. So a row from r0 on
+// sees two key ranges, [max(band lo, c1), band hi] and the band moved back by
+// sh, clipped to [0, c0); a key before c0 is seen by two row ranges, rows
+// before r0 through the band and rows from r0 on through the band moved
+// forward by sh (one range when sh = 0).
 struct Cut {
-  int r0, c0, c1;
+  int r0, c0, c1, sh;
 };
+// No cut (the rows that would be cut do not exist).
+constexpr Cut kNoCut = {0x7fffffff, 0, 0, 0};
 
 // The strides of contiguous [B, H, L, D] tensors. The kernels come in a dense
 // instantiation that uses these and no cut (row stride D known at compile

@@ -12,6 +12,20 @@
 
 namespace sdpa {
 
+// Calls f(j) for every key j that row i sees: the band [i + dlo, i + dhi]
+// within [0, Lk), except from the cut row on: the band from c1 on, and the
+// band moved back by the cut's shift, clipped to the keys before c0.
+template <typename F>
+__device__ inline void for_row_keys(int i, int Lk, int dlo, int dhi, const Cut& cut, F&& f) {
+  const int lo = max(0, i + dlo), hi = min(Lk - 1, i + dhi);
+  if (i >= cut.r0 && cut.c0 < cut.c1) {
+    for (int j = max(0, i + dlo - cut.sh), e = min(min(cut.c0 - 1, Lk - 1), i + dhi - cut.sh); j <= e; j++) f(j);
+    for (int j = max(lo, cut.c1); j <= hi; j++) f(j);
+  } else {
+    for (int j = lo; j <= hi; j++) f(j);
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(128)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -27,39 +41,27 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   float qr[D];
 #pragma unroll
   for (int d = 0; d < D; d++) qr[d] = q[d];
-  // allowed keys of row i: dlo <= j - i <= dhi, 0 <= j < Lk (empty: O = 0, lse = -inf)
-  const int jlo = max(0, i + dlo), jhi = min(Lk - 1, i + dhi);
+  // allowed keys of row i (empty: O = 0, lse = -inf)
   const float sink = Sinks != nullptr ? Sinks[h] : -INFINITY;  // one more score, with a zero value row
-  const bool cr = i >= cut.r0;  // this row skips the cut's keys
+  auto score = [&](int j) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
+    return s * scale;
+  };
   float m = sink;
-  for (int j = jlo; j <= jhi; j++) {
-    if (cr && j >= cut.c0 && j < cut.c1) continue;
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
-    m = fmaxf(m, s * scale);
-  }
+  for_row_keys(i, Lk, dlo, dhi, cut, [&](int j) { m = fmaxf(m, score(j)); });
   float l = sink != -INFINITY ? expf(sink - m) : 0.f;
-  for (int j = jlo; j <= jhi; j++) {
-    if (cr && j >= cut.c0 && j < cut.c1) continue;
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
-    l += expf(s * scale - m);
-  }
+  for_row_keys(i, Lk, dlo, dhi, cut, [&](int j) { l += expf(score(j) - m); });
   const float lse = l > 0.f ? m + logf(l) : -INFINITY;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; d++) acc[d] = 0.f;
-  for (int j = jlo; j <= jhi; j++) {
-    if (cr && j >= cut.c0 && j < cut.c1) continue;
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; d++) s = fmaf(qr[d], Kg[(long long)j * st.k.l + d], s);
-    const float p = expf(s * scale - lse);
+  for_row_keys(i, Lk, dlo, dhi, cut, [&](int j) {
+    const float p = expf(score(j) - lse);
 #pragma unroll
     for (int d = 0; d < D; d++) acc[d] = fmaf(p, Vg[(long long)j * st.v.l + d], acc[d]);
-  }
+  });
   float* o = O + b * st.o.b + h * st.o.h + (long long)i * st.o.l;
 #pragma unroll
   for (int d = 0; d < D; d++) o[d] = acc[d];
@@ -93,9 +95,7 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
     acc[d] = 0.f;
   }
   const float lse = LSE[row];
-  const bool cr = i >= cut.r0;  // this row skips the cut's keys
-  for (int j = max(0, i + dlo), jhi = min(Lk - 1, i + dhi); j <= jhi; j++) {
-    if (cr && j >= cut.c0 && j < cut.c1) continue;
+  for_row_keys(i, Lk, dlo, dhi, cut, [&](int j) {
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int d = 0; d < D; d++) {
@@ -106,7 +106,7 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
     const float ds = p * (dp - delta);
 #pragma unroll
     for (int d = 0; d < D; d++) acc[d] = fmaf(ds, Kg[(long long)j * st.k.l + d], acc[d]);
-  }
+  });
   float* dq = dQ + b * st.dq.b + h * st.dq.h + (long long)i * st.dq.l;
 #pragma unroll
   for (int d = 0; d < D; d++) dq[d] = acc[d] * scale;
@@ -134,12 +134,16 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
-  // rows that see key j: dlo <= j - i <= dhi, 0 <= i < Lq
-  const bool kc = j >= cut.c0 && j < cut.c1;  // a cut key is seen only by rows before r0
-  const int ilo = max(0, j - dhi), ihi = min(kc ? cut.r0 - 1 : Lq - 1, j - dlo);
+  // rows that see key j: dlo <= j - i <= dhi, 0 <= i < Lq; a cut key only
+  // rows before r0; with a shift, a key before c0 rows before r0 through the
+  // band and rows from r0 on through the band moved forward by the shift
+  const bool cutk = cut.c0 < cut.c1;
+  const bool kc = cutk && j >= cut.c0 && j < cut.c1, ks = cutk && j < cut.c0 && cut.sh > 0;
+  const int ilo = max(0, j - dhi), ihi = min(kc || ks ? cut.r0 - 1 : Lq - 1, j - dlo);
+  const int ilo2 = ks ? max(cut.r0, j + cut.sh - dhi) : 1, ihi2 = ks ? min(Lq - 1, j + cut.sh - dlo) : 0;
   for (int h = g * group; h < (g + 1) * group; h++) {
     const size_t hrow = ((size_t)b * Hq + h) * Lq;  // lse / Delta row block
-    for (int i = ilo; i <= ihi; i++) {
+    auto add_row = [&](int i) {
       const float* q = Q + b * st.q.b + h * st.q.h + (long long)i * st.q.l;
       const float* dor = dO + b * st.dO.b + h * st.dO.h + (long long)i * st.dO.l;
       float s = 0.f, dp = 0.f;
@@ -155,7 +159,9 @@ bwd_dkv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, con
         dk[d] = fmaf(ds, q[d], dk[d]);
         dv[d] = fmaf(p, dor[d], dv[d]);
       }
-    }
+    };
+    for (int i = ilo; i <= ihi; i++) add_row(i);
+    for (int i = ilo2; i <= ihi2; i++) add_row(i);
   }
   float* dkp = dK + b * st.dk.b + g * st.dk.h + (long long)j * st.dk.l;
   float* dvp = dV + b * st.dv.b + g * st.dv.h + (long long)j * st.dv.l;

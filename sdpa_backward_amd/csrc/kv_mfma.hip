@@ -84,7 +84,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
-  const Cut cut = DENSE ? Cut{0x7fffffff, 0, 0} : cut_arg;  // no cut in the dense instantiation
+  const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
   const int nkt = (Lk + C::BKT - 1) / C::BKT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
@@ -96,8 +96,14 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not exist);
   // a key inside the cut is seen only by rows before r0
   const bool kcut = kj >= cut.c0 && kj < cut.c1;
-  const int ihi = min(kcut ? cut.r0 - 1 : Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
+  // with a shifted cut, a key before c0 is seen by rows before r0 through the
+  // band and by rows from r0 on through the band moved forward by the shift:
+  // a second range [ihi2 - kspan2 + 1, ihi2] (the dense instantiation has no cut)
+  const bool kshift = !DENSE && cut.sh > 0 && kj < cut.c0;
+  const int ihi = min(kcut || kshift ? cut.r0 - 1 : Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
   const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
+  const int ihi2 = kshift ? min(Lq - 1, kj + cut.sh - dlo) : 0, ilo2 = max(cut.r0, kj + cut.sh - dhi);
+  const int kspan2 = kshift && kj < Lk && ihi2 >= ilo2 ? ihi2 - ilo2 + 1 : 0;
 
   zero_lds(ks, C::BKT * D, tid);
   zero_lds(qb0, QT, tid);
@@ -138,17 +144,56 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // (none: total = 0, and the keys get zero gradients)
   const int klast = min(k0 + C::BKT - 1, Lk - 1);
   const bool all_cut = k0 >= cut.c0 && klast < cut.c1;  // every key of the workgroup inside the cut
-  const int rlo = max(0, k0 - dhi), rhi = min(all_cut ? cut.r0 - 1 : Lq - 1, klast - dlo);
-  const int qt_lo = rlo / C::BQ;
-  const int nq = rlo <= rhi ? rhi / C::BQ - qt_lo + 1 : 0;
+  const bool all_shift = !DENSE && cut.sh > 0 && klast < cut.c0;  // every key seen from r0 on only when moved
+  const int rlo = max(0, k0 - dhi), rhi = min(all_cut || all_shift ? cut.r0 - 1 : Lq - 1, klast - dlo);
+  int qt_lo = rlo / C::BQ, nq = rlo <= rhi ? rhi / C::BQ - qt_lo + 1 : 0;
+  // with a shifted cut, the rows from r0 on that see a key before c0 through
+  // the moved band: their tiles come first, or merge with the band's range
+  // when the two touch; q0_of(it) is the first row of the it-th tile
+  int qt2_lo = 0, nq2 = 0;
+  if (!DENSE && cut.sh > 0 && k0 < cut.c0) {
+    const int lo2 = max(cut.r0, k0 + cut.sh - dhi), hi2 = min(Lq - 1, min(klast, cut.c0 - 1) + cut.sh - dlo);
+    if (lo2 <= hi2) {
+      const int a = lo2 / C::BQ, z = hi2 / C::BQ;
+      if (nq == 0) qt_lo = a, nq = z - a + 1;
+      else if (z + 1 >= qt_lo && a <= qt_lo + nq) {
+        const int e = max(qt_lo + nq - 1, z);
+        qt_lo = min(qt_lo, a);
+        nq = e - qt_lo + 1;
+      } else {
+        qt2_lo = a, nq2 = z - a + 1;
+      }
+    }
+  }
+  nq += nq2;
+  auto q0_of = [&](int it) {
+    const int t = it % nq;
+    return (t < nq2 ? qt2_lo + t : qt_lo + (t - nq2)) * C::BQ;
+  };
   const int total = group * nq;
   const int kb1 = min(kb0 + 31, Lk - 1);  // this wave's last key (kb1 < kb0: none)
   const bool wcut = kb0 >= cut.c0 && kb1 < cut.c1;                 // all of the wave's keys inside the cut
   const int wrhi = wcut ? min(kb1 - dlo, cut.r0 - 1) : kb1 - dlo;  // last row that sees a key of the wave
+  // some pair of the tile's rows [q0, q0 + 31] and the wave's keys allowed /
+  // every pair allowed (general instantiation: from the lanes' row ranges,
+  // which never touch)
+  auto tile_tests = [&](int q0, bool& active, bool& full) {
+    if constexpr (DENSE) {
+      const int r1 = min(q0 + 31, Lq - 1);
+      active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
+      full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi;
+    } else {
+      const int q1 = q0 + 31;
+      auto meets = [&](int hi, int sp) { return sp > 0 && hi >= q0 && hi - sp + 1 <= q1; };
+      auto covers = [&](int hi, int sp) { return sp > 0 && hi >= q1 && hi - sp + 1 <= q0; };
+      active = __any(meets(ihi, kspan) || meets(ihi2, kspan2));
+      full = __all(covers(ihi, kspan) || covers(ihi2, kspan2));
+    }
+  };
 
   auto tile_src = [&](int it, const E*& qs, const E*& ds, int& q0) {
     const int hq = g * group + it / nq;
-    q0 = (qt_lo + it % nq) * C::BQ;
+    q0 = q0_of(it);
     if constexpr (DENSE) {  // one offset for both (same layout), as few live scalars as possible
       const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
       qs = Q + off;
@@ -165,7 +210,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // which undoes the operand look-ahead.
   auto load_rows = [&](int it, float* rv) {
     const int hq = g * group + it / nq;
-    const int q0 = (qt_lo + it % nq) * C::BQ;
+    const int q0 = q0_of(it);
     const uint32_t off = (uint32_t)min(q0 + (lane & 31), Lq - 1) * 4;
     const size_t rb = ((size_t)b * Hq + hq) * Lq;
     auto* dst = (__attribute__((address_space(3))) void*)rv;
@@ -193,7 +238,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // tiles, as a select (the wave-uniform test stays outside the element loop)
   // row q0 + c_row(i, hh) is allowed for this lane's key iff it lies in
   // [ihi - kspan + 1, ihi]: ihi - q0 - c_row = base - rr, one unsigned compare
-  const int base = ihi - q0 - 4 * hh;
+  const int base = ihi - q0 - 4 * hh, base2 = ihi2 - q0 - 4 * hh;
   auto form = [&](auto masked) {
 #pragma unroll
     for (int blk = 0; blk < 4; blk++) {
@@ -206,7 +251,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], scale_log2, -lv));
         if constexpr (decltype(masked)::value) {
           const int rr = 8 * blk + r;  // c_row(i, hh) - 4 hh
-          p = in_band(base, rr, kspan) ? p : 0.f;
+          p = in_band(base, rr, kspan) || (!DENSE && in_band(base2, rr, kspan2)) ? p : 0.f;
         }
         s_acc[i] = p;
         if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
@@ -250,12 +295,9 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   auto compute = [&](auto prefetch, int it, const E* Qc, const E* dOc, const float* rv, E* qn,
                      E* dn, float* rvn) {
     constexpr bool PF = decltype(prefetch)::value;
-    const int q0 = (qt_lo + it % nq) * C::BQ;
-    // some pair of the tile's rows and the wave's keys allowed / every pair allowed
-    const int r1 = min(q0 + 31, Lq - 1);
-    const bool active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
-    const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi &&
-                      !(kb0 < cut.c1 && kb1 >= cut.c0 && q0 + 31 >= cut.r0);
+    const int q0 = q0_of(it);
+    bool active, full;
+    tile_tests(q0, active, full);
 
     __amdgpu_buffer_rsrc_t qrs, drs;
     if constexpr (PF) {
@@ -386,11 +428,9 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       }
     };
     auto tile = [&](int it, E* Qb, E* Db, float* rvc, float* rvn) {
-      const int q0 = (qt_lo + it % nq) * C::BQ;
-      const int r1 = min(q0 + 31, Lq - 1);
-      const bool active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
-      const bool full = kb0 + 32 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 31 - q0 <= dhi &&
-                        !(kb0 < cut.c1 && kb1 >= cut.c0 && q0 + 31 >= cut.r0);
+      const int q0 = q0_of(it);
+      bool active, full;
+      tile_tests(q0, active, full);
       const bool more = it + 1 < total;
       const int itn = more ? it + 1 : it;
       wait_vm_and_barrier<NJ>();  // Q(t) and lse/Delta(t) landed (dO(t) may not have)

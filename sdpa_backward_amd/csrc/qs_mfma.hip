@@ -95,7 +95,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
   la.init(lane);
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hq / group, Lq, Lk) : st_arg;
-  const Cut cut = DENSE ? Cut{0x7fffffff, 0, 0} : cut_arg;  // no cut in the dense instantiation
+  const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
   // per-lane source offsets of the K and V tile loads (the two share their row
   // stride: the host checks it)
   TileLoader<D, C::BK, C::NW, DENSE> ldk;
@@ -114,11 +114,19 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int i0 = qt * C::BQ, iw0 = i0 + 32 * qwi;
   const int qi = iw0 + (lane & 31);  // this lane's query row
   const bool qok = qi < Lq;
-  // this row's keys: [jhi - span + 1, jhi] (span 0: none, or the row does not exist)
-  const int jhi = min(Lk - 1, qi + dhi), jlo = max(0, qi + dlo);
+  // this row's keys: [jhi - span + 1, jhi] (span 0: none, or the row does not
+  // exist), and from the cut row on a second range [jhi2 - span2 + 1, jhi2]:
+  // the first is then the band from c1 on, the second the band moved back by
+  // the cut's shift, clipped to the keys before c0 (the dense instantiation
+  // has no cut: span2 = 0)
+  int jhi = min(Lk - 1, qi + dhi), jlo = max(0, qi + dlo), jhi2 = 0, span2 = 0;
+  if (!DENSE && qi >= cut.r0 && cut.c0 < cut.c1) {
+    jlo = max(jlo, cut.c1);
+    jhi2 = min(min(cut.c0 - 1, Lk - 1), qi + dhi - cut.sh);
+    const int jlo2 = max(0, qi + dlo - cut.sh);
+    span2 = qok && jhi2 >= jlo2 ? jhi2 - jlo2 + 1 : 0;
+  }
   const int span = qok && jhi >= jlo ? jhi - jlo + 1 : 0;
-  // the cut's keys [c0, c1) for rows from r0 on (cspan 0: this row keeps them)
-  const int cspan = qi >= cut.r0 ? cut.c1 - cut.c0 : 0;
 
   // this wave's rows as B operands: row qi, d-slots dw0 + 16*s + 8*hh + 0..7
   ex8 qreg[NKS];
@@ -162,13 +170,28 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
   }
 
-  // key tiles that a row of this workgroup can see (none: kt_hi < kt_lo)
+  // key tiles that a row of this workgroup can see: the band's, and with a
+  // shifted cut also the moved band's for the rows from r0 on (merged into
+  // one range when the two touch); kt(t) is the t-th of the nt tiles
   const int i1 = min(i0 + C::BQ - 1, Lq - 1);
   const int klo = max(0, i0 + dlo), khi = min(Lk - 1, i1 + dhi);
-  const int kt_lo = klo / BK, kt_hi = klo <= khi ? khi / BK : kt_lo - 1;
+  int kt_lo = klo / BK, kt_hi = klo <= khi ? khi / BK : kt_lo - 1;
+  int kt2_lo = 0, nt2 = 0;  // the moved band's tiles, visited first
+  if (!DENSE && cut.sh > 0 && cut.c0 < cut.c1 && i1 >= cut.r0) {
+    const int lo2 = max(0, max(i0, cut.r0) + dlo - cut.sh), hi2 = min(min(cut.c0 - 1, Lk - 1), i1 + dhi - cut.sh);
+    if (lo2 <= hi2) {
+      const int a = lo2 / BK, z = hi2 / BK;
+      if (kt_lo > kt_hi) kt_lo = a, kt_hi = z;
+      else if (z + 1 >= kt_lo && a <= kt_hi + 1) kt_lo = min(kt_lo, a), kt_hi = max(kt_hi, z);
+      else kt2_lo = a, nt2 = z - a + 1;
+    }
+  }
+  const int nt = nt2 + max(0, kt_hi - kt_lo + 1);
+  auto kt_of = [&](int t) { return t < nt2 ? kt2_lo + t : kt_lo + (t - nt2); };
   const int wr0 = iw0, wr1 = min(iw0 + 31, Lq - 1);  // this wave's rows (wr1 < wr0: none)
 
-  auto step = [&](int kt, const E* Kc, const E* Vc, E* Kn, E* Vn) {
+  auto step = [&](int t, const E* Kc, const E* Vc, E* Kn, E* Vn) {
+    const int kt = kt_of(t);
     // The next tile's loads (into the other buffers) are issued one at a time
     // between the score MFMAs below: issued back to back they stall the wave
     // until the CU's vector-memory path has taken the workgroup's whole tile.
@@ -176,8 +199,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // (it writes LDS), so the operand reads are software-pipelined by hand and
     // the loads slot in between them. On the last tile the resources cover no
     // rows and the loads read nothing.
-    const bool more = kt + 1 <= kt_hi;
-    const int jn = more ? (kt + 1) * BK : 0;
+    const bool more = t + 1 < nt;
+    const int jn = more ? kt_of(t + 1) * BK : 0;
     const auto krs = ldk.rsrc(Kg + (long long)jn * st.k.l, more ? Lk - jn : 0);
     const auto vrs = ldv.rsrc(Vg + (long long)jn * st.v.l, more ? Lk - jn : 0);
     using LD = decltype(ldk);
@@ -195,10 +218,17 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     for (int d = 0; d < NDB; d++) keep_in_agpr(acc[d]);
     const int j0 = kt * BK;
     // some pair of the wave's rows and the tile's keys allowed / every pair allowed
-    const bool active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo &&
-                        !(wr0 >= cut.r0 && j0 >= cut.c0 && j0 + BK <= cut.c1);
-    const bool full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk &&
-                      !(wr1 >= cut.r0 && j0 < cut.c1 && j0 + BK > cut.c0);
+    bool active, full;
+    if constexpr (DENSE) {
+      active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo;
+      full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk;
+    } else {  // from the lanes' key ranges (the two ranges never touch: c0 < c1)
+      const int j1 = j0 + BK - 1;
+      auto meets = [&](int hi, int sp) { return sp > 0 && hi >= j0 && hi - sp + 1 <= j1; };
+      auto covers = [&](int hi, int sp) { return sp > 0 && hi >= j1 && hi - sp + 1 <= j0; };
+      active = __any(meets(jhi, span) || meets(jhi2, span2));
+      full = __all(covers(jhi, span) || covers(jhi2, span2));
+    }
 
     // Scores of every wave, also of waves whose rows miss this tile (they
     // would only wait at the tile barrier): no branch around the MFMAs.
@@ -238,12 +268,12 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       auto scores = [&](auto masked) {
 #pragma unroll
         for (int mb = 0; mb < NMB; mb++) {
-          const int base = jhi - (j0 + 32 * mb + 4 * hh), cbase = cut.c1 - 1 - (j0 + 32 * mb + 4 * hh);
+          const int base = jhi - (j0 + 32 * mb + 4 * hh), base2 = jhi2 - (j0 + 32 * mb + 4 * hh);
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             const int r = 8 * (i >> 2) + (i & 3);
             if constexpr (decltype(masked)::value)
-              st[mb][i] = in_band(base, r, span) && !in_band(cbase, r, cspan) ? st[mb][i] : -INFINITY;
+              st[mb][i] = in_band(base, r, span) || (!DENSE && in_band(base2, r, span2)) ? st[mb][i] : -INFINITY;
             mx = fmaxf(mx, st[mb][i]);
           }
         }
@@ -288,14 +318,14 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; mb++) {
-        const int base = jhi - (j0 + 32 * mb + 4 * hh), cbase = cut.c1 - 1 - (j0 + 32 * mb + 4 * hh);
+        const int base = jhi - (j0 + 32 * mb + 4 * hh), base2 = jhi2 - (j0 + 32 * mb + 4 * hh);
         auto form = [&](auto masked) {  // dS^T = P^T (dP^T - Delta), masked on edge tiles
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][i], scale_log2, -lse2));
+            const int r = 8 * (i >> 2) + (i & 3);
             if constexpr (decltype(masked)::value)
-              p = in_band(base, 8 * (i >> 2) + (i & 3), span) && !in_band(cbase, 8 * (i >> 2) + (i & 3), cspan)
-                      ? p : 0.f;
+              p = in_band(base, r, span) || (!DENSE && in_band(base2, r, span2)) ? p : 0.f;
             st[NMB + mb][i] = p * (st[NMB + mb][i] - dlt);
           }
         };
@@ -317,8 +347,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
   };
 
-  if (kt_lo <= kt_hi) {  // first tile (uniform over the workgroup)
-    const int j0 = kt_lo * BK;
+  if (nt > 0) {  // first tile (uniform over the workgroup)
+    const int j0 = kt_of(0) * BK;
     zero_lds(kb0, C::TILE, tid);
     zero_lds(kb1, C::TILE, tid);
     zero_lds(vb0, C::TILE, tid);
@@ -328,11 +358,11 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     ldv.issue(vb0, Vg + (long long)j0 * st.v.l, Lk - j0, w);
     wait_all_and_barrier();
   }
-  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-    step(kt, kb0, vb0, kb1, vb1);
+  for (int t = 0; t < nt; t += 2) {
+    step(t, kb0, vb0, kb1, vb1);
     wait_all_and_barrier();
-    if (kt + 1 > kt_hi) break;
-    step(kt + 1, kb1, vb1, kb0, vb0);
+    if (t + 1 >= nt) break;
+    step(t + 1, kb1, vb1, kb0, vb0);
     wait_all_and_barrier();
   }
 

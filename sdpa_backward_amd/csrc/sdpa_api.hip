@@ -124,12 +124,13 @@ int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 
 // The block-sparse cut of an extension struct (none: an empty key range).
 int take_cut(const Shape& s, const sdpa_ext* ext, sdpa::Cut& cut) {
-  cut = {s.Lq, 0, 0};
+  cut = {s.Lq, 0, 0, 0};
   if (ext == nullptr || ext->cut_key_lo == ext->cut_key_hi) return SDPA_OK;
   if (ext->cut_key_lo < 0 || ext->cut_key_lo > ext->cut_key_hi || ext->cut_key_hi > s.Lk || ext->cut_row < 0 ||
-      ext->cut_row > s.Lq)
+      ext->cut_row > s.Lq || (ext->cut_logical != 0 && ext->cut_logical != 1))
     return SDPA_ERR_INVALID_ARG;
-  cut = {ext->cut_row, ext->cut_key_lo, ext->cut_key_hi};
+  const int sh = ext->cut_logical ? ext->cut_key_hi - ext->cut_key_lo : 0;
+  cut = {ext->cut_row, ext->cut_key_lo, ext->cut_key_hi, sh};
   return SDPA_OK;
 }
 
@@ -173,7 +174,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 300; }
+int sdpa_abi_version(void) { return 301; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {

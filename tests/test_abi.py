@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 300
+    assert lib.sdpa_abi_version() == 301
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -190,11 +190,12 @@ def _st(*triples):
     return arr
 
 
-def _x(strides=None, sinks=None, dsinks=None, cut=(0, 0, 0)):
+def _x(strides=None, sinks=None, dsinks=None, cut=(0, 0, 0), logical=0):
     e = _lib.SdpaExt()
     e.strides = strides
     e.sinks, e.dsinks = sinks, dsinks
     e.cut_row, e.cut_key_lo, e.cut_key_hi = cut
+    e.cut_logical = logical
     return ctypes.byref(e), e
 
 
@@ -235,7 +236,35 @@ def test_extension_errors(lib):
         x, _k = _x(cut=cut)
         assert lib.sdpa_fwd_lse_ex(*p, *args, x, None) == INVALID, cut
         assert lib.sdpa_bwd_ex(*pb, *ws, *args, x, None) == INVALID, cut
+    # the logical-position flag is 0 or 1
+    for lg in (2, -1):
+        x, _k = _x(cut=(40, 10, 40), logical=lg)
+        assert lib.sdpa_fwd_lse_ex(*p, *args, x, None) == INVALID, lg
+        assert lib.sdpa_bwd_ex(*pb, *ws, *args, x, None) == INVALID, lg
     # fp32 rows need 16-byte multiples too: 4 elements
     args32 = (B, Hq, 2, L, L, D, F32, CAUSAL, 0, 0.125)
     x, _k = _x(_st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)))
     assert lib.sdpa_fwd_lse_ex(*p, *args32, x, None) == INVALID
+
+
+def test_ext_layout_matches_header(tmp_path):
+    # the ctypes mirror of sdpa_ext against the C compiler's layout of the header
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "sdpa.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(sdpa_ext), offsetof(sdpa_ext, sinks), '
+                   'offsetof(sdpa_ext, dsinks), offsetof(sdpa_ext, cut_row), offsetof(sdpa_ext, cut_logical)); '
+                   'return 0; }\n')
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "layout"
+    r = subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("header does not compile on the host: " + r.stderr[-300:])
+    got = tuple(int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split())
+    E = _lib.SdpaExt
+    assert got == (ctypes.sizeof(E), E.sinks.offset, E.dsinks.offset, E.cut_row.offset, E.cut_logical.offset)

@@ -4,8 +4,11 @@ Rows from r0 on do not see keys [c0, c1), on top of the mask. With
 [prompt; chosen; rejected], a causal mask, r0 = c1 = start of rejected and
 c0 = start of chosen, one pass equals the two passes [prompt; chosen] and
 [prompt; rejected] (page "Training - design (ORPO, flash-CCE head, prefix
-sharing, segmented backward)", section 5.4). Checked against the fp64 oracle
-with the cut, and against the GPU's own two-branch passes.
+sharing, segmented backward)", section 5.4). With the fourth element of the
+cut set, rows from r0 on measure their window at logical positions (the cut
+keys do not count), and the equality holds under a window too. Checked
+against the fp64 oracle with the cut, and against the GPU's own two-branch
+passes.
 """
 import numpy as np
 import pytest
@@ -29,6 +32,16 @@ CASES = [
     ("cut_none_D128", 1, 2, 1, 400, 400, 128, "bf16", MASK_NONE, 0, (200, 0, 64)),
     ("orpo_f16_D256", 1, 2, 1, 600, 600, 256, "f16", MASK_CAUSAL, 0, (450, 200, 450)),
     ("orpo_f32_D64", 1, 2, 1, 120, 120, 64, "f32", MASK_CAUSAL, 0, (90, 40, 90)),
+    # the window at logical positions (rows from r0 see the keys before c0 through the band moved back by c1 - c0)
+    ("logical_w256_D256", 1, 4, 2, 1200, 1200, 256, "bf16", MASK_WINDOW, 256, (800, 300, 800, True)),
+    ("logical_w100_ragged_D128", 1, 2, 1, 1031, 1031, 128, "bf16", MASK_WINDOW, 100, (700, 233, 700, True)),
+    ("logical_w300_merged_D64", 1, 2, 2, 700, 700, 64, "bf16", MASK_WINDOW, 300, (500, 300, 330, True)),
+    ("logical_two_w64_D256", 1, 2, 1, 600, 600, 256, "bf16", MASK_TWO_SIDED, 64, (450, 100, 300, True)),
+    ("logical_w128_D512", 1, 2, 1, 800, 800, 512, "bf16", MASK_WINDOW, 128, (500, 200, 500, True)),
+    ("logical_w64_suffix_D256", 1, 2, 2, 300, 700, 256, "bf16", MASK_WINDOW, 64, (150, 300, 550, True)),
+    ("logical_causal_D256", 1, 2, 1, 640, 640, 256, "bf16", MASK_CAUSAL, 0, (400, 150, 400, True)),
+    ("logical_w90_f16_D256", 1, 2, 1, 650, 650, 256, "f16", MASK_WINDOW, 90, (420, 170, 420, True)),
+    ("logical_w20_f32_D64", 1, 2, 1, 150, 150, 64, "f32", MASK_WINDOW, 20, (100, 40, 100, True)),
 ]
 
 
@@ -82,6 +95,41 @@ def test_shared_prompt_pass_equals_two_branches():
     f = lambda t: t.double().cpu().numpy()
     assert rel_fro(f(o[:, :, P + Rc:]), f(ob[:, :, P:])) <= 1e-2
     assert float((lse[:, :, P + Rc:] - lb[:, :, P:]).abs().max()) <= LSE_TOL
+    assert rel_fro(f(dq[:, :, P + Rc:]), f(gb[0][:, :, P:])) <= 1e-2
+    for n, t in (("dK", dk), ("dV", dv)):
+        i = 1 if n == "dK" else 2
+        assert rel_fro(f(t[:, :, :P]), f(ga[i][:, :, :P].double() + gb[i][:, :, :P].double())) <= 1e-2, n
+        assert rel_fro(f(t[:, :, P:P + Rc]), f(ga[i][:, :, P:])) <= 1e-2, n
+        assert rel_fro(f(t[:, :, P + Rc:]), f(gb[i][:, :, P:])) <= 1e-2, n
+
+
+def test_logical_window_shared_pass_equals_two_branches():
+    # with the window at logical positions the shared pass equals the two
+    # windowed passes [prompt; chosen] and [prompt; rejected] for any window
+    P, Rc, Rr, D, W = 300, 260, 340, 256, 200
+    L = P + Rc + Rr
+    w = Workload("orpo_branches_w", 1, 4, 2, L, D, "bf16", MASK_WINDOW, W, seed=9965)
+    inp = {n: t.to(DEV) for n, t in make_inputs(w).items()}
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    cut = (P + Rc, P, P + Rc, True)
+    o, lse = sdpa_fwd_lse(q, k, v, "causal_window", W, cut=cut)
+    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, "causal_window", W, cut=cut)
+    ia = torch.arange(P + Rc, device=DEV)
+    ib = torch.cat([torch.arange(P, device=DEV), torch.arange(P + Rc, L, device=DEV)])
+    sel = lambda t, idx: t.index_select(2, idx).contiguous()
+    oa, la = sdpa_fwd_lse(sel(q, ia), sel(k, ia), sel(v, ia), "causal_window", W)
+    ga = sdpa_bwd(sel(q, ia), sel(k, ia), sel(v, ia), oa, sel(do, ia), la, "causal_window", W)
+    do_b = sel(do, ib)
+    do_b[:, :, :P] = 0
+    ob, lb = sdpa_fwd_lse(sel(q, ib), sel(k, ib), sel(v, ib), "causal_window", W)
+    gb = sdpa_bwd(sel(q, ib), sel(k, ib), sel(v, ib), ob, do_b, lb, "causal_window", W)
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    assert rel_fro(f(o[:, :, :P + Rc]), f(oa)) <= 1e-2
+    assert rel_fro(f(o[:, :, P + Rc:]), f(ob[:, :, P:])) <= 1e-2
+    assert float((lse[:, :, :P + Rc] - la).abs().max()) <= LSE_TOL
+    assert float((lse[:, :, P + Rc:] - lb[:, :, P:]).abs().max()) <= LSE_TOL
+    assert rel_fro(f(dq[:, :, :P + Rc]), f(ga[0])) <= 1e-2
     assert rel_fro(f(dq[:, :, P + Rc:]), f(gb[0][:, :, P:])) <= 1e-2
     for n, t in (("dK", dk), ("dV", dv)):
         i = 1 if n == "dK" else 2
