@@ -222,7 +222,8 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(1, sdpa.workspace_bytes(w.B, w.Hq, w.L, w.D, q.dtype)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, sdpa.bwd_workspace_bytes(w.B, w.Hq, w.Hq // w.Hkv, w.L, w.Lkv, w.D, q.dtype)),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = HipEvents()
     evs = [[ev.create() for _ in range(5)] for _ in range(a.steps)]

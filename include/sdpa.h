@@ -177,6 +177,20 @@ int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float*
  * invalid arguments. */
 size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, int32_t dtype);
 
+/* Bytes of workspace with which sdpa_bwd / sdpa_bwd_ex may also split the
+ * dK/dV pass of a small problem: the bytes above, plus, for 16-bit inputs
+ * with D <= 256 whose key blocks (128 keys per kv head and batch) number
+ * fewer than 256, fp32 shares of dK and dV (2 * n * B * (Hq/group) * Lk * D
+ * floats, n in {2, 4, 8}) that the query range of each key block is split
+ * over, summed afterwards in a fixed order. The split applies to calls with
+ * contiguous tensors and no cut, and only when the workspace given holds it;
+ * with sdpa_bwd_workspace_bytes(...) bytes the results are the same up to
+ * fp32 summation order. Returns 0 for empty shapes and invalid arguments.
+ * (The split gives small problems enough workgroups for every compute unit;
+ * it is a throughput choice, not part of the pages' method.) */
+size_t sdpa_bwd_workspace_bytes_ex(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                                   int32_t dtype);
+
 /* Backward. Reads q, k, v, o, dO and lse as written by sdpa_fwd_lse for the
  * same arguments; writes dq [B, Hq, Lq, D] and dk, dv [B, Hq/group, Lk, D] in
  * the input dtype, every element fully overwritten (keys no query attends get
@@ -217,7 +231,7 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 301. */
+/* ABI version of this header (major * 100 + minor): 302. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -31,7 +31,7 @@ DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
 EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed",
-           "sdpa_bwd_workspace_bytes", "sdpa_status_string", "sdpa_abi_version")
+           "sdpa_bwd_workspace_bytes", "sdpa_bwd_workspace_bytes_ex", "sdpa_status_string", "sdpa_abi_version")
 
 _lib = None
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
         getattr(lib, f).restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
+    lib.sdpa_bwd_workspace_bytes_ex.argtypes = [i32] * 7
+    lib.sdpa_bwd_workspace_bytes_ex.restype = sz
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
     lib.sdpa_status_string.restype = ctypes.c_char_p
     lib.sdpa_abi_version.argtypes = []
@@ -205,7 +207,13 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
 
 
 def workspace_bytes(B, Hq, L, D, dtype):
+    """Workspace of the backward without the small-problem dK/dV split (the Delta rows)."""
     return int(load().sdpa_bwd_workspace_bytes(B, Hq, L, D, DTYPE[dtype]))
+
+
+def bwd_workspace_bytes(B, Hq, group, Lq, Lk, D, dtype):
+    """Workspace with which the backward may also split a small problem's dK/dV pass."""
+    return int(load().sdpa_bwd_workspace_bytes_ex(B, Hq, group, Lq, Lk, D, DTYPE[dtype]))
 
 
 def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None,
@@ -225,7 +233,7 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
         raise ValueError("lse must be float32 [B, Hq, L]")
     scale = default_scale(D) if scale is None else float(scale)
     m, w = _mask_args(mask, window)
-    need = workspace_bytes(B, Hq, L, D, q.dtype)
+    need = bwd_workspace_bytes(B, Hq, group, L, Lk, D, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:

@@ -59,12 +59,18 @@ SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
   lds_barrier();
 }
 
-template <int D, int PASS, typename E, bool DENSE>
+// SPLIT (dense, one pass): blockIdx also picks one of nseg equal shares of the
+// key block's query tiles, and the workgroup writes fp32 partial dK (scaled)
+// and dV for its keys into Part, share-major: [2][nseg][B][Hkv][Lk][D] (dK
+// shares first); kv_reduce_kernel then sums the shares. Small problems whose
+// key blocks alone would leave CUs idle get more workgroups this way.
+template <int D, int PASS, typename E, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
           E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-          Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
+          Cut cut_arg, float scale, float scale_log2, AllStrides st_arg, float* __restrict__ Part, int nseg) {
+  static_assert(!SPLIT || (DENSE && PASS == 0), "the split runs the dense one-pass kernel");
   using C = KvCfg<D>;
   using ex8 = typename Vec<E>::x8;
   constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
@@ -87,7 +93,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
   const int nkt = (Lk + C::BKT - 1) / C::BKT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
+  const int seg = SPLIT ? logical % nseg : 0, kblk = SPLIT ? logical / nseg : logical;
+  const int kt = kblk % nkt, g = (kblk / nkt) % Hkv, b = kblk / (nkt * Hkv);
   const int k0 = kt * C::BKT;
   const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
@@ -171,6 +178,9 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     return (t < nq2 ? qt2_lo + t : qt_lo + (t - nq2)) * C::BQ;
   };
   const int total = group * nq;
+  // this workgroup's query tiles: [it_b, it_e) of the total (all of them without the split)
+  const int it_b = SPLIT ? (int)((long long)seg * total / nseg) : 0;
+  const int it_e = SPLIT ? (int)((long long)(seg + 1) * total / nseg) : total;
   const int kb1 = min(kb0 + 31, Lk - 1);  // this wave's last key (kb1 < kb0: none)
   const bool wcut = kb0 >= cut.c0 && kb1 < cut.c1;                 // all of the wave's keys inside the cut
   const int wrhi = wcut ? min(kb1 - dlo, cut.r0 - 1) : kb1 - dlo;  // last row that sees a key of the wave
@@ -301,7 +311,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 
     __amdgpu_buffer_rsrc_t qrs, drs;
     if constexpr (PF) {
-      const bool more = it + 1 < total;
+      const bool more = it + 1 < it_e;
       const E *qs, *ds;
       int q0n;
       tile_src(more ? it + 1 : it, qs, ds, q0n);
@@ -359,15 +369,15 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     form_and_update(q0, full, rv, s_acc, dp_acc, Qc, dOc);
   };
 
-  if (total == 0) {
-    // no row sees these keys: zero gradients
+  if (it_b >= it_e) {
+    // no row sees these keys (or no tile falls to this share): zero gradients
   } else if constexpr (C::NBUF == 2) {
-    issue(0, qb0, db0, rv0);
+    issue(it_b, qb0, db0, rv0);
     wait_all_and_barrier();
-    for (int it = 0; it < total; it += 2) {
+    for (int it = it_b; it < it_e; it += 2) {
       compute(std::true_type{}, it, qb0, db0, rv0, qb1, db1, rv1);
       wait_all_and_barrier();
-      if (it + 1 >= total) break;
+      if (it + 1 >= it_e) break;
       compute(std::true_type{}, it + 1, qb1, db1, rv1, qb0, db0, rv0);
       wait_all_and_barrier();
     }
@@ -457,6 +467,24 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
+  if constexpr (SPLIT) {
+    const size_t slice = (size_t)(gridDim.x / nseg / nkt) * Lk * D;  // B * Hkv * Lk * D
+    float* pk = Part + (size_t)seg * slice + ((size_t)b * Hkv + g) * Lk * D;
+    float* pv = pk + (size_t)nseg * slice;
+#pragma unroll
+    for (int d = 0; d < NDB; d++) {
+      const int col = dw0 + 32 * d + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = kb0 + c_row(i, hh);
+        if (key < Lk) {
+          pk[(size_t)key * D + col] = dkacc[d][i] * scale;
+          pv[(size_t)key * D + col] = dvacc[d][i];
+        }
+      }
+    }
+    return;
+  }
   E* dKg = dK + b * st.dk.b + g * st.dk.h;
   E* dVg = dV + b * st.dv.b + g * st.dv.h;
 #pragma unroll
@@ -473,35 +501,78 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
 }
 
+// dK, dV = the sum of the nseg fp32 shares of Part ([2][nseg][n] with n =
+// B * Hkv * Lk * D, contiguous outputs), summed in share order; 8 elements
+// per thread, blockIdx.y = 0 for dK, 1 for dV.
+template <typename E>
+__global__ void __launch_bounds__(256) kv_reduce_kernel(const float* __restrict__ Part, E* __restrict__ dK,
+                                                        E* __restrict__ dV, size_t n, int nseg) {
+  using ex8 = typename Vec<E>::x8;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const float* p = Part + (size_t)blockIdx.y * nseg * n + i;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nseg; s++) {
+    const float4 x = *(const float4*)(p + (size_t)s * n), y = *(const float4*)(p + (size_t)s * n + 4);
+    a[0] += x.x, a[1] += x.y, a[2] += x.z, a[3] += x.w, a[4] += y.x, a[5] += y.y, a[6] += y.z, a[7] += y.w;
+  }
+  ex8 v;
+#pragma unroll
+  for (int j = 0; j < 8; j++) v[j] = (E)a[j];
+  *(ex8*)((blockIdx.y == 0 ? dK : dV) + i) = v;
+}
+
+// Shares of the split for this shape, or 1 (no split): only for the dense
+// one-pass kernel, when the key blocks alone fill fewer than 256 workgroups.
+template <int D>
+int kv_split_shares(int B, int Hq, int group, int Lq, int Lk, bool dense) {
+  if (D > 256 || !dense || Lq == 0) return 1;
+  const long nwg = (long)((Lk + KvCfg<D>::BKT - 1) / KvCfg<D>::BKT) * (Hq / group) * B;
+  int n = 1;
+  while (n < 8 && nwg * n < 256) n *= 2;
+  return n;
+}
+
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
+                     int dhi, Cut cut, float scale, const AllStrides& st, float* part, int nseg,
+                     hipStream_t stream) {
   using C = KvCfg<D>;
   const long nwg = (long)((Lk + C::BKT - 1) / C::BKT) * (Hq / group) * B;
-  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  if (nwg * (nseg > 1 ? nseg : 1) > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
   auto run = [&](auto dense_kernel, auto strided_kernel) {
     auto kernel = dense ? dense_kernel : strided_kernel;
     hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
-                       Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st);
+                       Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st, (float*)nullptr, 1);
     return hipGetLastError();
   };
   if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
-    const hipError_t e = run(kv_kernel<D, KV_DV, E, true>, kv_kernel<D, KV_DV, E, false>);
+    const hipError_t e = run(kv_kernel<D, KV_DV, E, true, false>, kv_kernel<D, KV_DV, E, false, false>);
     if (e != hipSuccess) return e;
-    return run(kv_kernel<D, KV_DK, E, true>, kv_kernel<D, KV_DK, E, false>);
+    return run(kv_kernel<D, KV_DK, E, true, false>, kv_kernel<D, KV_DK, E, false, false>);
   } else {
-    return run(kv_kernel<D, KV_BOTH, E, true>, kv_kernel<D, KV_BOTH, E, false>);
+    if (nseg <= 1 || part == nullptr || !dense)
+      return run(kv_kernel<D, KV_BOTH, E, true, false>, kv_kernel<D, KV_BOTH, E, false, false>);
+    hipLaunchKernelGGL((kv_kernel<D, KV_BOTH, E, true, true>), dim3((unsigned)(nwg * nseg)), dim3(256), 0, stream,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
+                       Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st, part, nseg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)B * (Hq / group) * Lk * D;
+    hipLaunchKernelGGL(kv_reduce_kernel<E>, dim3((unsigned)((n / 8 + 255) / 256), 2), dim3(256), 0, stream,
+                       (const float*)part, (E*)dk, (E*)dv, n, nseg);
+    return hipGetLastError();
   }
 }
 
 #define SDPA_INST_KV(D, E)                                                                                \
   template hipError_t launch_kv<D, E>(const void*, const void*, const void*, const void*, const float*,    \
                                       const float*, void*, void*, int, int, int, int, int, int, int, Cut,   \
-                                      float, const AllStrides&, hipStream_t);
+                                      float, const AllStrides&, float*, int, hipStream_t);
 SDPA_INST_KV(64, bf16)
 SDPA_INST_KV(128, bf16)
 SDPA_INST_KV(256, bf16)
@@ -510,5 +581,9 @@ SDPA_INST_KV(64, f16)
 SDPA_INST_KV(128, f16)
 SDPA_INST_KV(256, f16)
 SDPA_INST_KV(512, f16)
+template int kv_split_shares<64>(int, int, int, int, int, bool);
+template int kv_split_shares<128>(int, int, int, int, int, bool);
+template int kv_split_shares<256>(int, int, int, int, int, bool);
+template int kv_split_shares<512>(int, int, int, int, int, bool);
 
 }  // namespace sdpa

@@ -23,7 +23,10 @@ hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o,
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
+                     int dhi, Cut cut, float scale, const AllStrides& st, float* part, int nseg,
+                     hipStream_t stream);
+template <int D>
+int kv_split_shares(int B, int Hq, int group, int Lq, int Lk, bool dense);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, const float*, int, int,
                           int, int, int, Cut, float, const AllStrides&, hipStream_t);
@@ -34,19 +37,21 @@ hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, co
                           void*, void*, void*, float*, int, int, int, int, int, int, int, Cut, float,
                           const AllStrides&, hipStream_t, hipEvent_t, hipEvent_t);
 
-// 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass; the
-// optional events bracket the dK/dV kernel.
+// 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass (split
+// into nseg shares summed into part when nseg > 1); the optional events
+// bracket the dK/dV pass.
 template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
-                           hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                           float* part, int nseg, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group,
                                         Lq, Lk, dlo, dhi, cut, scale, st, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
+  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part, nseg,
+                      stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
@@ -118,6 +123,22 @@ size_t workspace_for(const Shape& s) {
   return align_up(rows * sizeof(float));  // Delta_i = <dO_i, O_i>, one float per query row
 }
 
+// Shares of the dK/dV split for a 16-bit call (1: none).
+int split_shares(const Shape& s, bool dense) {
+  if (s.dtype == SDPA_F32) return 1;
+  switch (s.D) {
+    case 64: return sdpa::kv_split_shares<64>(s.B, s.Hq, s.group, s.Lq, s.Lk, dense);
+    case 128: return sdpa::kv_split_shares<128>(s.B, s.Hq, s.group, s.Lq, s.Lk, dense);
+    case 256: return sdpa::kv_split_shares<256>(s.B, s.Hq, s.group, s.Lq, s.Lk, dense);
+    default: return 1;
+  }
+}
+
+// Bytes of the split's fp32 dK and dV shares.
+size_t split_bytes(const Shape& s, int nseg) {
+  return nseg > 1 ? align_up(2 * (size_t)nseg * s.B * (s.Hq / s.group) * s.Lk * s.D * sizeof(float)) : 0;
+}
+
 int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
 
 int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
@@ -141,6 +162,13 @@ sdpa::AllStrides dense_all(const Shape& s) {
   const int Hkv = s.Hq / s.group;
   const sdpa::Strides q = dense(s.Hq, s.Lq, s.D), kv = dense(Hkv, s.Lk, s.D);
   return {q, kv, kv, q, q, q, kv, kv};
+}
+
+// Whether every tensor of a call is contiguous.
+bool is_dense_call(const Shape& s, const sdpa::AllStrides& t) {
+  const sdpa::AllStrides d = dense_all(s);
+  return sdpa::same(t.q, d.q) && sdpa::same(t.k, d.k) && sdpa::same(t.v, d.v) && sdpa::same(t.o, d.o) &&
+         sdpa::same(t.dO, d.dO) && sdpa::same(t.dq, d.dq) && sdpa::same(t.dk, d.dk) && sdpa::same(t.dv, d.dv);
 }
 
 // Caller strides (n tensors, in the AllStrides order q, k, v, o, dO, dq, dk, dv),
@@ -174,7 +202,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 301; }
+int sdpa_abi_version(void) { return 302; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -191,6 +219,14 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
   Shape s{B, Hq, 1, Lq, 0, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
   if (check_shape(s) != SDPA_OK) return 0;
   return workspace_for(s);
+}
+
+size_t sdpa_bwd_workspace_bytes_ex(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                                   int32_t dtype) {
+  Shape s{B, Hq, group, Lq, Lk, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
+  if (check_shape(s) != SDPA_OK) return 0;
+  const size_t base = workspace_for(s);
+  return base == 0 || s.no_keys() ? base : base + split_bytes(s, split_shares(s, true));
 }
 
 int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
@@ -273,6 +309,11 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return SDPA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
+  // the dK/dV split of a small dense call, when the workspace holds its shares
+  const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
+  int nseg = split_shares(s, dense);
+  if (nseg > 1 && workspace_bytes < need + split_bytes(s, nseg)) nseg = 1;
+  float* part = nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need) : nullptr;
   int dlo, dhi;
   s.band(dlo, dhi);
   hipError_t e;
@@ -280,7 +321,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 #define SDPA_BWD_CASE(DT, E, DD)                                                                              \
   case DT * 1000 + DD:                                                                                        \
     e = sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi,   \
-                                     cut, scale, str, stream, main_begin, main_end);                          \
+                                     cut, scale, str, part, nseg, stream, main_begin, main_end);              \
     break;
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)

@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 301
+    assert lib.sdpa_abi_version() == 302
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -245,6 +245,27 @@ def test_extension_errors(lib):
     args32 = (B, Hq, 2, L, L, D, F32, CAUSAL, 0, 0.125)
     x, _k = _x(_st(blhd_q, blhd_kv, blhd_kv, (0, D, Hq * D + 2)))
     assert lib.sdpa_fwd_lse_ex(*p, *args32, x, None) == INVALID
+
+
+def test_split_workspace_sizes(lib):
+    ex = lib.sdpa_bwd_workspace_bytes_ex
+    ex.argtypes = [ctypes.c_int32] * 7
+    ex.restype = ctypes.c_size_t
+    delta = lambda B, Hq, Lq: -(-(B * Hq * Lq * 4) // 256) * 256
+    # causal L=2048 D=256 8/4: 16 key blocks x 4 kv heads = 64 workgroups -> 4 shares of fp32 dK, dV
+    assert ex(1, 8, 2, 2048, 2048, 256, BF16) == delta(1, 8, 2048) + 2 * 4 * 4 * 2048 * 256 * 4
+    assert ex(1, 8, 2, 2048, 2048, 256, F16) == ex(1, 8, 2, 2048, 2048, 256, BF16)
+    # 8 blocks: capped at 8 shares; 128 blocks: 2 shares; 256 blocks and more: none
+    assert ex(1, 2, 2, 500, 1000, 64, BF16) == delta(1, 2, 500) + 2 * 8 * 1 * 1000 * 64 * 4
+    assert ex(1, 4, 1, 4096, 4096, 128, BF16) == delta(1, 4, 4096) + 2 * 2 * 1 * 4 * 4096 * 128 * 4
+    assert ex(2, 8, 1, 4096, 4096, 128, BF16) == delta(2, 8, 4096)     # 512 blocks
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16) == lib.sdpa_bwd_workspace_bytes(1, 32, 16384, 256, BF16)
+    # fp32 and D = 512 never split; empty and invalid shapes need nothing
+    assert ex(1, 2, 2, 128, 128, 64, F32) == lib.sdpa_bwd_workspace_bytes(1, 2, 128, 64, F32)
+    assert ex(1, 16, 4, 2048, 2048, 512, BF16) == lib.sdpa_bwd_workspace_bytes(1, 16, 2048, 512, BF16)
+    assert ex(1, 8, 2, 2048, 0, 256, BF16) == delta(1, 8, 2048)
+    assert ex(0, 8, 2, 2048, 2048, 256, BF16) == 0
+    assert ex(1, 8, 3, 2048, 2048, 256, BF16) == 0
 
 
 def test_ext_layout_matches_header(tmp_path):

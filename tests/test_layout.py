@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from sdpa_backward_amd import attention, sdpa_bwd, sdpa_fwd_lse
+from sdpa_backward_amd import attention, sdpa_bwd, sdpa_fwd_lse, workspace_bytes
 from tests.oracle_pins import rel_fro
 from tests.test_parity import DEV, LSE_TOL, TOL, _np, check_full, oracle_full, run
 from workloads import MASK_CAUSAL, MASK_NONE, MASK_TWO_SIDED, MASK_WINDOW, Workload, make_inputs
@@ -72,7 +72,10 @@ def test_strided_equals_contiguous_bitwise(kind, dtype):
     inp = {n: t.to(DEV) for n, t in make_inputs(w).items()}
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window)
-    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window)
+    # strided calls never take the small-problem dK/dV split (its shares are
+    # summed in another order): the contiguous reference runs unsplit too
+    ws = torch.empty(max(1, workspace_bytes(2, 4, 333, D, q.dtype)), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, workspace=ws)
     if kind == "fused":
         qs, ks, vs = _fused_qkv(q, k, v)
     else:

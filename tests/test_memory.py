@@ -5,11 +5,14 @@ tensors, so torch's peak-allocation counter sees every byte. Above the inputs,
 one fwd+bwd holds exactly O, lse, dQ, dK, dV and the workspace (one fp32 row
 statistic per query row); the test checks that sum and that doubling L doubles
 it, for the sliding-window geometry (window 1024) and the causal global one.
+The shapes are large enough (at least 256 key blocks, or D = 512) that the
+small-problem dK/dV split, whose fp32 shares are linear in L too but sized by
+the block count, stays off.
 """
 import pytest
 import torch
 
-from sdpa_backward_amd import sdpa_bwd, sdpa_fwd_lse, workspace_bytes
+from sdpa_backward_amd import bwd_workspace_bytes, sdpa_bwd, sdpa_fwd_lse
 from workloads import MASK_CAUSAL, MASK_WINDOW, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +31,7 @@ def peak_above_inputs(w):
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(DEV) - base
     outs = sum(t.numel() * t.element_size() for t in (o, lse, dq, dk, dv))
-    expect = outs + workspace_bytes(w.B, w.Hq, w.L, w.D, q.dtype)
+    expect = outs + bwd_workspace_bytes(w.B, w.Hq, w.Hq // w.Hkv, w.L, w.Lkv, w.D, q.dtype)
     del inp, q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
     return peak, expect
@@ -37,7 +40,7 @@ def peak_above_inputs(w):
 @pytest.mark.parametrize("geom", ["window1024_D256", "causal_D512"])
 def test_peak_memory_is_linear_in_L(geom):
     if geom == "window1024_D256":
-        make = lambda L: Workload(f"mem_w_{L}", 1, 4, 2, L, 256, "bf16", MASK_WINDOW, 1024, seed=7400)
+        make = lambda L: Workload(f"mem_w_{L}", 1, 16, 8, L, 256, "bf16", MASK_WINDOW, 1024, seed=7400)
         Ls = (4096, 8192, 16384, 32768)
     else:
         make = lambda L: Workload(f"mem_c_{L}", 1, 4, 1, L, 512, "bf16", MASK_CAUSAL, 0, seed=7401)
