@@ -1,0 +1,364 @@
+// Key-stationary dK/dV kernel on v_mfma_f32_16x16x32 (bf16 or fp16 in, fp32
+// accumulate), one pass for both gradients: each wave owns 16 keys, so its
+// dK and dV accumulators (16 keys x D fp32 each) and its K and V rows (as
+// MFMA operands) fit one wave's registers even at D = 512, where a 32-key
+// wave would need two passes and a head-dim split.
+//
+// Same method as kv_mfma.hip (page "Lab 028 lab detail: Off NVIDIA, you fix
+// the platform yourself", section "What I changed, in plain terms", items 3-5:
+// every query tile whose rows see a key of the block, the GQA group summed in
+// registers, every key's dK/dV written; P recomputed from S and the stored
+// lse, dS per element, section "2026-10-21"; S and dP kept in fp32, section
+// "fp32 score tiles").
+//
+// MFMA 16x16x32 lane layouts (checked on the hardware):
+//   A (16x32, M x K): lane l holds row l%16, k-slots for group g = l/16
+//   B (32x16, K x N): lane l holds col l%16, k-slots for group g = l/16
+//   C (16x16 fp32):   lane l holds col l%16, rows 4g + i, i = 0..3
+// Per query tile of 32 rows (row blocks rb = 0, 1), per wave:
+//   S  (32q x 16k) = Q_tile . K_w^T   A: Q (LDS, direct)   B: K_w (registers)
+//   dP (32q x 16k) = dO_tile . V_w^T  A: dO (LDS, direct)  B: V_w (registers)
+//   P = exp2(S c - lse2), dS = P (dP - Delta)
+//   dV_w += P^T . dO                  A: P^T (the two S C tiles)  B: dO (LDS, transposed reads)
+//   dK_w += dS^T . Q                  A: dS^T (the two dP C tiles) B: Q (LDS, transposed reads)
+// A lane's C values of both row blocks (rows 4g + i and 16 + 4g + i) are
+// exactly 8 k-slots of the update's A operand; the B operand reads the same
+// rows from LDS with two transposed 4-row reads per lane group.
+#include "common.h"
+
+namespace sdpa {
+
+SDPA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+SDPA_DEV f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// Per-lane LDS byte offsets of the two 16x16x32 operand read patterns of a
+// swizzled [32][D] tile (lane l, group g = l/16, i = l%16):
+//   dir[j]: direct read, row i, 16-byte chunk 4j + g (k-step t reads dir[t & 3]
+//           + 256 (t >> 2), row block rb adds 16 rows)
+//   trn[j]: transposed read for columns 16j.. (d-block b reads trn[b & 7] +
+//           256 (b >> 3)): row 4g + i/4, column 16j + 4 (i%4); rows + 16 for
+//           the second half of the k-slots
+template <int D>
+struct LaneAddr16 {
+  uint32_t dir[4], trn[8];
+  SDPA_DEV void init(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; j++) dir[j] = i * D * 2 + (Tile<D>::slot(i, 4 * j + g) & 15) * 16;
+    const int r = 4 * g + (i >> 2);
+#pragma unroll
+    for (int j = 0; j < 8; j++) trn[j] = r * D * 2 + (Tile<D>::slot(r, 2 * j + ((i & 3) >> 1)) & 15) * 16 + (i & 1) * 8;
+  }
+};
+
+template <int D, typename E, bool DENSE>
+__global__ void __launch_bounds__(256, 1)
+kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+            const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+            E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
+            Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
+  using ex8 = typename Vec<E>::x8;
+  using ex4 = typename Vec<E>::x4;
+  constexpr int NW = 4, BKT = 16 * NW, BQ = 32, NT = D / 32, NB = D / 16, QT = BQ * D;
+  __shared__ __attribute__((aligned(16))) E qb0[QT];
+  __shared__ __attribute__((aligned(16))) E db0[QT];
+  __shared__ __attribute__((aligned(16))) E qb1[QT];
+  __shared__ __attribute__((aligned(16))) E db1[QT];
+  __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
+  __shared__ __attribute__((aligned(16))) float rv1[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  LaneAddr16<D> la;
+  la.init(lane);
+  const int Hkv = Hq / group;
+  const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
+  const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
+  const int nkt = (Lk + BKT - 1) / BKT;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
+  const int k0 = kt * BKT;
+  const int kb0 = k0 + 16 * w;        // first key of this wave
+  const int kj = kb0 + (lane & 15);   // key held by this lane (C-tile column of S and dP)
+  const E* Kg = K + b * st.k.b + g * st.k.h;
+  const E* Vg = V + b * st.v.b + g * st.v.h;
+  // this key's rows: [ihi - kspan + 1, ihi] (kspan 0: none, or the key does not
+  // exist); a key inside the cut only rows before r0; with a shifted cut, a key
+  // before c0 also rows from r0 on through the band moved forward by the shift
+  const bool kcut = kj >= cut.c0 && kj < cut.c1;
+  const bool kshift = !DENSE && cut.sh > 0 && kj < cut.c0;
+  const int ihi = min(kcut || kshift ? cut.r0 - 1 : Lq - 1, kj - dlo), ilo = max(0, kj - dhi);
+  const int kspan = kj < Lk && ihi >= ilo ? ihi - ilo + 1 : 0;
+  const int ihi2 = kshift ? min(Lq - 1, kj + cut.sh - dlo) : 0, ilo2 = max(cut.r0, kj + cut.sh - dhi);
+  const int kspan2 = kshift && kj < Lk && ihi2 >= ilo2 ? ihi2 - ilo2 + 1 : 0;
+
+  // K_w^T and V_w^T as B operands: lane holds key kj, d-slots 32 t + 8 g + 0..7
+  ex8 kreg[NT], vreg[NT];
+  {
+    const E* krow = Kg + (long long)(kj < Lk ? kj : 0) * st.k.l;
+    const E* vrow = Vg + (long long)(kj < Lk ? kj : 0) * st.v.l;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      kreg[t] = kj < Lk ? *(const ex8*)(krow + 32 * t + 8 * gq) : zero8<E>();
+      vreg[t] = kj < Lk ? *(const ex8*)(vrow + 32 * t + 8 * gq) : zero8<E>();
+    }
+  }
+  f32x4 dkacc[NB], dvacc[NB];
+#pragma unroll
+  for (int d = 0; d < NB; d++) dkacc[d] = dvacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // query tiles that can see a key of this workgroup, for each q-head of the
+  // group; with a shifted cut a second range (rows from r0 on), visited first
+  // or merged when the two touch
+  const int klast = min(k0 + BKT - 1, Lk - 1);
+  const bool all_cut = k0 >= cut.c0 && klast < cut.c1;
+  const bool all_shift = !DENSE && cut.sh > 0 && klast < cut.c0;
+  const int rlo = max(0, k0 - dhi), rhi = min(all_cut || all_shift ? cut.r0 - 1 : Lq - 1, klast - dlo);
+  int qt_lo = rlo / BQ, nq = rlo <= rhi ? rhi / BQ - qt_lo + 1 : 0;
+  int qt2_lo = 0, nq2 = 0;
+  if (!DENSE && cut.sh > 0 && k0 < cut.c0) {
+    const int lo2 = max(cut.r0, k0 + cut.sh - dhi), hi2 = min(Lq - 1, min(klast, cut.c0 - 1) + cut.sh - dlo);
+    if (lo2 <= hi2) {
+      const int a = lo2 / BQ, z = hi2 / BQ;
+      if (nq == 0) qt_lo = a, nq = z - a + 1;
+      else if (z + 1 >= qt_lo && a <= qt_lo + nq) {
+        const int e = max(qt_lo + nq - 1, z);
+        qt_lo = min(qt_lo, a);
+        nq = e - qt_lo + 1;
+      } else {
+        qt2_lo = a, nq2 = z - a + 1;
+      }
+    }
+  }
+  nq += nq2;
+  const int total = group * nq;
+  auto q0_of = [&](int it) {
+    const int t = it % nq;
+    return (t < nq2 ? qt2_lo + t : qt_lo + (t - nq2)) * BQ;
+  };
+  const int kb1 = min(kb0 + 15, Lk - 1);  // this wave's last key (kb1 < kb0: none)
+  const int wrhi = kb1 - dlo;             // last row that sees a key of the wave (dense: no cut)
+  // some pair of the tile's rows [q0, q0 + 31] and the wave's keys allowed / every pair allowed
+  auto tile_tests = [&](int q0, bool& active, bool& full) {
+    if constexpr (DENSE) {
+      const int r1 = min(q0 + 31, Lq - 1);
+      active = kb0 <= kb1 && q0 <= wrhi && r1 >= kb0 - dhi;
+      full = kb0 + 16 <= Lk && q0 + 32 <= Lq && kb0 - q0 - 31 >= dlo && kb0 + 15 - q0 <= dhi;
+    } else {
+      const int q1 = q0 + 31;
+      auto meets = [&](int hi, int sp) { return sp > 0 && hi >= q0 && hi - sp + 1 <= q1; };
+      auto covers = [&](int hi, int sp) { return sp > 0 && hi >= q1 && hi - sp + 1 <= q0; };
+      active = __any(meets(ihi, kspan) || meets(ihi2, kspan2));
+      full = __all(covers(ihi, kspan) || covers(ihi2, kspan2));
+    }
+  };
+
+  TileLoader<D, BQ, NW, DENSE> ldq;  // Q and dO share their row stride (checked by the host)
+  ldq.init(w, lane, st.q.l);
+  using LD = decltype(ldq);
+  auto tile_src = [&](int it, const E*& qs, const E*& ds, int& q0) {
+    const int hq = g * group + it / nq;
+    q0 = q0_of(it);
+    if constexpr (DENSE) {
+      const size_t off = (((size_t)b * Hq + hq) * Lq + q0) * D;
+      qs = Q + off;
+      ds = dO + off;
+    } else {
+      qs = Q + b * st.q.b + hq * st.q.h + (long long)q0 * st.q.l;
+      ds = dO + b * st.dO.b + hq * st.dO.h + (long long)q0 * st.dO.l;
+    }
+  };
+  // lanes 0..31: lse of the tile's rows, lanes 32..63: Delta (rows clamped to
+  // Lq - 1); a buffer->LDS load (wave 0 only), which keeps the compiler's LDS
+  // waits partial (an outstanding global_load_lds makes them full drains)
+  auto load_rows = [&](int it, float* rv) {
+    const int hq = g * group + it / nq;
+    const int q0 = q0_of(it);
+    const uint32_t off = (uint32_t)min(q0 + (lane & 31), Lq - 1) * 4;
+    const size_t rb = ((size_t)b * Hq + hq) * Lq;
+    auto* dst = (__attribute__((address_space(3))) void*)rv;
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Delta + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
+  };
+
+  // direct A operand: rows 16 rb + l%16 of the tile, d-slots 32 t + 8 g + 0..7
+  auto rd_dir = [&](const E* T, int t, int rb) {
+    const char* p = reinterpret_cast<const char*>(T) + la.dir[t & 3] + (t >> 2) * 256 + rb * 16 * D * 2;
+    return *(const ex8*)p;
+  };
+  // transposed B operand: column 16 b + l%16, k-slots = rows 4g + 0..3 then 16 + 4g + 0..3
+  auto rd_trn = [&](const E* T, int blk) {
+    const char* p = reinterpret_cast<const char*>(T) + la.trn[blk & 7] + (blk >> 3) * 256;
+    const ex4 lo = lds_tr4<E>(p), hi = lds_tr4<E>(p + 16 * D * 2);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  // One query tile; the next tile's Q, dO, lse and Delta loads go into
+  // (qn, dn, rvn) one at a time between the score MFMAs (past the last tile
+  // the resources cover no rows).
+  auto compute = [&](int it, const E* Qc, const E* dOc, const float* rv, E* qn, E* dn, float* rvn) {
+    const int q0 = q0_of(it);
+    bool active, full;
+    tile_tests(q0, active, full);
+    __amdgpu_buffer_rsrc_t qrs, drs;
+    {
+      const bool more = it + 1 < total;
+      const E *qs, *ds;
+      int q0n;
+      tile_src(more ? it + 1 : it, qs, ds, q0n);
+      qrs = ldq.rsrc(qs, more ? Lq - q0n : 0);
+      drs = ldq.rsrc(ds, more ? Lq - q0n : 0);
+      if (w == 0) load_rows(more ? it + 1 : it, rvn);
+    }
+    constexpr int NJ = LD::NJ, NLD = 2 * NJ;
+    auto load_one = [&, qrs, drs](int j) {  // j in [0, 2 NJ): Q blocks, then dO blocks
+      if constexpr (LD::PER % NW != 0) {
+        if ((j % NJ) * NW + w >= LD::PER) return;
+      }
+      if (j < NJ) ldq.issue_one(qn, qrs, j, w);
+      else ldq.issue_one(dn, drs, j - NJ, w);
+    };
+
+    // scores: S of both row blocks, then dP of both; every wave, active or not
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+    {
+      constexpr int NM = 2 * NT, AH = 2, EVERY = NM / NLD > 0 ? NM / NLD : 1;
+      ex8 ra[AH], rb[AH];
+      auto rd = [&](int k) {  // step k < NT: S with k-step k; NT + k: dP with k-step k
+        const E* T = k < NT ? Qc : dOc;
+        ra[k % AH] = rd_dir(T, k % NT, 0);
+        rb[k % AH] = rd_dir(T, k % NT, 1);
+      };
+#pragma unroll
+      for (int k = 0; k < AH; k++) rd(k);
+#pragma unroll
+      for (int k = 0; k < NM; k++) {
+        if (k < NT) {
+          s0 = mfma16(ra[k % AH], kreg[k], s0);
+          s1 = mfma16(rb[k % AH], kreg[k], s1);
+        } else {
+          p0 = mfma16(ra[k % AH], vreg[k - NT], p0);
+          p1 = mfma16(rb[k % AH], vreg[k - NT], p1);
+        }
+        if (k + AH < NM) rd(k + AH);
+        if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
+      }
+#pragma unroll
+      for (int j = NM / EVERY; j < NLD; j++) load_one(j);
+    }
+    if (!active) return;
+
+    // P and dS: lane's key kj, rows q0 + 16 rb + 4 g + i; row allowed iff it
+    // lies in [ihi - kspan + 1, ihi] (or the second range)
+    const int base = ihi - q0 - 4 * gq, base2 = ihi2 - q0 - 4 * gq;
+    auto form = [&](auto masked, f32x4& s, f32x4& p, int rb) {
+      const float4 l4 = *(const float4*)(rv + 16 * rb + 4 * gq);
+      const float4 d4 = *(const float4*)(rv + 32 + 16 * rb + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -(&l4.x)[i] * kLog2e));
+        if constexpr (decltype(masked)::value) {
+          const int rr = 16 * rb + i;
+          pr = in_band(base, rr, kspan) || (!DENSE && in_band(base2, rr, kspan2)) ? pr : 0.f;
+        }
+        s[i] = pr;
+        p[i] = pr * (p[i] - (&d4.x)[i]);
+      }
+    };
+    if (full) {
+      form(std::false_type{}, s0, p0, 0);
+      form(std::false_type{}, s1, p1, 1);
+    } else {
+      form(std::true_type{}, s0, p0, 0);
+      form(std::true_type{}, s1, p1, 1);
+    }
+    ex8 pa, da;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      pa[i] = (E)s0[i];
+      pa[4 + i] = (E)s1[i];
+      da[i] = (E)p0[i];
+      da[4 + i] = (E)p1[i];
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; blk++) {
+      dvacc[blk] = mfma16(pa, rd_trn(dOc, blk), dvacc[blk]);
+      dkacc[blk] = mfma16(da, rd_trn(Qc, blk), dkacc[blk]);
+    }
+    // transposed reads one d-block ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int blk = 0; blk < NB; blk++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    }
+  };
+
+  zero_lds(qb0, QT, tid);
+  zero_lds(db0, QT, tid);
+  zero_lds(qb1, QT, tid);
+  zero_lds(db1, QT, tid);
+  lds_barrier();
+  if (total > 0) {
+    {
+      const E *qs, *ds;
+      int q0;
+      tile_src(0, qs, ds, q0);
+      ldq.issue(qb0, qs, Lq - q0, w);
+      ldq.issue(db0, ds, Lq - q0, w);
+      if (w == 0) load_rows(0, rv0);
+    }
+    wait_all_and_barrier();
+    for (int it = 0; it < total; it += 2) {
+      compute(it, qb0, db0, rv0, qb1, db1, rv1);
+      wait_all_and_barrier();
+      if (it + 1 >= total) break;
+      compute(it + 1, qb1, db1, rv1, qb0, db0, rv0);
+      wait_all_and_barrier();
+    }
+  }
+
+  // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index 16 blk + l%16, rows = keys kb0 + 4g + i
+  E* dKg = dK + b * st.dk.b + g * st.dk.h;
+  E* dVg = dV + b * st.dv.b + g * st.dv.h;
+#pragma unroll
+  for (int blk = 0; blk < NB; blk++) {
+    const int col = 16 * blk + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int key = kb0 + 4 * gq + i;
+      if (key < Lk) {
+        dKg[(long long)key * st.dk.l + col] = (E)(dkacc[blk][i] * scale);
+        dVg[(long long)key * st.dv.l + col] = (E)dvacc[blk][i];
+      }
+    }
+  }
+}
+
+template <int D, typename E>
+hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                       const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                       int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
+  const long nwg = (long)((Lk + 63) / 64) * (Hq / group) * B;
+  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+  if (nwg == 0) return hipSuccess;
+  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
+  auto kernel = dense ? kv16_kernel<D, E, true> : kv16_kernel<D, E, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                     (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk, dlo, dhi, cut, scale,
+                     scale * kLog2e, st);
+  return hipGetLastError();
+}
+
+#define SDPA_INST_KV16(D, E)                                                                              \
+  template hipError_t launch_kv16<D, E>(const void*, const void*, const void*, const void*, const float*,  \
+                                        const float*, void*, void*, int, int, int, int, int, int, int, Cut, \
+                                        float, const AllStrides&, hipStream_t);
+SDPA_INST_KV16(512, bf16)
+SDPA_INST_KV16(512, f16)
+
+}  // namespace sdpa

@@ -27,6 +27,10 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
                      hipStream_t stream);
 template <int D>
 int kv_split_shares(int B, int Hq, int group, int Lq, int Lk, bool dense);
+template <int D, typename E>
+hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                       const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                       int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, const float*, int, int,
                           int, int, int, Cut, float, const AllStrides&, hipStream_t);
@@ -50,8 +54,11 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part, nseg,
-                      stream);
+  if constexpr (D == 512)  // one pass with 16-key waves (the 32-key kernel needs two passes here)
+    e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
+  else
+    e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part, nseg,
+                        stream);
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
