@@ -34,8 +34,19 @@ METRIC = "attention fwd+bwd mask-aware TFLOP/s and % of bf16 MFMA peak; peak mem
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public figure (no sparsity)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_window1024_L16384_D256_h32kv16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv_kernel_window1024_L16384_D256.json")
-MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv16_kernel_window1024_L16384_D256.json")
+# the dK/dV kernel of the default workload (dense, D = 256, 4096 key blocks)
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
+
+
+def dkdv_kernel(w):
+    """Name of the dK/dV kernel the library picks for this (dense, 16-bit) workload: 16-key waves at
+    D = 512, and at D = 256 unless the key blocks (128 keys per kv head) number fewer than 256, when
+    32-key waves split each block's query tiles; 32-key waves below D = 256."""
+    blocks = -(-w.Lkv // 128) * w.Hkv * w.B
+    if w.D == 512 or (w.D == 256 and blocks >= 256):
+        return f"kv16_kernel<{w.D}>"
+    return f"kv_kernel<{w.D}>" + (" + share reduce" if blocks < 256 else "")
 
 
 def log(*a):
@@ -301,7 +312,7 @@ def main():
             "fwd_plus_bwd_wall": {"ms": round(ms_per_step, 4)},
         },
         "roofline": {
-            "kernel": f"kv_kernel<{w.D}> (dK/dV pass)",
+            "kernel": f"{dkdv_kernel(w)} (dK/dV pass)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS,

@@ -2,7 +2,9 @@
 // accumulate), one pass for both gradients: each wave owns 16 keys, so its
 // dK and dV accumulators (16 keys x D fp32 each) and its K and V rows (as
 // MFMA operands) fit one wave's registers even at D = 512, where a 32-key
-// wave would need two passes and a head-dim split.
+// wave would need two passes and a head-dim split; at D = 256 they fit 256
+// registers, so two workgroups share a CU. Each of these MFMAs reads one
+// 1 KB operand from LDS, twice the bytes per FLOP of the 32x32x16 kernel.
 //
 // Same method as kv_mfma.hip (page "Lab 028 lab detail: Off NVIDIA, you fix
 // the platform yourself", section "What I changed, in plain terms", items 3-5:
@@ -51,8 +53,10 @@ struct LaneAddr16 {
   }
 };
 
+// D <= 256: two workgroups per CU (two waves per SIMD, at most 256 registers
+// per lane); D = 512: one.
 template <int D, typename E, bool DENSE>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, D <= 256 ? 2 : 1)
 kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
             const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
             E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
@@ -358,6 +362,8 @@ hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* 
   template hipError_t launch_kv16<D, E>(const void*, const void*, const void*, const void*, const float*,  \
                                         const float*, void*, void*, int, int, int, int, int, int, int, Cut, \
                                         float, const AllStrides&, hipStream_t);
+SDPA_INST_KV16(256, bf16)
+SDPA_INST_KV16(256, f16)
 SDPA_INST_KV16(512, bf16)
 SDPA_INST_KV16(512, f16)
 

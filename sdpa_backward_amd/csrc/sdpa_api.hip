@@ -48,13 +48,19 @@ template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
-                           float* part, int nseg, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                           bool wide, float* part, int nseg, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group,
                                         Lq, Lk, dlo, dhi, cut, scale, st, stream);
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  if constexpr (D == 512)  // one pass with 16-key waves (the 32-key kernel needs two passes here)
+  // 16-key waves (v_mfma_f32_16x16x32): at D = 512 always (the 32-key kernel
+  // needs two passes there), at D = 256 for dense calls whose key blocks fill
+  // the GPU (two workgroups per CU; measured faster than the 32-key kernel
+  // there); otherwise 32-key waves. The choice depends on the shape and
+  // layout only, never on the workspace given.
+  const bool k16 = D == 512 || (D == 256 && wide);
+  if (k16)
     e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
   else
     e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part, nseg,
@@ -319,6 +325,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   // the dK/dV split of a small dense call, when the workspace holds its shares
   const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
   int nseg = split_shares(s, dense);
+  const bool wide = dense && nseg == 1;  // dense, and the key blocks alone fill the GPU
   if (nseg > 1 && workspace_bytes < need + split_bytes(s, nseg)) nseg = 1;
   float* part = nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need) : nullptr;
   int dlo, dhi;
@@ -328,7 +335,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 #define SDPA_BWD_CASE(DT, E, DD)                                                                              \
   case DT * 1000 + DD:                                                                                        \
     e = sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi,   \
-                                     cut, scale, str, part, nseg, stream, main_begin, main_end);              \
+                                     cut, scale, str, wide, part, nseg, stream, main_begin, main_end);        \
     break;
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)

@@ -5,7 +5,7 @@ hardware counters, HBM traffic of the dK/dV kernel).
 
 OUTDIR is what collect_profiles.sh wrote: trace/ (kernel trace), p1..p4/
 (counter passes), trace.log (the bench JSON line of the traced run). Writes
-kernel_stats_<tag>.md, counters_<tag>.md and traffic_kv_kernel_<tag>.json into
+kernel_stats_<tag>.md, counters_<tag>.md and traffic_<dK/dV kernel>_<tag>.json into
 OUTDIR; <tag> names the workload by its mask and sizes.
 """
 from __future__ import annotations
@@ -24,7 +24,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
+MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
 COPY_KERNEL = "copyBuffer"   # the 1 GiB device copy bench.py --copy-probe runs
 COPY_BYTES = 1 << 30
 
@@ -48,6 +48,8 @@ def short(name: str) -> str:
     name = name.replace("void ", "")
     name = re.sub(r"\(.*", "", name)
     name = re.sub(r"<(\d+), (\d+), [^<>]+>", r"<\1, \2>", name)  # the workloads here are bf16
+    name = re.sub(r"^(sdpa::kv16_kernel)<(\d+), [^<>]+>", r"\1<\2>", name)
+    name = re.sub(r"^(sdpa::kv_reduce_kernel)<[^<>]+>", r"\1", name)
     return name
 
 
@@ -63,9 +65,8 @@ def roles(w):
     return {
         f"sdpa::qs_kernel<{D}, 0>": ("forward (O, lse)", 4 * D * N, q + 2 * kv, q + row),
         f"sdpa::qs_kernel<{D}, 1>": ("dQ pass (+Delta)", 6 * D * N, 3 * q + 2 * kv + row, q + row),
-        f"sdpa::kv_kernel<{D}, 0>": ("dK/dV pass", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
-        f"sdpa::kv_kernel<{D}, 1>": ("dV pass (D=512)", 4 * D * N, q + 2 * kv + 2 * row, kv),
-        f"sdpa::kv_kernel<{D}, 2>": ("dK pass (D=512)", 6 * D * N, 2 * q + 2 * kv + 2 * row, kv),
+        f"sdpa::kv_kernel<{D}, 0>": ("dK/dV pass (32-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
+        f"sdpa::kv16_kernel<{D}>": ("dK/dV pass (16-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
     }
 
 
@@ -137,7 +138,7 @@ def main():
         timed[k] = ta
         lines.append(f"| `{k}` | {role} | {len(v)} | {statistics.mean(v):.1f} | {ta:.1f} | {min(v):.1f} | "
                      f"{flop:.4e} | {flop / ta / 1e6:.1f} |")
-    main_k = f"sdpa::kv_kernel<{w.D}, 0>"
+    main_k = next((k for k in (f"sdpa::kv16_kernel<{w.D}>", f"sdpa::kv_kernel<{w.D}, 0>") if k in timed), None)
     if bl and main_k in timed:
         ev = bl["roofline"]["avg_launch_ms"] * 1e3
         lines += ["", f"In-bench HIP events around `{main_k}` in the same run (mean over the timed steps): "
@@ -183,7 +184,7 @@ def main():
         lines.append(f"| `{k}` | {100 * busy:.1f} % | {valu:.2f} | {bank:.3f} | {rd / 1e9:.3f} GB | {ar / 1e9:.3f} GB "
                      f"| {wr / 1e9:.3f} GB | {aw / 1e9:.3f} GB |")
         if k == main_k:
-            traffic = {"kernel": f"kv_kernel<{w.D}, 0> (dK/dV pass)", "workload": w.name,
+            traffic = {"kernel": f"{main_k[len('sdpa::'):]} (dK/dV pass)", "workload": w.name,
                        "sources_sha256": sources_sha256(),
                        "fetch_kib_per_launch": mean_of(3, k, "FETCH_SIZE"),
                        "write_kib_per_launch": mean_of(4, k, "WRITE_SIZE"),
@@ -195,7 +196,8 @@ def main():
               "output written once (bf16 tensors, fp32 lse / Delta rows)."]
     open(os.path.join(out, f"counters_{t}.md"), "w").write("\n".join(lines) + "\n")
     if traffic:
-        json.dump(traffic, open(os.path.join(out, f"traffic_kv_kernel_{t}.json"), "w"), indent=1)
+        name = "kv16_kernel" if "kv16" in traffic["kernel"] else "kv_kernel"
+        json.dump(traffic, open(os.path.join(out, f"traffic_{name}_{t}.json"), "w"), indent=1)
     print(f"wrote summaries for {t} into {out}")
 
 

@@ -1,0 +1,49 @@
+"""The 16-key dK/dV kernel at D = 256 on the GPU (run on an MI355X).
+
+Dense 16-bit calls at D = 256 whose key blocks (128 keys per kv head and
+batch) number at least 256 run their dK/dV pass with 16-key waves on
+v_mfma_f32_16x16x32 (D = 512 always does; its cases live in the other
+files). Checked against the fp64 oracle, and against the 32-key kernel,
+which a strided copy of the same tensors takes.
+"""
+import pytest
+import torch
+
+import oracle
+from sdpa_backward_amd import sdpa_bwd, sdpa_fwd_lse
+from tests.oracle_pins import rel_fro
+from tests.test_parity import DEV, TOL, _np
+from workloads import MASK_CAUSAL, MASK_TWO_SIDED, MASK_WINDOW, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, Hq, Hkv, Lq, Lk, D, dtype, mask, window   (key blocks: ceil(Lk / 128) * Hkv * B >= 256)
+    ("mha64_causal_L512", 1, 64, 64, 512, 512, 256, "bf16", MASK_CAUSAL, 0),
+    ("gqa2_w100_ragged_L1000", 1, 64, 32, 1000, 1000, 256, "bf16", MASK_WINDOW, 100),
+    ("B2_two_sided_suffix", 2, 32, 16, 300, 1000, 256, "f16", MASK_TWO_SIDED, 77),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_kv16_d256(case):
+    name, B, Hq, Hkv, Lq, Lk, D, dtype, mask, window = case
+    assert -(-Lk // 128) * Hkv * B >= 256
+    w = Workload(name, B, Hq, Hkv, Lq, D, dtype, mask, window, seed=9850 + Lq, Lk=Lk)
+    inp = make_inputs(w)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale)
+    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale)
+    # the same values in a [B, L, H, D] layout: the strided instantiation, 32-key waves
+    blhd = lambda t: t.transpose(1, 2).contiguous().transpose(1, 2)
+    g2 = sdpa_bwd(blhd(q), blhd(k), blhd(v), blhd(o), blhd(do), lse, w.mask, w.window, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.sdpa_fwd_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window)
+    errs = {"dK": rel_fro(_np(dk), ref["dK"]), "dV": rel_fro(_np(dv), ref["dV"]), "dQ": rel_fro(_np(dq), ref["dQ"])}
+    cross = {"dK": rel_fro(_np(dk), _np(g2[1])), "dV": rel_fro(_np(dv), _np(g2[2]))}
+    print(name, {k_: f"{x:.2e}" for k_, x in errs.items()}, {k_: f"{x:.2e}" for k_, x in cross.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
+    for n, e in cross.items():
+        assert e <= 4e-3, (n, e)   # two kernels, same rounding points, fp32 sums in another order
+    assert torch.equal(dq, g2[0].contiguous())   # dQ comes from the same kernel either way
