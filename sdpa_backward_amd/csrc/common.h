@@ -23,7 +23,7 @@
 // LDS tiles are row-major 16-bit [rows][D] with no padding; the 16-byte chunk c
 // of row r sits at chunk slot c ^ swz(r). swz maps 16 consecutive rows to 16
 // distinct slots (conflict-free 16-byte reads of one column chunk across rows)
-// and 4 consecutive rows to 4 distinct chunk pairs (transposed reads).
+// and 8 consecutive rows to 8 distinct chunk pairs (transposed reads).
 //
 // Tiles arrive by buffer_load_dwordx4 ... lds (checked on the hardware: the 16
 // bytes a lane fetches land at LDS base + 16 * lane, one 1 KB block per wave
@@ -172,20 +172,27 @@ SDPA_DEV bool in_band(int base, int r, int span) { return (uint32_t)base - (uint
 
 // ---------------------------------------------------------------- swizzled tiles
 // Chunk c (16 bytes) of row r sits at chunk slot c ^ swz(r), swz(r) < 16:
-//   bits 2-3 = r & 3, bits 0-1 = (r >> 2) & 3.
+//   bits 2-3 = r & 3, bit 1 = (r >> 2) & 1, bit 0 = (r >> 3) & 1   (D >= 128)
+//   bits 2-3 = r & 3, bits 0-1 = (r >> 2) & 3, masked to 3 bits    (D = 64)
 // 16 consecutive rows get 16 distinct slots (16-byte reads of one chunk
 // across rows, serviced 16 lanes per cycle, hit 16 distinct 16-byte bank
-// groups), and rows r..r+3 (r a multiple of 4) get distinct 64-byte quarters
-// (transposed reads, serviced 32 lanes = 4 rows x 64 bytes per cycle). Both
-// patterns measured conflict-free on the hardware bank-conflict counter for
-// the row strides used here. Only the low 4 chunk bits are permuted, so higher
-// chunk offsets stay additive and every read is a per-lane base plus an
-// immediate offset.
+// groups); rows r..r+3 (r a multiple of 4) get distinct 32-byte chunk pairs,
+// and so do rows r+4..r+7 among themselves and against rows r..r+3
+// (transposed reads, serviced 32 lanes per cycle: the 32x32x16 kernels read 4
+// rows x 4 chunks, the 16x16x32 kernel 8 rows x 2 chunks at a time). The
+// 32x32x16 patterns measured conflict-free on the hardware bank-conflict
+// counter; the earlier D >= 128 form (bits 0-1 = (r >> 2) & 3) put rows r and
+// r + 4 on one chunk pair and gave the 16x16x32 reads 2-way conflicts. Only
+// the low 4 chunk bits are permuted, so higher chunk offsets stay additive and
+// every read is a per-lane base plus an immediate offset.
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;                         // 16-byte chunks per row
   static constexpr int SMASK = CPR >= 16 ? 15 : CPR - 1;   // swizzle bits available
-  SDPA_DEV static int swz(int r) { return (((r & 3) << 2) | ((r >> 2) & 3)) & SMASK; }
+  SDPA_DEV static int swz(int r) {
+    if constexpr (CPR >= 16) return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+    else return (((r & 3) << 2) | ((r >> 2) & 3)) & SMASK;
+  }
   SDPA_DEV static int slot(int r, int c) { return c ^ swz(r); }
 };
 

@@ -16,8 +16,7 @@
 // MFMA 16x16x32 lane layouts (checked on the hardware):
 //   A (16x32, M x K): lane l holds row l%16, k-slots for group g = l/16
 //   B (32x16, K x N): lane l holds col l%16, k-slots for group g = l/16
-//   C (16x16 fp32):   lane l holds col l%16, rows 4g + i, i = 0..3 (tile rows
-//                     4 rho(g) + i, see perm below)
+//   C (16x16 fp32):   lane l holds col l%16, rows 4g + i, i = 0..3
 // Per query tile of 32 rows (row blocks rb = 0, 1), per wave:
 //   S  (32q x 16k) = Q_tile . K_w^T   A: Q (LDS, direct)   B: K_w (registers)
 //   dP (32q x 16k) = dO_tile . V_w^T  A: dO (LDS, direct)  B: V_w (registers)
@@ -34,34 +33,23 @@ namespace sdpa {
 SDPA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 SDPA_DEV f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// Row order (PERM). C row 4g + i of a 16-row block (lane group g) is tile
-// row 4 rho(g) + i, rho = (0, 2, 1, 3): the direct reads fetch A row m from
-// tile row perm(m), so a group's transposed reads (lane groups 0 and 1 are
-// served together) cover rows 0-3 and 8-11, then 4-7 and 12-15, which the
-// swizzle puts in disjoint bank sets (rows r and r + 4 share theirs). Used at
-// D <= 256 (dK/dV 1.19 -> 1.10 ms on the window-1024 L = 16384 layer); at
-// D = 512 the extra registers spill and the plain order is faster.
-template <bool PERM>
-SDPA_DEV int rho(int g) { return PERM ? ((g & 1) << 1) | (g >> 1) : g; }
-template <bool PERM>
-SDPA_DEV int perm(int m) { return 4 * rho<PERM>(m >> 2) + (m & 3); }
-
 // Per-lane LDS byte offsets of the two 16x16x32 operand read patterns of a
 // swizzled [32][D] tile (lane l, group g = l/16, i = l%16):
-//   dir[j]: direct read, row perm(i), 16-byte chunk 4j + g (k-step t reads
-//           dir[t & 3] + 256 (t >> 2), row block rb adds 16 rows)
+//   dir[j]: direct read, row i, 16-byte chunk 4j + g (k-step t reads dir[t & 3]
+//           + 256 (t >> 2), row block rb adds 16 rows)
 //   trn[j]: transposed read for columns 16j.. (d-block b reads trn[b & 7] +
-//           256 (b >> 3)): row 4 rho(g) + i/4, column 16j + 4 (i%4); rows + 16
-//           for the second half of the k-slots
+//           256 (b >> 3)): row 4g + i/4, column 16j + 4 (i%4); rows + 16 for
+//           the second half of the k-slots. Lane groups 0 and 1 (served
+//           together) read rows 0-7 of one chunk pair: the tile swizzle gives
+//           those 8 rows 8 distinct pairs.
 template <int D>
 struct LaneAddr16 {
-  static constexpr bool PERM = D <= 256;
   uint32_t dir[4], trn[8];
   SDPA_DEV void init(int lane) {
-    const int g = lane >> 4, i = lane & 15, pi = perm<PERM>(i);
+    const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; j++) dir[j] = pi * D * 2 + (Tile<D>::slot(pi, 4 * j + g) & 15) * 16;
-    const int r = 4 * rho<PERM>(g) + (i >> 2);
+    for (int j = 0; j < 4; j++) dir[j] = i * D * 2 + (Tile<D>::slot(i, 4 * j + g) & 15) * 16;
+    const int r = 4 * g + (i >> 2);
 #pragma unroll
     for (int j = 0; j < 8; j++) trn[j] = r * D * 2 + (Tile<D>::slot(r, 2 * j + ((i & 3) >> 1)) & 15) * 16 + (i & 1) * 8;
   }
@@ -85,8 +73,7 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
   __shared__ __attribute__((aligned(16))) float rv1[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
-  const int rg = 4 * rho<LaneAddr16<D>::PERM>(gq);  // first tile row of the lane's C rows
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, rg = 4 * gq;  // rg: first row of the lane's C rows
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   LaneAddr16<D> la;
   la.init(lane);
@@ -204,7 +191,7 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
           __builtin_amdgcn_make_buffer_rsrc((void*)(Delta + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
   };
 
-  // direct A operand: tile row 16 rb + perm(l%16), d-slots 32 t + 8 g + 0..7
+  // direct A operand: tile row 16 rb + l%16, d-slots 32 t + 8 g + 0..7
   auto rd_dir = [&](const E* T, int t, int rb) {
     const char* p = reinterpret_cast<const char*>(T) + la.dir[t & 3] + (t >> 2) * 256 + rb * 16 * D * 2;
     return *(const ex8*)p;
