@@ -22,6 +22,9 @@ CASES = [
     ("mha64_causal_L512", 1, 64, 64, 512, 512, 256, "bf16", MASK_CAUSAL, 0),
     ("gqa2_w100_ragged_L1000", 1, 64, 32, 1000, 1000, 256, "bf16", MASK_WINDOW, 100),
     ("B2_two_sided_suffix", 2, 32, 16, 300, 1000, 256, "f16", MASK_TWO_SIDED, 77),
+    ("gqa4_causal_f16_L1024", 1, 128, 32, 1024, 1024, 256, "f16", MASK_CAUSAL, 0),
+    ("more_rows_than_keys", 1, 64, 64, 700, 512, 256, "bf16", MASK_CAUSAL, 0),   # 188 rows see no key
+    ("window_one", 1, 64, 64, 512, 512, 256, "bf16", MASK_WINDOW, 1),
 ]
 
 
@@ -39,7 +42,7 @@ def test_kv16_d256(case):
     g2 = sdpa_bwd(blhd(q), blhd(k), blhd(v), blhd(o), blhd(do), lse, w.mask, w.window, w.scale)
     torch.cuda.synchronize()
     ref = oracle.sdpa_fwd_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window)
-    errs = {"dK": rel_fro(_np(dk), ref["dK"]), "dV": rel_fro(_np(dv), ref["dV"]), "dQ": rel_fro(_np(dq), ref["dQ"])}
+    errs = {n: rel_fro(_np(t), ref[n]) for n, t in (("dK", dk), ("dV", dv), ("dQ", dq))}
     cross = {"dK": rel_fro(_np(dk), _np(g2[1])), "dV": rel_fro(_np(dv), _np(g2[2]))}
     print(name, {k_: f"{x:.2e}" for k_, x in errs.items()}, {k_: f"{x:.2e}" for k_, x in cross.items()}, flush=True)
     for n, e in errs.items():
