@@ -35,8 +35,11 @@ SDPA_DEV f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_
 
 // Per-lane LDS byte offsets of the two 16x16x32 operand read patterns of a
 // swizzled [32][D] tile (lane l, group g = l/16, i = l%16):
-//   dir[j]: direct read, row i, 16-byte chunk 4j + g (k-step t reads dir[t & 3]
-//           + 256 (t >> 2), row block rb adds 16 rows)
+//   dir[j]: direct read, row i, 16-byte chunk 4g + j (k-step t reads dir[t & 3]
+//           + 256 (t >> 2), row block rb adds 16 rows). The four lane groups
+//           take chunks 4 apart: with chunks 0-3 (group g on chunk g) the
+//           16-byte reads measure about 3 bank-conflict cycles each under
+//           this swizzle, with chunks 0, 4, 8, 12 none.
 //   trn[j]: transposed read for columns 16j.. (d-block b reads trn[b & 7] +
 //           256 (b >> 3)): row 4g + i/4, column 16j + 4 (i%4); rows + 16 for
 //           the second half of the k-slots. Lane groups 0 and 1 (served
@@ -48,7 +51,7 @@ struct LaneAddr16 {
   SDPA_DEV void init(int lane) {
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; j++) dir[j] = i * D * 2 + (Tile<D>::slot(i, 4 * j + g) & 15) * 16;
+    for (int j = 0; j < 4; j++) dir[j] = i * D * 2 + (Tile<D>::slot(i, 4 * g + j) & 15) * 16;
     const int r = 4 * g + (i >> 2);
 #pragma unroll
     for (int j = 0; j < 8; j++) trn[j] = r * D * 2 + (Tile<D>::slot(r, 2 * j + ((i & 3) >> 1)) & 15) * 16 + (i & 1) * 8;
@@ -98,15 +101,18 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   const int ihi2 = kshift ? min(Lq - 1, kj + cut.sh - dlo) : 0, ilo2 = max(cut.r0, kj + cut.sh - dhi);
   const int kspan2 = kshift && kj < Lk && ihi2 >= ilo2 ? ihi2 - ilo2 + 1 : 0;
 
-  // K_w^T and V_w^T as B operands: lane holds key kj, d-slots 32 t + 8 g + 0..7
+  // K_w^T and V_w^T as B operands: lane holds key kj; its k-slots in step t
+  // are d = 128 (t / 4) + 32 g + 8 (t % 4) + 0..7, the chunk the direct read
+  // of the same step gives the A operand
   ex8 kreg[NT], vreg[NT];
   {
     const E* krow = Kg + (long long)(kj < Lk ? kj : 0) * st.k.l;
     const E* vrow = Vg + (long long)(kj < Lk ? kj : 0) * st.v.l;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      kreg[t] = kj < Lk ? *(const ex8*)(krow + 32 * t + 8 * gq) : zero8<E>();
-      vreg[t] = kj < Lk ? *(const ex8*)(vrow + 32 * t + 8 * gq) : zero8<E>();
+      const int d0 = 128 * (t >> 2) + 32 * gq + 8 * (t & 3);
+      kreg[t] = kj < Lk ? *(const ex8*)(krow + d0) : zero8<E>();
+      vreg[t] = kj < Lk ? *(const ex8*)(vrow + d0) : zero8<E>();
     }
   }
   f32x4 dkacc[NB], dvacc[NB];
@@ -191,7 +197,7 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
           __builtin_amdgcn_make_buffer_rsrc((void*)(Delta + rb), 0, (uint32_t)Lq * 4, 0x00020000), dst, 4, off, 0, 0, 0);
   };
 
-  // direct A operand: tile row 16 rb + l%16, d-slots 32 t + 8 g + 0..7
+  // direct A operand: tile row 16 rb + l%16, d-slots 128 (t / 4) + 32 g + 8 (t % 4) + 0..7
   auto rd_dir = [&](const E* T, int t, int rb) {
     const char* p = reinterpret_cast<const char*>(T) + la.dir[t & 3] + (t >> 2) * 256 + rb * 16 * D * 2;
     return *(const ex8*)p;

@@ -6,6 +6,7 @@ v_mfma_f32_16x16x32 (D = 512 always does; its cases live in the other
 files). Checked against the fp64 oracle, and against the 32-key kernel,
 which a strided copy of the same tensors takes.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -47,6 +48,12 @@ def test_kv16_d256(case):
     print(name, {k_: f"{x:.2e}" for k_, x in errs.items()}, {k_: f"{x:.2e}" for k_, x in cross.items()}, flush=True)
     for n, e in errs.items():
         assert e <= TOL[dtype], (n, e)
+    if mask == MASK_WINDOW and window == 1:
+        # one key per row: P = 1 and dP equals Delta, so dK is exactly zero and
+        # both kernels return fp32 cancellation noise, summed over d in different
+        # orders; bound the difference absolutely instead of relatively
+        assert float(np.linalg.norm(_np(dk) - _np(g2[1]))) <= TOL[dtype], cross
+        cross.pop("dK")
     for n, e in cross.items():
         assert e <= 4e-3, (n, e)   # two kernels, same rounding points, fp32 sums in another order
     assert torch.equal(dq, g2[0].contiguous())   # dQ comes from the same kernel either way
