@@ -49,6 +49,17 @@ def dkdv_kernel(w):
     return f"kv_kernel<{w.D}>" + (" + share reduce" if blocks < 256 else "")
 
 
+def tile_config(w):
+    """The kernels' tile shapes for this workload (as the library picks them)."""
+    if w.dtype == "f32":
+        return "fp32 VALU kernels (one query row per lane; one key per lane in dK/dV)"
+    bq = 128 if w.D <= 256 else 64
+    bk = 64 if w.D <= 256 else 32
+    split = "" if w.D <= 256 else ", head dim split over wave pairs"
+    return (f"forward and dQ: {bq} query rows x {bk}-key tiles per workgroup (4 waves, 32x32x16 MFMA{split}); "
+            f"dK/dV: {dkdv_kernel(w)}")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -195,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold", type=int, default=3,
+                    help="steps timed after a 1 GiB device write (caches cold), before the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference kernel for HBM counter scaling)")
@@ -253,6 +266,19 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # cold caches: a 1 GiB write (well above the L2s and the 256 MB MALL) before each
+    # of these steps; they run before the timed steps, which stay the last calls
+    cold = []
+    if a.cold > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for i in range(a.cold):
+            scratch.fill_(float(i))
+            e = [ev.create() for _ in range(5)]
+            step(e)
+            torch.cuda.synchronize()
+            cold.append((ev.ms(e[0], e[1]), ev.ms(e[1], e[4])))
+        del scratch
+        torch.cuda.empty_cache()
     t0 = time.perf_counter()
     for i in range(a.steps):
         step(evs[i])
@@ -311,6 +337,10 @@ def main():
                             "tflops_6DN": round(6 * w.D * N / (med(bwd_ms) - med(main_ms)) / 1e9, 1)},
             "fwd_plus_bwd_wall": {"ms": round(ms_per_step, 4)},
         },
+        "cold": None if not cold else {
+            "steps": len(cold), "note": "each step after a 1 GiB device write",
+            "fwd_ms_median": round(med([c[0] for c in cold]), 4),
+            "bwd_ms_median": round(med([c[1] for c in cold]), 4)},
         "roofline": {
             "kernel": f"{dkdv_kernel(w)} (dK/dV pass)",
             "bound": "mfma",
@@ -328,7 +358,10 @@ def main():
         },
     }
     result["env"] = {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,
-                     "hip": getattr(torch.version, "hip", None), "arch": "gfx950"}
+                     "hip": getattr(torch.version, "hip", None), "arch": "gfx950",
+                     "abi": sdpa.load().sdpa_abi_version(),
+                     "clock_ghz_from_mfma_probe": round(peak_meas / (BF16_PEAK_TFLOPS / 2.4), 3),
+                     "tiles": tile_config(w)}
     if not a.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, cpu_inp, a.cpu_seconds)

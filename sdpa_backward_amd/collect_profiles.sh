@@ -26,7 +26,7 @@ while read -r C; do
   i=$((i + 1))
   echo "== counters pass $i: $C"
   timeout -s KILL 120 rocprofv3 --pmc $C --output-format csv -d "$OUT/p$i" -o run -- \
-    python -u bench.py --no-cpu-baseline --workload "$W" --steps 2 --warmup 1 --copy-probe > "$OUT/p$i.log" 2>&1 || exit $?
+    python -u bench.py --no-cpu-baseline --workload "$W" --steps 2 --warmup 1 --cold 0 --copy-probe > "$OUT/p$i.log" 2>&1 || exit $?
 done < <(python -c "import sdpa_backward_amd.profsum as p; print('\n'.join(p.PASSES))")
 
 python -m sdpa_backward_amd.profsum "$OUT" --workload "$W" || exit $?

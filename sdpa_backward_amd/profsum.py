@@ -164,7 +164,7 @@ def main():
              "```", "", "whose counter passes are (one rocprofv3 run each):", "", "```"]
     for i, cs in enumerate(PASSES, 1):
         lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {cs} --output-format csv -d OUTDIR/p{i} -o run -- "
-                     f"python -u bench.py --no-cpu-baseline --workload {w.name} --steps 2 --warmup 1 --copy-probe")
+                     f"python -u bench.py --no-cpu-baseline --workload {w.name} --steps 2 --warmup 1 --cold 0 --copy-probe")
     lines += ["```", "",
               f"HBM byte scaling from the 1 GiB device copy in the same runs: FETCH_SIZE KiB x {fetch_scale:.3f} "
               f"= bytes read / 1024, WRITE_SIZE KiB x {write_scale:.3f} = bytes written / 1024.", "",
