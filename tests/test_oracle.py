@@ -17,7 +17,7 @@ import torch
 import oracle
 from oracle import sdpa_oracle
 from tests import oracle_pins as pins
-from workloads import CONFIGS, make_inputs
+from workloads import BY_NAME, make_inputs
 
 pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
 
@@ -88,15 +88,15 @@ def _cfg_inputs(w, **shrink):
     return [t[n].to(torch.float64).numpy() for n in ("q", "k", "v", "do")], w
 
 
-@pytest.mark.parametrize("which,shrink", [
-    (0, {}),
-    (1, {}),
-    (2, {"Hq": 4, "Hkv": 1, "L": 1024}),      # global layer geometry (D=512, group 4), shortened
-    (3, {"Hq": 4, "Hkv": 2, "L": 1500, "window": 300}),  # sliding geometry, several windows
-    (4, {"Hq": 2, "Hkv": 1, "L": 777, "window": 129}),   # ragged length, window not a power of 2
+@pytest.mark.parametrize("name,shrink", [
+    ("tiny_fp32_causal_L128_D64_gqa2", {}),
+    ("bf16_causal_gqa_L2048_D256_h8kv4", {}),
+    ("bf16_causal_global_L8192_D512_h16kv4", {"Hq": 4, "Hkv": 1, "L": 1024}),      # global layer geometry (D=512, group 4), shortened
+    ("bf16_window1024_L16384_D256_h32kv16", {"Hq": 4, "Hkv": 2, "L": 1500, "window": 300}),  # sliding geometry, several windows
+    ("bf16_window1024_ragged_L30553_D256_h32kv16", {"Hq": 2, "Hkv": 1, "L": 777, "window": 129}),   # ragged length, window not a power of 2
 ])
-def test_autograd_independent(which, shrink):
-    (q, k, v, do), w = _cfg_inputs(CONFIGS[which], **shrink)
+def test_autograd_independent(name, shrink):
+    (q, k, v, do), w = _cfg_inputs(BY_NAME[name], **shrink)
     err = pins.autograd_error(sdpa_oracle, q, k, v, do, w.scale, w.mask, w.window)
     assert err <= 1e-12, err
 
@@ -119,8 +119,9 @@ def test_autograd_independent_more_masks(Lq, Lk, mask, window):
 
 def test_library_sdpa_forward():
     import torch.nn.functional as F
-    for which, shrink in ((0, {}), (1, {"L": 1024}), (3, {"Hq": 4, "Hkv": 2, "L": 700, "window": 100})):
-        (q, k, v, do), w = _cfg_inputs(CONFIGS[which], **shrink)
+    for name, shrink in (("tiny_fp32_causal_L128_D64_gqa2", {}), ("bf16_causal_gqa_L2048_D256_h8kv4", {"L": 1024}),
+                         ("bf16_window1024_L16384_D256_h32kv16", {"Hq": 4, "Hkv": 2, "L": 700, "window": 100})):
+        (q, k, v, do), w = _cfg_inputs(BY_NAME[name], **shrink)
         O, lse = oracle.sdpa_forward(q, k, v, w.scale, w.mask, w.window)
         L = w.L
         i = torch.arange(L)[:, None]

@@ -20,7 +20,7 @@ import torch
 import oracle
 from sdpa_backward_amd import sdpa_bwd, sdpa_fwd_lse
 from tests.oracle_pins import rel_fro
-from workloads import CONFIGS, MASK_CAUSAL, MASK_WINDOW, Workload, make_inputs
+from workloads import BY_NAME, MASK_CAUSAL, MASK_WINDOW, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -105,16 +105,20 @@ def test_scale_one_and_three():
 
 
 # ------------------------------------------------------------------ the five workloads
-@pytest.mark.parametrize("which", [0, 1])
-def test_small_workloads_full(which):
-    w = CONFIGS[which]
+SMALL = ["tiny_fp32_causal_L128_D64_gqa2", "bf16_causal_gqa_L2048_D256_h8kv4"]
+LARGE = ["bf16_causal_global_L8192_D512_h16kv4", "bf16_window1024_L16384_D256_h32kv16", "bf16_window1024_ragged_L30553_D256_h32kv16"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workloads_full(name):
+    w = BY_NAME[name]
     inp = make_inputs(w)
     check_full(w, run(w, inp), oracle_full(w, inp))
 
 
 def test_second_seed_draw():
-    for which in (0, 1):
-        w = CONFIGS[which]
+    for name in SMALL:
+        w = BY_NAME[name]
         inp = make_inputs(w, seed=w.seed + 1000)
         check_full(w, run(w, inp), oracle_full(w, inp))
 
@@ -195,9 +199,9 @@ def _check_poison(w, bufs, views):
         assert torch.all(bufs[n][v.numel():] == 12345.0).item(), f"{n} canary tail overwritten"
 
 
-@pytest.mark.parametrize("which", [2, 3, 4])
-def test_large_workloads_sampled(which):
-    w = CONFIGS[which]
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workloads_sampled(name):
+    w = BY_NAME[name]
     inp = make_inputs(w)
     bufs, views = _poisoned_outputs(w)
     gpu = run(w, inp, out=[views[n] for n in ("O", "lse", "dQ", "dK", "dV")])
@@ -285,7 +289,7 @@ def test_masked_keys_do_not_change_outputs():
 
 
 def test_determinism():
-    w = CONFIGS[1]
+    w = BY_NAME["bf16_causal_gqa_L2048_D256_h8kv4"]
     inp = make_inputs(w)
     a = run(w, inp)
     b = run(w, inp)

@@ -66,7 +66,7 @@ class Workload:
 
 
 # The five workloads of this path, smallest first.
-CONFIGS = [
+WORKLOADS = [
     Workload("tiny_fp32_causal_L128_D64_gqa2", 1, 2, 1, 128, 64, "f32", MASK_CAUSAL, 0, 1000),
     Workload("bf16_causal_gqa_L2048_D256_h8kv4", 1, 8, 4, 2048, 256, "bf16", MASK_CAUSAL, 0, 1001),
     Workload("bf16_causal_global_L8192_D512_h16kv4", 1, 16, 4, 8192, 512, "bf16", MASK_CAUSAL, 0, 1002),
@@ -84,7 +84,7 @@ VARIANTS = [
              Lk=16384),
     Workload("bf16_nomask_L4096_D256_h32kv16", 1, 32, 16, 4096, 256, "bf16", MASK_NONE, 0, 1007),
 ]
-BY_NAME = {w.name: w for w in CONFIGS + VARIANTS}
+BY_NAME = {w.name: w for w in WORKLOADS + VARIANTS}
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
