@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -34,9 +33,6 @@ METRIC = "attention fwd+bwd mask-aware TFLOP/s and % of bf16 MFMA peak; peak mem
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public figure (no sparsity)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_window1024_L16384_D256_h32kv16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv16_kernel_window1024_L16384_D256.json")
-# the dK/dV kernel of the default workload (dense, D = 256, 4096 key blocks)
-MAIN_KERNEL_SOURCES = ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h"]
 
 
 def dkdv_kernel(w):
@@ -136,22 +132,17 @@ class HipEvents:
         return out.value
 
 
-def sources_sha256():
-    h = hashlib.sha256()
-    for rel in MAIN_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def measured_traffic(workload_name):
-    """HBM bytes per main-kernel launch from the committed counter runs, if they match this source."""
+def measured_traffic(w):
+    """HBM bytes per dK/dV-kernel launch from the committed counter runs on this workload
+    (profiles/traffic_<kernel>_<workload tag>.json), if they were taken on this source."""
+    from sdpa_backward_amd.profsum import sources_sha256, tag
+    kernel = dkdv_kernel(w).split("<")[0]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", f"traffic_{kernel}_{tag(w)}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("sources_sha256") != sources_sha256() or t.get("workload") != workload_name:
+    if t.get("sources_sha256") != sources_sha256(kernel) or t.get("workload") != w.name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -305,7 +296,7 @@ def main():
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
     kv_flop = 8 * w.D * N  # the dK/dV kernel's own work: S, dP, dV, dK contractions
     achieved = kv_flop / (statistics.mean(main_ms) * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w)
     med = statistics.median
 
     result = {
