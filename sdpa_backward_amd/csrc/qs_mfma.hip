@@ -259,6 +259,12 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       for (int j = NM / EVERY; j < NLD; j++) load_one(j);  // (when there are more loads than MFMA steps)
     }
     if constexpr (C::DS == 2) exchange_add<NX>(st, xbuf, w, lane);
+    if constexpr (MODE == QS_FWD) {
+      // the softmax reads every score twice (max, then exp): move them to
+      // VGPRs once here rather than out of the accumulator registers twice
+#pragma unroll
+      for (int t = 0; t < NX; t++) asm volatile("" : "+v"(st[t]));
+    }
     if (!active) return;
 
     if constexpr (MODE == QS_FWD) {
