@@ -24,10 +24,13 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-# sources of each dK/dV kernel, hashed into its traffic file: the counters hold
-# only for the code they were taken on
-KERNEL_SOURCES = {"kv16_kernel": ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h"],
-                  "kv_kernel": ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h"]}
+# sources of each dK/dV kernel (and the build script, which holds the compiler
+# flags), hashed into its traffic file: the counters hold only for the code
+# they were taken on
+KERNEL_SOURCES = {"kv16_kernel": ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h",
+                                  "sdpa_backward_amd/build.py"],
+                  "kv_kernel": ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h",
+                                "sdpa_backward_amd/build.py"]}
 COPY_KERNEL = "copyBuffer"   # the 1 GiB device copy bench.py --copy-probe runs
 COPY_BYTES = 1 << 30
 
