@@ -310,7 +310,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": w.dtype,
         "data": "synthetic (seeded i.i.d. N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "Lk": w.Lkv, "D": w.D,
                    "mask": w.mask, "window": w.window, "scale": w.scale, "allowed_pairs": N},

@@ -28,6 +28,13 @@ class SDPAFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse, sinks = ctx.saved_tensors
         mask, window, scale, cut = ctx.cfg
+        # The incoming gradient is often an expanded view: o.sum().backward()
+        # hands over strides (0, 0, 0, 0), a loss weighted by a broadcast vector
+        # a zero row stride. The library reads rows of D contiguous elements
+        # with one row stride shared by q and dO, so such views become a
+        # contiguous copy in q's layout.
+        if do.stride(3) != 1 or 0 in do.stride() or do.stride(2) != q.stride(2):
+            do = torch.empty_like(q).copy_(do)  # q's strides when q is dense, else contiguous
         grads = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale, sinks=sinks, cut=cut)
         dsinks = grads[3] if sinks is not None else None
         return grads[0], grads[1], grads[2], None, None, None, dsinks, None

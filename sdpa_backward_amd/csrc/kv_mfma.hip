@@ -11,26 +11,19 @@
 // says"); S and dP stay in fp32 registers, only P and dS are rounded to the
 // input type as MFMA operands (section "fp32 score tiles").
 //
-// Per query tile of 32 rows, per wave (owning 32 keys; for D = 512 two waves
-// share a key block and split the head dimension, adding their partial S and
-// dP tiles through LDS):
+// Per query tile of 32 rows, per wave (owning 32 keys):
 //   S  (32q x 32k) = Q_tile . K_w^T   A: Q (LDS, direct)   B: K_w (LDS, direct)
 //   dP (32q x 32k) = dO_tile . V_w^T  A: dO (LDS, direct)  B: V_w (registers)
 //   P = exp2(S c - lse2), dS = P * (dP - Delta)      (Delta from the dQ pass)
 //   dV_w += P^T . dO                  A: P^T (C tile reused)  B: dO (LDS, transposed reads)
 //   dK_w += dS^T . Q                  A: dS^T (C tile)        B: Q  (LDS, transposed reads)
-// Q/dO tiles stream into LDS with asynchronous global->LDS loads, double
-// buffered when they fit (D <= 256).
+// Q/dO tiles stream into double-buffered LDS with asynchronous global->LDS
+// loads. Head dims up to 256 (D = 512 runs the 16-key kernel of kv16_mfma.hip).
 #include <type_traits>
 
 #include "common.h"
 
 namespace sdpa {
-
-// Which gradients one launch produces. D = 512 splits them into two launches
-// (dV, then dK) so each wave's accumulators fit the register file; smaller D
-// produce both in one pass.
-enum { KV_BOTH = 0, KV_DV = 1, KV_DK = 2 };
 
 #ifndef KV_AHEAD
 #define KV_AHEAD 3  // S / dP operand reads issued this many MFMAs ahead
@@ -38,48 +31,32 @@ enum { KV_BOTH = 0, KV_DV = 1, KV_DK = 2 };
 
 template <int D>
 struct KvCfg {
+  static_assert(D <= 256, "the 32-key kernel serves head dims up to 256");
   static constexpr int NW = 4;
-  static constexpr int DS = D > 256 ? 2 : 1;   // waves sharing one key block (head-dim split)
-  static constexpr int NWK = NW / DS;          // key blocks per workgroup
-  static constexpr int BKT = 32 * NWK;         // keys per workgroup
-  static constexpr int DW = D / DS;            // head-dim slice of one wave
+  static constexpr int BKT = 32 * NW;          // keys per workgroup
   static constexpr int BQ = 32;                // query rows per step
-  static constexpr int NBUF = D > 256 ? 1 : 2; // Q/dO buffers
 };
-
-// Add the partner wave's partial C tile (head-dim split): both waves of the
-// pair end with identical sums. One 16 KB buffer, so S and dP go one at a time.
-SDPA_DEV void kv_exchange_add(f32x16& c, float* xbuf, int w, int lane) {
-#pragma unroll
-  for (int i = 0; i < 16; i++) xbuf[(w * 16 + i) * 64 + lane] = c[i];
-  lds_barrier();
-  const int p = w ^ 1;
-#pragma unroll
-  for (int i = 0; i < 16; i++) c[i] += xbuf[(p * 16 + i) * 64 + lane];
-  lds_barrier();
-}
 
 // SPLIT (dense, one pass): blockIdx also picks one of nseg equal shares of the
 // key block's query tiles, and the workgroup writes fp32 partial dK (scaled)
 // and dV for its keys into Part, share-major: [2][nseg][B][Hkv][Lk][D] (dK
 // shares first); kv_reduce_kernel then sums the shares. Small problems whose
 // key blocks alone would leave CUs idle get more workgroups this way.
-template <int D, int PASS, typename E, bool DENSE, bool SPLIT>
+template <int D, typename E, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
           E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
           Cut cut_arg, float scale, float scale_log2, AllStrides st_arg, float* __restrict__ Part, int nseg) {
-  static_assert(!SPLIT || (DENSE && PASS == 0), "the split runs the dense one-pass kernel");
+  static_assert(!SPLIT || DENSE, "the split runs the dense kernel");
   using C = KvCfg<D>;
   using ex8 = typename Vec<E>::x8;
-  constexpr int DW = C::DW, NKS = DW / 16, NDB = DW / 32, QT = C::BQ * D;
+  constexpr int NKS = D / 16, NDB = D / 32, QT = C::BQ * D;
   __shared__ __attribute__((aligned(16))) E ks[C::BKT * D];
   __shared__ __attribute__((aligned(16))) E qb0[QT];
   __shared__ __attribute__((aligned(16))) E db0[QT];
-  __shared__ __attribute__((aligned(16))) E qb1[C::NBUF == 2 ? QT : 8];
-  __shared__ __attribute__((aligned(16))) E db1[C::NBUF == 2 ? QT : 8];
-  __shared__ __attribute__((aligned(16))) float xbuf[C::DS == 2 ? C::NW * 1024 : 4];
+  __shared__ __attribute__((aligned(16))) E qb1[QT];
+  __shared__ __attribute__((aligned(16))) E db1[QT];
   __shared__ __attribute__((aligned(16))) float rv0[64];  // lse (rows 0..31) and Delta (rows 0..31) of a tile
   __shared__ __attribute__((aligned(16))) float rv1[64];
 
@@ -87,7 +64,6 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   LaneAddr<D> la;  // per-lane LDS offsets of the operand read patterns
   la.init(lane);
-  const int kwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int Hkv = Hq / group;
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
   const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
@@ -96,7 +72,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int seg = SPLIT ? logical % nseg : 0, kblk = SPLIT ? logical / nseg : logical;
   const int kt = kblk % nkt, g = (kblk / nkt) % Hkv, b = kblk / (nkt * Hkv);
   const int k0 = kt * C::BKT;
-  const int kb0 = k0 + 32 * kwi;           // first key of this wave's block
+  const int kb0 = k0 + 32 * w;             // first key of this wave's block
   const int kj = kb0 + (lane & 31);        // key held by this lane (C-tile column)
   const E* Kg = K + b * st.k.b + g * st.k.h;
   const E* Vg = V + b * st.v.b + g * st.v.h;
@@ -115,10 +91,8 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   zero_lds(ks, C::BKT * D, tid);
   zero_lds(qb0, QT, tid);
   zero_lds(db0, QT, tid);
-  if constexpr (C::NBUF == 2) {
-    zero_lds(qb1, QT, tid);
-    zero_lds(db1, QT, tid);
-  }
+  zero_lds(qb1, QT, tid);
+  zero_lds(db1, QT, tid);
   lds_barrier();
   {
     TileLoader<D, C::BKT, C::NW, DENSE> kld;
@@ -131,21 +105,17 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   ldq.init(w, lane, st.q.l);
   const auto& ldd = ldq;
   using LD = decltype(ldq);
-  // V_w^T as B operands of dP: lane holds key kj, d-slots dw0 + 16*s + 8*hh + 0..7
-  constexpr bool WANT_DV = PASS != KV_DK, WANT_DK = PASS != KV_DV;
-  ex8 vreg[WANT_DK ? NKS : 1];
-  if constexpr (WANT_DK) {
+  // V_w^T as B operands of dP: lane holds key kj, d-slots 16*s + 8*hh + 0..7
+  ex8 vreg[NKS];
+  {
     const E* vrow = Vg + (long long)(kj < Lk ? kj : 0) * st.v.l;
 #pragma unroll
-    for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const ex8*)(vrow + dw0 + 16 * s + 8 * hh) : zero8<E>();
+    for (int s = 0; s < NKS; s++) vreg[s] = kj < Lk ? *(const ex8*)(vrow + 16 * s + 8 * hh) : zero8<E>();
   }
 
-  f32x16 dkacc[WANT_DK ? NDB : 1], dvacc[WANT_DV ? NDB : 1];
+  f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
-  for (int d = 0; d < NDB; d++) {
-    if constexpr (WANT_DK) dkacc[d] = zero16();
-    if constexpr (WANT_DV) dvacc[d] = zero16();
-  }
+  for (int d = 0; d < NDB; d++) dkacc[d] = dvacc[d] = zero16();
 
   // query tiles that can see a key of this workgroup, for each q-head of the group
   // (none: total = 0, and the keys get zero gradients)
@@ -264,7 +234,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
           p = in_band(base, rr, kspan) || (!DENSE && in_band(base2, rr, kspan2)) ? p : 0.f;
         }
         s_acc[i] = p;
-        if constexpr (WANT_DK) dp_acc[i] = p * (dp_acc[i] - dv);
+        dp_acc[i] = p * (dp_acc[i] - dv);
       }
     }
   };
@@ -272,19 +242,14 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   else form(std::true_type{});
   const ex8 pa0 = c_to_op<E>(s_acc, 0), pa1 = c_to_op<E>(s_acc, 1);
   const ex8 da0 = c_to_op<E>(dp_acc, 0), da1 = c_to_op<E>(dp_acc, 1);
-  (void)pa0; (void)pa1; (void)da0; (void)da1;
-  constexpr int MPB = (WANT_DV ? 2 : 0) + (WANT_DK ? 2 : 0);  // MFMAs per head-dim block
+  constexpr int MPB = 4;  // MFMAs per head-dim block
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
-    const int c0 = dw0 + 32 * d;
-    if constexpr (WANT_DV) {
-      dvacc[d] = mfma(pa0, op_tr<D, E>(dOc, la, 0, c0), dvacc[d]);
-      dvacc[d] = mfma(pa1, op_tr<D, E>(dOc, la, 16, c0), dvacc[d]);
-    }
-    if constexpr (WANT_DK) {
-      dkacc[d] = mfma(da0, op_tr<D, E>(Qc, la, 0, c0), dkacc[d]);
-      dkacc[d] = mfma(da1, op_tr<D, E>(Qc, la, 16, c0), dkacc[d]);
-    }
+    const int c0 = 32 * d;
+    dvacc[d] = mfma(pa0, op_tr<D, E>(dOc, la, 0, c0), dvacc[d]);
+    dvacc[d] = mfma(pa1, op_tr<D, E>(dOc, la, 16, c0), dvacc[d]);
+    dkacc[d] = mfma(da0, op_tr<D, E>(Qc, la, 0, c0), dkacc[d]);
+    dkacc[d] = mfma(da1, op_tr<D, E>(Qc, la, 16, c0), dkacc[d]);
   }
   // schedule: transposed reads run one head-dim block ahead of their MFMAs
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * MPB, 1);
@@ -295,22 +260,20 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
   };
 
-  // One query tile. With PREFETCH the next tile's Q, dO (and lse, Delta) loads
-  // into (qn, dn, rvn) are issued one at a time between the S / dP MFMAs: in
+  // One query tile. The next tile's Q, dO (and lse, Delta) loads into
+  // (qn, dn, rvn) are issued one at a time between the S / dP MFMAs: in
   // one burst they stall the wave until the CU's vector-memory path has taken
   // them all. A load stays after the LDS reads that precede it in program
   // order (it writes LDS), so the operand reads are software-pipelined by hand
   // and the loads slot in between them. Past the last tile the resources cover
   // no rows (nothing is read).
-  auto compute = [&](auto prefetch, int it, const E* Qc, const E* dOc, const float* rv, E* qn,
-                     E* dn, float* rvn) {
-    constexpr bool PF = decltype(prefetch)::value;
+  auto compute = [&](int it, const E* Qc, const E* dOc, const float* rv, E* qn, E* dn, float* rvn) {
     const int q0 = q0_of(it);
     bool active, full;
     tile_tests(q0, active, full);
 
     __amdgpu_buffer_rsrc_t qrs, drs;
-    if constexpr (PF) {
+    {
       const bool more = it + 1 < it_e;
       const E *qs, *ds;
       int q0n;
@@ -334,15 +297,15 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // is S with k-slice k, step NKS + k is dP with k-slice k.
     f32x16 s_acc = zero16(), dp_acc = zero16();
     {
-      constexpr int NM = WANT_DK ? 2 * NKS : NKS, AH = KV_AHEAD, NLD = PF ? 2 * NJ : 0;
-      constexpr int EVERY = NLD > 0 && NM / NLD > 0 ? NM / NLD : 1;
+      constexpr int NM = 2 * NKS, AH = KV_AHEAD, NLD = 2 * NJ;
+      constexpr int EVERY = NM / NLD > 0 ? NM / NLD : 1;
       ex8 ra[AH], rb[AH];
       auto rd = [&](int k) {
         if (k < NKS) {
-          ra[k % AH] = op_direct<D, E>(Qc, la, dw0 + 16 * k, 0);
-          rb[k % AH] = op_direct<D, E>(ks, la, dw0 + 16 * k, 32 * kwi);
+          ra[k % AH] = op_direct<D, E>(Qc, la, 16 * k, 0);
+          rb[k % AH] = op_direct<D, E>(ks, la, 16 * k, 32 * w);
         } else {
-          ra[k % AH] = op_direct<D, E>(dOc, la, dw0 + 16 * (k - NKS), 0);
+          ra[k % AH] = op_direct<D, E>(dOc, la, 16 * (k - NKS), 0);
         }
       };
 #pragma unroll
@@ -350,120 +313,27 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 #pragma unroll
       for (int k = 0; k < NM; k++) {
         if (k < NKS) s_acc = mfma(ra[k % AH], rb[k % AH], s_acc);
-        else if constexpr (WANT_DK) dp_acc = mfma(ra[k % AH], vreg[k - NKS], dp_acc);
+        else dp_acc = mfma(ra[k % AH], vreg[k - NKS], dp_acc);
         if (k + AH < NM) rd(k + AH);
-        if constexpr (NLD > 0) {
-          if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
-        }
+        if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
       }
-      if constexpr (NLD > 0) {
 #pragma unroll
-        for (int j = NM / EVERY; j < NLD; j++) load_one(j);
-      }
-    }
-    if constexpr (C::DS == 2) {
-      kv_exchange_add(s_acc, xbuf, w, lane);
-      if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
+      for (int j = NM / EVERY; j < NLD; j++) load_one(j);
     }
     if (!active) return;
     form_and_update(q0, full, rv, s_acc, dp_acc, Qc, dOc);
   };
 
-  if (it_b >= it_e) {
-    // no row sees these keys (or no tile falls to this share): zero gradients
-  } else if constexpr (C::NBUF == 2) {
+  if (it_b < it_e) {  // (none: no row sees these keys, or no tile falls to this share: zero gradients)
     issue(it_b, qb0, db0, rv0);
     wait_all_and_barrier();
     for (int it = it_b; it < it_e; it += 2) {
-      compute(std::true_type{}, it, qb0, db0, rv0, qb1, db1, rv1);
+      compute(it, qb0, db0, rv0, qb1, db1, rv1);
       wait_all_and_barrier();
       if (it + 1 >= it_e) break;
-      compute(std::true_type{}, it + 1, qb1, db1, rv1, qb0, db0, rv0);
+      compute(it + 1, qb1, db1, rv1, qb0, db0, rv0);
       wait_all_and_barrier();
     }
-  } else {
-    // One Q and one dO buffer (two of each do not fit at D = 512). Each is
-    // refilled as soon as every wave is done with it, so its load has part of
-    // a tile's work to land instead of stalling the next tile:
-    //   dV pass: Q(t) feeds only the S MFMAs and dO(t) only the dV MFMAs, so
-    //     Q(t+1) loads after the S exchange and dO(t+1) after the dV MFMAs.
-    //   dK pass: Q(t) feeds S and dK, dO(t) only dP; the two buffers swap roles
-    //     every tile: Q(t+1) loads into dO(t)'s buffer after the exchanges,
-    //     dO(t+1) into Q(t)'s buffer after the dK MFMAs.
-    // A wave's loads complete in order, so "Q landed, dO may still be in
-    // flight" is vmcnt(NJ): at most one tile's worth of this wave's loads
-    // outstanding (wave 0's extra lse/Delta load rides with the Q tile).
-    constexpr int NJ = LD::NJ;
-    auto issue_q = [&](int it, bool more, E* dst, float* rvd) {
-      const E *qs, *ds;
-      int q0n;
-      tile_src(it, qs, ds, q0n);
-      ldq.issue(dst, qs, more ? Lq - q0n : 0, w);
-      if (w == 0) load_rows(it, rvd);
-    };
-    auto issue_do = [&](int it, bool more, E* dst) {
-      const E *qs, *ds;
-      int q0n;
-      tile_src(it, qs, ds, q0n);
-      ldd.issue(dst, ds, more ? Lq - q0n : 0, w);
-    };
-    // S, then (dK pass) dP once dO has landed; operand reads pipelined by hand
-    auto sdp = [&](const E* Qc, const E* dOc, f32x16& s_acc, f32x16& dp_acc) {
-      constexpr int AH = KV_AHEAD;
-      ex8 ra[AH], rb[AH];
-      s_acc = zero16();
-      dp_acc = zero16();
-#pragma unroll
-      for (int k = 0; k < AH; k++) {
-        ra[k] = op_direct<D, E>(Qc, la, dw0 + 16 * k, 0);
-        rb[k] = op_direct<D, E>(ks, la, dw0 + 16 * k, 32 * kwi);
-      }
-#pragma unroll
-      for (int k = 0; k < NKS; k++) {
-        s_acc = mfma(ra[k % AH], rb[k % AH], s_acc);
-        if (k + AH < NKS) {
-          ra[k % AH] = op_direct<D, E>(Qc, la, dw0 + 16 * (k + AH), 0);
-          rb[k % AH] = op_direct<D, E>(ks, la, dw0 + 16 * (k + AH), 32 * kwi);
-        }
-      }
-      if constexpr (WANT_DK) {
-        wait_vm_and_barrier<0>();  // dO(t) in every wave's part of the buffer
-#pragma unroll
-        for (int k = 0; k < AH; k++) ra[k] = op_direct<D, E>(dOc, la, dw0 + 16 * k, 0);
-#pragma unroll
-        for (int k = 0; k < NKS; k++) {
-          dp_acc = mfma(ra[k % AH], vreg[k], dp_acc);
-          if (k + AH < NKS) ra[k % AH] = op_direct<D, E>(dOc, la, dw0 + 16 * (k + AH), 0);
-        }
-      }
-    };
-    auto tile = [&](int it, E* Qb, E* Db, float* rvc, float* rvn) {
-      const int q0 = q0_of(it);
-      bool active, full;
-      tile_tests(q0, active, full);
-      const bool more = it + 1 < total;
-      const int itn = more ? it + 1 : it;
-      wait_vm_and_barrier<NJ>();  // Q(t) and lse/Delta(t) landed (dO(t) may not have)
-      f32x16 s_acc, dp_acc;
-      sdp(Qb, Db, s_acc, dp_acc);
-      kv_exchange_add(s_acc, xbuf, w, lane);
-      if constexpr (WANT_DK) kv_exchange_add(dp_acc, xbuf, w, lane);
-      // dV pass: Q(t)'s buffer is free; dK pass: dO(t)'s buffer is free
-      issue_q(itn, more, WANT_DK ? Db : Qb, rvn);
-      if constexpr (!WANT_DK) wait_vm_and_barrier<NJ>();  // dO(t) landed (Q(t+1) may not have)
-      if (active) form_and_update(q0, full, rvc, s_acc, dp_acc, Qb, Db);
-      lds_barrier();  // every wave is done with the buffer refilled next
-      issue_do(itn, more, WANT_DK ? Qb : Db);
-    };
-    issue_q(0, true, qb0, rv0);
-    issue_do(0, true, db0);
-    for (int it = 0; it < total; it += 2) {
-      tile(it, qb0, db0, rv0, rv1);
-      if (it + 1 >= total) break;
-      if constexpr (WANT_DK) tile(it + 1, db0, qb0, rv1, rv0);
-      else tile(it + 1, qb0, db0, rv1, rv0);
-    }
-    wait_all_and_barrier();  // (the last no-op loads)
   }
 
   // dK = scale * dS^T Q, dV = P^T dO; C tile: column = head-dim index, rows = keys
@@ -473,7 +343,7 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     float* pv = pk + (size_t)nseg * slice;
 #pragma unroll
     for (int d = 0; d < NDB; d++) {
-      const int col = dw0 + 32 * d + (lane & 31);
+      const int col = 32 * d + (lane & 31);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int key = kb0 + c_row(i, hh);
@@ -489,13 +359,13 @@ kv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   E* dVg = dV + b * st.dv.b + g * st.dv.h;
 #pragma unroll
   for (int d = 0; d < NDB; d++) {
-    const int col = dw0 + 32 * d + (lane & 31);
+    const int col = 32 * d + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
       const int key = kb0 + c_row(i, hh);
       if (key < Lk) {
-        if constexpr (WANT_DK) dKg[(long long)key * st.dk.l + col] = (E)(dkacc[d][i] * scale);
-        if constexpr (WANT_DV) dVg[(long long)key * st.dv.l + col] = (E)dvacc[d][i];
+        dKg[(long long)key * st.dk.l + col] = (E)(dkacc[d][i] * scale);
+        dVg[(long long)key * st.dv.l + col] = (E)dvacc[d][i];
       }
     }
   }
@@ -522,11 +392,11 @@ __global__ void __launch_bounds__(256) kv_reduce_kernel(const float* __restrict_
   *(ex8*)((blockIdx.y == 0 ? dK : dV) + i) = v;
 }
 
-// Shares of the split for this shape, or 1 (no split): only for the dense
-// one-pass kernel, when the key blocks alone fill fewer than 256 workgroups.
+// Shares of the split for this shape, or 1 (no split): only for dense calls
+// whose key blocks alone fill fewer than 256 workgroups.
 template <int D>
 int kv_split_shares(int B, int Hq, int group, int Lq, int Lk, bool dense) {
-  if (D > 256 || !dense || Lq == 0) return 1;
+  if (!dense || Lq == 0) return 1;
   const long nwg = (long)((Lk + KvCfg<D>::BKT - 1) / KvCfg<D>::BKT) * (Hq / group) * B;
   int n = 1;
   while (n < 8 && nwg * n < 256) n *= 2;
@@ -550,23 +420,16 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
                        Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st, (float*)nullptr, 1);
     return hipGetLastError();
   };
-  if constexpr (D > 256) {  // two passes: each wave's accumulators then fit the register file
-    const hipError_t e = run(kv_kernel<D, KV_DV, E, true, false>, kv_kernel<D, KV_DV, E, false, false>);
-    if (e != hipSuccess) return e;
-    return run(kv_kernel<D, KV_DK, E, true, false>, kv_kernel<D, KV_DK, E, false, false>);
-  } else {
-    if (nseg <= 1 || part == nullptr || !dense)
-      return run(kv_kernel<D, KV_BOTH, E, true, false>, kv_kernel<D, KV_BOTH, E, false, false>);
-    hipLaunchKernelGGL((kv_kernel<D, KV_BOTH, E, true, true>), dim3((unsigned)(nwg * nseg)), dim3(256), 0, stream,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
-                       Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st, part, nseg);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t n = (size_t)B * (Hq / group) * Lk * D;
-    hipLaunchKernelGGL(kv_reduce_kernel<E>, dim3((unsigned)((n / 8 + 255) / 256), 2), dim3(256), 0, stream,
-                       (const float*)part, (E*)dk, (E*)dv, n, nseg);
-    return hipGetLastError();
-  }
+  if (nseg <= 1 || part == nullptr || !dense) return run(kv_kernel<D, E, true, false>, kv_kernel<D, E, false, false>);
+  hipLaunchKernelGGL((kv_kernel<D, E, true, true>), dim3((unsigned)(nwg * nseg)), dim3(256), 0, stream,
+                     (const E*)q, (const E*)k, (const E*)v, (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group,
+                     Lq, Lk, dlo, dhi, cut, scale, scale * kLog2e, st, part, nseg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)B * (Hq / group) * Lk * D;
+  hipLaunchKernelGGL(kv_reduce_kernel<E>, dim3((unsigned)((n / 8 + 255) / 256), 2), dim3(256), 0, stream,
+                     (const float*)part, (E*)dk, (E*)dv, n, nseg);
+  return hipGetLastError();
 }
 
 #define SDPA_INST_KV(D, E)                                                                                \
@@ -576,14 +439,11 @@ hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO
 SDPA_INST_KV(64, bf16)
 SDPA_INST_KV(128, bf16)
 SDPA_INST_KV(256, bf16)
-SDPA_INST_KV(512, bf16)
 SDPA_INST_KV(64, f16)
 SDPA_INST_KV(128, f16)
 SDPA_INST_KV(256, f16)
-SDPA_INST_KV(512, f16)
 template int kv_split_shares<64>(int, int, int, int, int, bool);
 template int kv_split_shares<128>(int, int, int, int, int, bool);
 template int kv_split_shares<256>(int, int, int, int, int, bool);
-template int kv_split_shares<512>(int, int, int, int, int, bool);
 
 }  // namespace sdpa

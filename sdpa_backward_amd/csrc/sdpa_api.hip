@@ -54,17 +54,20 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  // 16-key waves (v_mfma_f32_16x16x32): at D = 512 always (the 32-key kernel
-  // needs two passes there), at D = 256 for dense calls whose key blocks fill
-  // the GPU (two workgroups per CU; measured faster than the 32-key kernel
-  // there); otherwise 32-key waves. The choice depends on the shape and
-  // layout only, never on the workspace given.
-  const bool k16 = D == 512 || (D == 256 && wide);
-  if (k16)
+  // 16-key waves (v_mfma_f32_16x16x32): at D = 512 always (32-key waves would
+  // not fit their accumulators in registers there), at D = 256 for dense calls
+  // whose key blocks fill the GPU (two workgroups per CU; measured faster than
+  // the 32-key kernel there); otherwise 32-key waves. The choice depends on
+  // the shape and layout only, never on the workspace given.
+  if constexpr (D == 512) {
     e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
-  else
-    e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part, nseg,
-                        stream);
+  } else {
+    if (D == 256 && wide)
+      e = launch_kv16<256, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
+    else
+      e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part,
+                          nseg, stream);
+  }
   if (e != hipSuccess) return e;
   if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;

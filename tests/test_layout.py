@@ -104,6 +104,36 @@ def test_autograd_matches_oracle():
         assert e <= TOL["bf16"], (n, e)
 
 
+@pytest.mark.parametrize("loss", ["sum", "row_weighted", "head_summed"])
+def test_autograd_expanded_upstream_gradient(loss):
+    """Losses whose gradient reaches attention() as an expanded view: o.sum()
+    gives dO strides (0, 0, 0, 0), a row-weighted sum over D a zero stride
+    along D, a sum over heads a zero head stride. The backward must give the
+    oracle's gradients for the dO those views stand for."""
+    w = Workload(f"autograd_{loss}", 2, 4, 2, 300, 256, "bf16", MASK_WINDOW, 90, seed=9710)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(DEV).requires_grad_() for n in ("q", "k", "v"))
+    o = attention(q, k, v, w.mask, w.window)
+    g = torch.Generator().manual_seed(9711)
+    if loss == "sum":
+        do = torch.ones(o.shape, dtype=torch.float64)
+        o.sum().backward()
+    elif loss == "row_weighted":
+        wr = torch.randn(w.L, generator=g).to(torch.bfloat16)
+        (o.sum(-1) * wr.to(DEV)).sum().backward()
+        do = wr.double()[:, None].expand(o.shape)
+    else:
+        wh = torch.randn(w.L, w.D, generator=g).to(torch.bfloat16)
+        (o.sum(1) * wh.to(DEV)).sum().backward()
+        do = wh.double()[None, None].expand(o.shape)
+    ref = oracle.sdpa_fwd_bwd(inp["q"], inp["k"], inp["v"], do.contiguous().numpy(), w.scale, w.mask, w.window)
+    errs = {n: rel_fro(_np(t), ref[n]) for n, t in (("dQ", q.grad), ("dK", k.grad), ("dV", v.grad))}
+    print("autograd", loss, {k: f"{x:.2e}" for k, x in errs.items()}, flush=True)
+    # the expanded dO holds exact values (ones, or the bf16 weights times ones)
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
+
+
 class _OracleAttention(torch.autograd.Function):
     """fp64 CPU attention through the oracle (reference side of the layer test)."""
 

@@ -2,53 +2,63 @@
 
 The library allocates nothing: outputs and the backward workspace are torch
 tensors, so torch's peak-allocation counter sees every byte. Above the inputs,
-one fwd+bwd holds exactly O, lse, dQ, dK, dV and the workspace (one fp32 row
-statistic per query row); the test checks that sum and that doubling L doubles
-it, for the sliding-window geometry (window 1024) and the causal global one.
-The shapes are large enough (at least 256 key blocks, or D = 512) that the
-small-problem dK/dV split, whose fp32 shares are linear in L too but sized by
-the block count, stays off.
+one fwd+bwd holds exactly O, lse, dQ, dK, dV and the backward workspace; the
+test checks that sum and that doubling L doubles it, at the two attention
+layer shapes the pages measure (page "Lab 028 lab detail: Off NVIDIA, you fix
+the platform yourself", section "Build log, 2026-10-21", peak-memory table:
+32 q-heads with 16 kv heads at D = 256 under a 1024-key causal window, and the
+causal D = 512 layer, here with the benchmark's 16 q-heads and 4 kv heads), at
+the pages' lengths up to 32,768 tokens. Values do not matter for memory, so
+the inputs are drawn on the GPU. Every length has at least 256 key blocks per
+call (or D = 512), so the small-problem dK/dV split, whose fp32 shares are
+linear in L too but sized by the block count, stays off.
 """
 import pytest
 import torch
 
 from sdpa_backward_amd import bwd_workspace_bytes, sdpa_bwd, sdpa_fwd_lse
-from workloads import MASK_CAUSAL, MASK_WINDOW, Workload, make_inputs
+from workloads import MASK_CAUSAL, MASK_WINDOW
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
+GEOMS = {
+    # name: (Hq, Hkv, D, mask, window, lengths)
+    "window1024_h32kv16_D256": (32, 16, 256, MASK_WINDOW, 1024, (4096, 8192, 16384, 32768)),
+    "causal_h16kv4_D512": (16, 4, 512, MASK_CAUSAL, 0, (2048, 4096, 8192, 16384, 32768)),
+}
 
-def peak_above_inputs(w):
-    inp = {n: x.to(DEV) for n, x in make_inputs(w).items()}
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+
+def peak_above_inputs(Hq, Hkv, D, mask, window, L, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    mk = lambda H: torch.randn(1, H, L, D, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v, do = mk(Hq), mk(Hkv), mk(Hkv), mk(Hq)
+    scale = D ** -0.5
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated(DEV)
     torch.cuda.reset_peak_memory_stats(DEV)
-    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale)
-    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale)
+    o, lse = sdpa_fwd_lse(q, k, v, mask, window, scale)
+    dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, mask, window, scale)
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(DEV) - base
     outs = sum(t.numel() * t.element_size() for t in (o, lse, dq, dk, dv))
-    expect = outs + bwd_workspace_bytes(w.B, w.Hq, w.Hq // w.Hkv, w.L, w.Lkv, w.D, q.dtype)
-    del inp, q, k, v, do, o, lse, dq, dk, dv
+    ws = bwd_workspace_bytes(1, Hq, Hq // Hkv, L, L, D, q.dtype)
+    finite = all(bool(torch.isfinite(t).all()) for t in (o, dq, dk, dv))
+    del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
-    return peak, expect
+    return peak, outs + ws, ws, finite
 
 
-@pytest.mark.parametrize("geom", ["window1024_D256", "causal_D512"])
+@pytest.mark.parametrize("geom", list(GEOMS))
 def test_peak_memory_is_linear_in_L(geom):
-    if geom == "window1024_D256":
-        make = lambda L: Workload(f"mem_w_{L}", 1, 16, 8, L, 256, "bf16", MASK_WINDOW, 1024, seed=7400)
-        Ls = (4096, 8192, 16384, 32768)
-    else:
-        make = lambda L: Workload(f"mem_c_{L}", 1, 4, 1, L, 512, "bf16", MASK_CAUSAL, 0, seed=7401)
-        Ls = (2048, 4096, 8192, 16384)
+    Hq, Hkv, D, mask, window, Ls = GEOMS[geom]
     peaks = []
-    for L in Ls:
-        peak, expect = peak_above_inputs(make(L))
-        print(geom, L, peak, expect, flush=True)
+    for i, L in enumerate(Ls):
+        peak, expect, ws, finite = peak_above_inputs(Hq, Hkv, D, mask, window, L, 7400 + i)
+        print(f"{geom} L={L}: peak above inputs {peak / 1e9:.3f} GB (outputs + workspace {expect / 1e9:.3f} GB, "
+              f"workspace {ws / 1e9:.3f} GB)", flush=True)
+        assert finite, L
         # torch rounds each allocation up to 512 bytes
         assert expect <= peak <= expect + 8 * 512, (L, peak, expect)
         peaks.append(peak)

@@ -7,9 +7,10 @@ Frobenius error <= 1e-2 (bf16) / 2e-3 (fp16) / 1e-5 (fp32) on O, dQ, dK, dV,
 and lse max-abs error <= 1e-4. The fp16 gate keeps the bf16 gate's ratio to
 the unit roundoff: 1e-2 is about 2.6 u for bf16 (u = 2^-8), and 2.6 u for
 fp16 (u = 2^-11) is 1.3e-3, rounded up to 2e-3; P, dS and the outputs are
-rounded to the input type, everything else stays fp32. At the three large workloads the oracle computes
-sampled rows (O, lse, dQ) and sampled keys (dK, dV) one by one, and the GPU
-run uses the same launch configuration as the benchmark.
+rounded to the input type, everything else stays fp32. At the three large
+workloads the oracle computes one whole kv group (every row of its q-heads,
+every key of its kv head) and samples of every other head, and the GPU run
+uses the same launch configuration as the benchmark.
 """
 import math
 
@@ -132,6 +133,29 @@ RISING = [
 ]
 
 
+def _rounded_path_grads(w, inp, ref):
+    """dQ and dK from the oracle's arithmetic with only the roundings that any
+    attention on 16-bit matrix-core operands makes before those products: the
+    forward's O formed from P rounded to the input type and itself rounded to
+    it, Delta_i = <dO_i, O_i> from that O, and dS rounded to the input type as
+    an operand. Everything else stays fp64. Used to size the gate of a case
+    that amplifies these roundings, never as a reference."""
+    rnd = lambda x: torch.from_numpy(x).float().to(w.torch_dtype).double().numpy()
+    q, k, v, do = (_np(inp[n]) for n in ("q", "k", "v", "do"))
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    rows = np.arange(w.L)
+    ok = oracle.allowed_block(rows, w.L, w.Lkv, w.mask, w.window)
+    for h in range(w.Hq):
+        g = h // w.group
+        S = w.scale * (q[0, h] @ k[0, g].T)
+        P = np.where(ok, np.exp(np.where(ok, S, 0.0) - ref["lse"][0, h][:, None]), 0.0)
+        delta = np.sum(do[0, h] * rnd(rnd(P) @ v[0, g]), axis=1)
+        dS = rnd(P * (do[0, h] @ v[0, g].T - delta[:, None]))
+        dq[0, h] = w.scale * (dS @ k[0, g])
+        dk[0, g] += w.scale * (dS.T @ q[0, h])
+    return dq, dk
+
+
 @pytest.mark.parametrize("case", RISING, ids=[c[0] for c in RISING])
 def test_rising_scores_force_rescales(case):
     """Scores that grow along the key axis by about 8 (natural log units) per
@@ -139,11 +163,11 @@ def test_rising_scores_force_rescales(case):
     almost every key tile, so the accumulator rescale runs again and again.
     Every query shares a direction u; key j carries (j / L) * alpha * u.
 
-    O and lse (what the rescale touches) keep the usual gates. dQ gets 6e-2:
-    with u in every key, dQ_i = sum_j dS_ij k_j cancels heavily, and rounding
-    dS and O (through Delta) to bf16, as every bf16 MFMA path must, already
-    leaves 2.3e-2 against the fp64 oracle in the D=256 case (oracle arithmetic
-    with only those two roundings added)."""
+    O, lse and dV (what the rescale touches) keep the usual gates. With u in
+    every key, dQ_i = scale sum_j dS_ij k_j (and dK) cancel heavily, so the
+    bf16 rounding of dS and of O (through Delta) is amplified: their gate is
+    the error that those roundings alone leave in an otherwise exact
+    computation (measured here on the same inputs), plus the usual 1e-2."""
     name, Hq, Hkv, L, D, mask, window = case
     w = Workload(name, 1, Hq, Hkv, L, D, "bf16", mask, window, seed=7300 + D)
     g = torch.Generator().manual_seed(w.seed)
@@ -157,25 +181,27 @@ def test_rising_scores_force_rescales(case):
         "v": torch.randn(1, Hkv, L, D, generator=g).to(torch.bfloat16),
         "do": torch.randn(1, Hq, L, D, generator=g).to(torch.bfloat16),
     }
-    check_full(w, run(w, inp), oracle_full(w, inp), tol={"O": 1e-2, "dQ": 6e-2, "dK": 1e-2, "dV": 1e-2})
+    ref = oracle_full(w, inp)
+    dq_r, dk_r = _rounded_path_grads(w, inp, ref)
+    floor = {"dQ": rel_fro(dq_r, ref["dQ"]), "dK": rel_fro(dk_r, ref["dK"])}
+    print(name, "error of the rounded-operand arithmetic:", {k: f"{x:.2e}" for k, x in floor.items()}, flush=True)
+    tol = {"O": 1e-2, "dV": 1e-2, "dQ": floor["dQ"] + 1e-2, "dK": floor["dK"] + 1e-2}
+    check_full(w, run(w, inp), ref, tol=tol)
 
 
-def _sample_rows(L, rng, n=24):
+def _sample_rows(L, rng, n):
     fixed = [0, 1, 31, 32, 63, 64, 127, 128, 1023, 1024, L // 2, L - 2, L - 1]
     rows = set(r for r in fixed if 0 <= r < L)
     rows.update(int(x) for x in rng.integers(0, L, n))
     return np.array(sorted(rows))
 
 
-def _sample_keys(w, rng):
+def _sample_key_pair(w, rng):
+    """Two adjacent keys (the rows that see them, at most window + 1 or the causal
+    tail, stay cheap for the oracle)."""
     L = w.L
-    if w.mask == MASK_CAUSAL:  # a causal key is seen by every later row: stay near the end
-        cand = [L - 1, L - 2, L - 64, L - 65, L - 129, L - 700]
-        cand += [int(x) for x in rng.integers(L - 1024, L, 4)]
-    else:
-        cand = [0, 1, 63, 64, 127, 128, 1023, 1024, L // 2, L - 1025, L - 2, L - 1]
-        cand += [int(x) for x in rng.integers(0, L, 4)]
-    return np.array(sorted(set(c for c in cand if 0 <= c < L)))
+    j = int(rng.integers(L - 1024, L - 1)) if w.mask == MASK_CAUSAL else int(rng.integers(0, L - 1))
+    return np.array([j, j + 1])
 
 
 def _poisoned_outputs(w):
@@ -200,38 +226,67 @@ def _check_poison(w, bufs, views):
 
 
 @pytest.mark.parametrize("name", LARGE)
-def test_large_workloads_sampled(name):
+def test_large_workloads(name):
+    """The three large workloads in the benchmark's launch configuration.
+
+    * One whole kv group (the last) against the oracle: every row of its
+      q-heads for O, lse and dQ, every key of its kv head for dK and dV, each
+      gated as a per-tensor relative Frobenius error over that group.
+    * Every other head too, on samples: rows of every q-head (O, lse, dQ) and
+      two adjacent keys of every kv head (dK, dV, from every row and q-head
+      that sees them), pooled into one relative error per tensor.
+    * Whole-tensor properties: NaN-poisoned outputs are all written, canary
+      tails untouched, and the column sums of dV and dK match their closed
+      forms (sum_j dV_j = sum of the group's dO rows, sum_j dK_j = 0).
+    """
     w = BY_NAME[name]
     inp = make_inputs(w)
     bufs, views = _poisoned_outputs(w)
     gpu = run(w, inp, out=[views[n] for n in ("O", "lse", "dQ", "dK", "dV")])
     _check_poison(w, bufs, views)
-    rng = np.random.default_rng(w.seed)
     tol = TOL[w.dtype]
+
+    g = w.Hkv - 1
+    hs = slice(g * w.group, (g + 1) * w.group)
+    ref = oracle.sdpa_fwd_bwd(inp["q"][:, hs], inp["k"][:, g:g + 1], inp["v"][:, g:g + 1], inp["do"][:, hs],
+                              w.scale, w.mask, w.window)
+    errs = {n: rel_fro(_np(gpu[n][:, hs]), ref[n]) for n in ("O", "dQ")}
+    errs.update({n: rel_fro(_np(gpu[n][:, g:g + 1]), ref[n]) for n in ("dK", "dV")})
+    errs["lse"] = float(np.max(np.abs(_np(gpu["lse"][:, hs]) - ref["lse"])))
+    print(w.name, f"kv group {g} (q-heads {hs.start}..{hs.stop - 1}), whole:",
+          {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n in ("O", "dQ", "dK", "dV"):
+        assert errs[n] <= tol, ("group", n, errs[n])
+    assert errs["lse"] <= LSE_TOL, ("group", errs["lse"])
+
+    rng = np.random.default_rng(w.seed)
     got = {n: [] for n in ("O", "lse", "dQ", "dK", "dV")}
-    ref = {n: [] for n in got}
-    for h in sorted({0, w.Hq // 2 + 1, w.Hq - 1}):
-        rows = _sample_rows(w.L, rng)
+    want = {n: [] for n in got}
+    for h in range(w.Hq):
+        if hs.start <= h < hs.stop:
+            continue
+        rows = _sample_rows(w.L, rng, 6)
         r = oracle.sampled_rows(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window, 0, h, rows)
         for n in ("O", "lse", "dQ"):
             got[n].append(_np(gpu[n][0, h][torch.as_tensor(rows, device=DEV)]))
-            ref[n].append(r[n])
-    for g in sorted({0, w.Hkv - 1}):
-        keys = _sample_keys(w, rng)
-        r = oracle.sampled_keys(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window, 0, g, keys)
+            want[n].append(r[n])
+    for gg in range(w.Hkv - 1):
+        keys = _sample_key_pair(w, rng)
+        r = oracle.sampled_keys(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window, 0, gg, keys)
         for n in ("dK", "dV"):
-            got[n].append(_np(gpu[n][0, g][torch.as_tensor(keys, device=DEV)]))
-            ref[n].append(r[n])
-    errs = {}
+            got[n].append(_np(gpu[n][0, gg][torch.as_tensor(keys, device=DEV)]))
+            want[n].append(r[n])
+    serr = {}
     for n in got:
-        a, b = np.concatenate(got[n]), np.concatenate(ref[n])
-        errs[n] = float(np.max(np.abs(a - b))) if n == "lse" else rel_fro(a, b)
-    print(w.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+        a, b = np.concatenate(got[n]), np.concatenate(want[n])
+        serr[n] = float(np.max(np.abs(a - b))) if n == "lse" else rel_fro(a, b)
+    print(w.name, "other heads, sampled:", {k: f"{v:.2e}" for k, v in serr.items()}, flush=True)
     for n in ("O", "dQ", "dK", "dV"):
-        assert errs[n] <= tol, (n, errs[n])
-    assert errs["lse"] <= LSE_TOL
-    # a property of the whole tensors: every softmax row sums to one, so
-    # sum_j dV_{g,j} = sum over the group's heads and rows of dO
+        assert serr[n] <= tol, ("sampled", n, serr[n])
+    assert serr["lse"] <= LSE_TOL, ("sampled", serr["lse"])
+
+    # every softmax row sums to one, so sum_j dV_{g,j} = sum over the group's
+    # heads and rows of dO
     dv_sum = gpu["dV"].double().sum(dim=2)
     do_sum = inp["do"].to(DEV).double().view(w.B, w.Hkv, w.group, w.L, w.D).sum(dim=(2, 3))
     rel = (torch.linalg.norm(dv_sum - do_sum) / torch.linalg.norm(do_sum)).item()
