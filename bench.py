@@ -4,9 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = the whole hot path on one batch: sdpa_fwd_lse (forward kernel),
-then sdpa_bwd (query-stationary dQ kernel, which also writes Delta, then the
-key-stationary dK/dV kernel), with inputs resident in device memory before the
-timed region starts. Default workload: the causal +
+then sdpa_bwd, with inputs resident in device memory before the timed region
+starts. The backward runs three passes: with a bounded (windowed) band at
+D = 256, the Delta pass, the key-stationary dK/dV pass that also writes dS for
+the band, and dQ = scale dS K from it; otherwise the query-stationary dQ pass
+(recomputing S and dP, also forming Delta) and the dK/dV pass. Default workload: the causal +
 sliding-window (1024) layer at L = 16384, D = 256, 32 query / 16 kv heads.
 Prints one JSON line on stdout; diagnostics go to stderr.
 
@@ -43,6 +45,16 @@ def dkdv_kernel(w):
     if w.D == 512 or (w.D == 256 and blocks >= 256):
         return f"kv16_kernel<{w.D}>"
     return f"kv_kernel<{w.D}>" + (" + share reduce" if blocks < 256 else "")
+
+
+def uses_band(w, sdpa, dtype):
+    """Whether the backward keeps dS for the band on this workload: the library does so for the
+    16-key dK/dV kernel at D = 256 when its full workspace (the size the bench gives) exceeds the
+    Delta rows (at D = 256 the 16-key kernel never splits)."""
+    if not (w.D == 256 and dkdv_kernel(w).startswith("kv16")):
+        return False
+    full = sdpa.bwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, dtype, w.mask, w.window)
+    return full > sdpa.workspace_bytes(w.B, w.Hq, w.L, w.D, dtype)
 
 
 def tile_config(w):
@@ -237,22 +249,21 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(1, sdpa.bwd_workspace_bytes(w.B, w.Hq, w.Hq // w.Hkv, w.L, w.Lkv, w.D, q.dtype)),
-                     dtype=torch.uint8, device=dev)
+    ws_bytes = sdpa.bwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, q.dtype, w.mask, w.window)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    band = uses_band(w, sdpa, q.dtype)
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = HipEvents()
+    # per step: [0] forward start, [1] forward end = backward start, [2] after the
+    # backward's first pass, [3] after the dK/dV pass, [4] backward end
     evs = [[ev.create() for _ in range(5)] for _ in range(a.steps)]
 
     def step(e=None):
         if e:
             ev.record(e[0], stream)
         sdpa.sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale, out=o, lse=lse)
-        if e:
-            ev.record(e[1], stream)
         sdpa.sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale, workspace=ws, out=(dq, dk, dv),
-                      main_events=(e[2], e[3]) if e else None)
-        if e:
-            ev.record(e[4], stream)
+                      events=e[1:] if e else None)
 
     for _ in range(a.warmup):
         step()
@@ -289,7 +300,9 @@ def main():
 
     fwd_ms = [ev.ms(e[0], e[1]) for e in evs]
     bwd_ms = [ev.ms(e[1], e[4]) for e in evs]
+    p1_ms = [ev.ms(e[1], e[2]) for e in evs]
     main_ms = [ev.ms(e[2], e[3]) for e in evs]
+    p3_ms = [ev.ms(e[3], e[4]) for e in evs]
     ms_per_step = (t1 - t0) * 1e3 / a.steps
     N = allowed_pairs(w)
     fwd_flop, bwd_flop = 4 * w.D * N, 10 * w.D * N
@@ -298,6 +311,32 @@ def main():
     achieved = kv_flop / (statistics.mean(main_ms) * 1e-3) / 1e12
     traffic = measured_traffic(w)
     med = statistics.median
+    esz = 4 if w.dtype == "f32" else 2
+    q_bytes = w.B * w.Hq * w.L * w.D * esz
+
+    def mfma_entry(name, flop, what, ms_list):
+        t = statistics.mean(ms_list)
+        return {"kernel": name, "bound": "mfma", "algorithmic": what, "avg_launch_ms": round(t, 4),
+                "achieved": round(flop / (t * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                "frac": round(flop / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    def hbm_entry(name, nbytes, what, ms_list):
+        t = statistics.mean(ms_list)
+        return {"kernel": name, "bound": "hbm", "algorithmic": what, "avg_launch_ms": round(t, 4),
+                "achieved": round(nbytes / (t * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "frac": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    kernels = [mfma_entry(f"qs_kernel<{w.D}, forward>", fwd_flop, "4*D FLOP per allowed pair (S, PV)", fwd_ms)]
+    if band:
+        kernels.append(hbm_entry("delta_kernel", 2 * q_bytes, "O and dO read once", p1_ms))
+        kernels.append(mfma_entry(dkdv_kernel(w) + " writing dS", kv_flop,
+                                  "8*D FLOP per allowed pair (S, dP, dV, dK)", main_ms))
+        kernels.append(mfma_entry(f"dsq_kernel<{w.D}>", 2 * w.D * N, "2*D FLOP per allowed pair (dS K)", p3_ms))
+    else:
+        kernels.append(mfma_entry(f"qs_kernel<{w.D}, dQ>", 6 * w.D * N,
+                                  "6*D FLOP per allowed pair (S, dP recomputed; dS K)", p1_ms))
+        kernels.append(mfma_entry(dkdv_kernel(w), kv_flop, "8*D FLOP per allowed pair (S, dP, dV, dK)", main_ms))
+    bwd_useful = bwd_flop / (statistics.mean(bwd_ms) * 1e-3) / 1e12
 
     result = {
         "metric": METRIC,
@@ -321,11 +360,13 @@ def main():
             "fwd": {"ms_median": round(med(fwd_ms), 4), "ms_min": round(min(fwd_ms), 4),
                     "tflops": round(fwd_flop / med(fwd_ms) / 1e9, 1)},
             "bwd": {"ms_median": round(med(bwd_ms), 4), "ms_min": round(min(bwd_ms), 4),
-                    "tflops": round(bwd_flop / med(bwd_ms) / 1e9, 1)},
+                    "tflops": round(bwd_flop / med(bwd_ms) / 1e9, 1),
+                    "plan": "Delta pass, dK/dV pass writing dS for the band, dQ = scale dS K" if band else
+                            "dQ pass (recomputes S and dP, forms Delta), dK/dV pass"},
+            "bwd_pass1": {"what": "Delta" if band else "dQ (6*D*N)", "ms_median": round(med(p1_ms), 4)},
             "bwd_dkdv_kernel": {"ms_median": round(med(main_ms), 4), "ms_min": round(min(main_ms), 4),
                                 "tflops_8DN": round(kv_flop / med(main_ms) / 1e9, 1)},
-            "bwd_dq_pass": {"ms_median": round(med(bwd_ms) - med(main_ms), 4),
-                            "tflops_6DN": round(6 * w.D * N / (med(bwd_ms) - med(main_ms)) / 1e9, 1)},
+            "bwd_pass3": {"what": "dQ from dS (2*D*N)" if band else "none", "ms_median": round(med(p3_ms), 4)},
             "fwd_plus_bwd_wall": {"ms": round(ms_per_step, 4)},
         },
         "cold": None if not cold else {
@@ -346,6 +387,10 @@ def main():
             "algorithmic_flop_per_launch": kv_flop,
             "algorithmic_unit": "8*D FLOP per allowed (query, key) pair (S, dP, dV, dK)",
             "avg_launch_ms": round(statistics.mean(main_ms), 4),
+            "kernels": kernels,
+            "backward_useful": {"flop": bwd_flop, "algorithmic": "10*D FLOP per allowed pair",
+                                "avg_ms": round(statistics.mean(bwd_ms), 4), "achieved": round(bwd_useful, 1),
+                                "frac": round(bwd_useful / BF16_PEAK_TFLOPS, 4), "target_frac": 0.5},
         },
     }
     result["env"] = {"device": torch.cuda.get_device_name(dev), "torch": torch.__version__,

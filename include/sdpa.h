@@ -177,19 +177,31 @@ int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float*
  * invalid arguments. */
 size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, int32_t dtype);
 
-/* Bytes of workspace with which sdpa_bwd / sdpa_bwd_ex may also split the
- * dK/dV pass of a small problem: the bytes above, plus, for 16-bit inputs
- * with D <= 256 whose key blocks (128 keys per kv head and batch) number
- * fewer than 256, fp32 shares of dK and dV (2 * n * B * (Hq/group) * Lk * D
- * floats, n in {2, 4, 8}) that the query range of each key block is split
- * over, summed afterwards in a fixed order. The split applies to calls with
- * contiguous tensors and no cut, and only when the workspace given holds it;
- * with sdpa_bwd_workspace_bytes(...) bytes the results are the same up to
- * fp32 summation order. Returns 0 for empty shapes and invalid arguments.
- * (The split gives small problems enough workgroups for every compute unit;
- * it is a throughput choice, not part of the pages' method.) */
+/* Bytes of workspace with which sdpa_bwd / sdpa_bwd_ex run their fastest
+ * plan for this shape and mask (mask and window as for sdpa_fwd_lse): the
+ * bytes above, plus the larger of
+ *  - the small-problem split: for 16-bit inputs with D <= 256 whose key
+ *    blocks (128 keys per kv head and batch) number fewer than 256, fp32
+ *    shares of dK and dV (2 * n * B * (Hq/group) * Lk * D floats, n in
+ *    {2, 4, 8}) that the query range of each key block is split over, summed
+ *    afterwards in a fixed order;
+ *  - the dS band buffer: for 16-bit inputs at D = 256 with at least 256 key
+ *    blocks, when every block of 128 query rows sees keys in at most
+ *    nkb <= 32 tiles of 64 (a band at most 8 D = 2048 keys wide: sliding
+ *    windows up to about 1900 keys), B * Hq * ceil(Lq / 128) * nkb tiles of
+ *    64 x 128 16-bit values. The dK/dV pass then also writes dS for the band
+ *    and dQ = scale * dS K is formed from it, instead of a dQ pass that
+ *    recomputes the scores (page "Lab 028 lab detail: Off NVIDIA, you fix the
+ *    platform yourself", section "What I changed, in plain terms", item 5(a):
+ *    dQ summed over the key tiles). At most 8 times the bytes of q, and
+ *    linear in Lq at a fixed window.
+ * Both apply to calls with contiguous tensors and no cut, and only when the
+ * workspace given holds them; with sdpa_bwd_workspace_bytes(...) bytes the
+ * results are the same up to fp32 summation order. Returns 0 for empty
+ * shapes and invalid arguments. (Both are throughput choices, not part of
+ * the pages' method.) */
 size_t sdpa_bwd_workspace_bytes_ex(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
-                                   int32_t dtype);
+                                   int32_t dtype, int32_t mask, int32_t window);
 
 /* Backward. Reads q, k, v, o, dO and lse as written by sdpa_fwd_lse for the
  * same arguments; writes dq [B, Hq, Lq, D] and dk, dv [B, Hq/group, Lk, D] in
@@ -214,24 +226,30 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 int32_t dtype, int32_t mask, int32_t window, float scale,
                 const sdpa_ext* ext, hipStream_t stream);
 
-/* Measurement variant of sdpa_bwd: identical arguments and results, plus two
- * caller-created HIP events. When both are non-null, `main_begin` and
- * `main_end` are recorded on `stream` immediately before and after the main
- * backward kernel, the key-stationary dK/dV pass (bf16; the dQ pass runs
- * before it, outside the events; for float32 they bracket both passes), so
- * hipEventElapsedTime gives that kernel's duration. Null events: same as
- * sdpa_bwd. The events stay owned by the caller. */
+/* Measurement variant of sdpa_bwd: identical arguments and results, plus an
+ * array of four caller-created HIP events (or null: same as sdpa_bwd; a null
+ * entry: SDPA_ERR_INVALID_ARG). They are recorded on `stream` before the
+ * first kernel and after each of the backward's three passes, so
+ * hipEventElapsedTime between neighbours gives each pass's duration:
+ *   events[0] -> [1]: the dQ pass (which also forms Delta), or, with the dS
+ *                     band buffer, the Delta pass;
+ *   events[1] -> [2]: the key-stationary dK/dV pass (with its share reduce
+ *                     when split; with the band buffer it also writes dS);
+ *   events[2] -> [3]: with the band buffer the dQ = scale dS K pass, else
+ *                     nothing.
+ * (float32: [0] -> [1] the dQ kernel, [1] -> [2] the dK/dV kernel.) The
+ * events stay owned by the caller. */
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                    const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                    int32_t dtype, int32_t mask, int32_t window, float scale,
-                   hipStream_t stream, hipEvent_t main_begin, hipEvent_t main_end);
+                   hipStream_t stream, const hipEvent_t* events);
 
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 302. */
+/* ABI version of this header (major * 100 + minor): 400. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -69,12 +69,12 @@ def load(path: str = LIB_PATH):
     lib.sdpa_fwd_lse_ex.argtypes = [p, p, p, p, p] + dims + [ext, p]
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
     lib.sdpa_bwd_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [ext, p]
-    lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, p, p]
+    lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, ctypes.POINTER(ctypes.c_void_p)]
     for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
-    lib.sdpa_bwd_workspace_bytes_ex.argtypes = [i32] * 7
+    lib.sdpa_bwd_workspace_bytes_ex.argtypes = [i32] * 9
     lib.sdpa_bwd_workspace_bytes_ex.restype = sz
     lib.sdpa_status_string.argtypes = [ctypes.c_int]
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -211,19 +211,22 @@ def workspace_bytes(B, Hq, L, D, dtype):
     return int(load().sdpa_bwd_workspace_bytes(B, Hq, L, D, DTYPE[dtype]))
 
 
-def bwd_workspace_bytes(B, Hq, group, Lq, Lk, D, dtype):
-    """Workspace with which the backward may also split a small problem's dK/dV pass."""
-    return int(load().sdpa_bwd_workspace_bytes_ex(B, Hq, group, Lq, Lk, D, DTYPE[dtype]))
+def bwd_workspace_bytes(B, Hq, group, Lq, Lk, D, dtype, mask="causal", window=0):
+    """Workspace with which the backward runs its fastest plan for this shape and mask: it may
+    also split a small problem's dK/dV pass, or keep dS for a bounded (windowed) band."""
+    m, w = _mask_args(mask, window)
+    return int(load().sdpa_bwd_workspace_bytes_ex(B, Hq, group, Lq, Lk, D, DTYPE[dtype], m, w))
 
 
 def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace=None, out=None,
-             main_events=None, sinks=None, cut=None):
+             events=None, sinks=None, cut=None):
     """dQ, dK, dV for the forward sdpa_fwd_lse(q, k, v, mask, window, scale) returned (o, lse);
     with ``sinks`` (the forward's), also d sinks: (dq, dk, dv, dsinks).
 
-    Gradients take the strides of q, k, v when those are dense. ``main_events``:
-    optional pair of raw hipEvent_t handles recorded around the main backward
-    kernel (sdpa_bwd_timed; contiguous tensors, no sinks)."""
+    Gradients take the strides of q, k, v when those are dense. ``events``:
+    optional four raw hipEvent_t handles recorded before the first kernel and
+    after each of the three passes (sdpa_bwd_timed; contiguous tensors, no
+    sinks, no cut)."""
     B, Hq, group, L, Lk, D = _validate(q, k, v, (("o", o), ("do", do)))
     sinks = _sinks_arg(sinks, q, Hq)
     dsinks = None if sinks is None else torch.empty(Hq, dtype=torch.float32, device=q.device)
@@ -233,7 +236,7 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
         raise ValueError("lse must be float32 [B, Hq, L]")
     scale = default_scale(D) if scale is None else float(scale)
     m, w = _mask_args(mask, window)
-    need = bwd_workspace_bytes(B, Hq, group, L, Lk, D, q.dtype)
+    need = bwd_workspace_bytes(B, Hq, group, L, Lk, D, q.dtype, mask, window)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -244,12 +247,14 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
     q, do = _same_rows(q, do)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(workspace), workspace.numel(), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale)
-    if main_events is None:
+    if events is None:
         ext, _keep = _ext(_strides(q, k, v, o, do, dq, dk, dv), sinks, dsinks, cut)
         _check("sdpa_bwd_ex", load().sdpa_bwd_ex(*args, ext, _stream(q.device)))
     else:
         if sinks is not None or cut is not None or not all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
             raise ValueError("the timed backward takes contiguous tensors, no sinks and no cut")
-        ev0, ev1 = (ctypes.c_void_p(e) for e in main_events)
-        _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), ev0, ev1))
+        if len(events) != 4:
+            raise ValueError("events: four hipEvent_t handles")
+        arr = (ctypes.c_void_p * 4)(*events)
+        _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), arr))
     return (dq, dk, dv) if sinks is None else (dq, dk, dv, dsinks)

@@ -22,7 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsdpa.so")
-SOURCES = ["sdpa_api.hip", "qs_mfma.hip", "kv_mfma.hip", "kv16_mfma.hip", "f32_valu.hip", "sinks.hip"]
+SOURCES = ["sdpa_api.hip", "qs_mfma.hip", "kv_mfma.hip", "kv16_mfma.hip", "dsq_mfma.hip", "f32_valu.hip",
+           "sinks.hip"]
 # measurement helper, its own library (include/sdpa_probe.h)
 PROBE_LIB = os.path.join(PKG, "libsdpa_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]

@@ -416,6 +416,13 @@ SDPA_DEV void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Tiles of the dS band buffer that the dK/dV pass writes and the dQ pass
+// reads (bounded bands): [kBandKeys keys][kBandRows query rows], key-major,
+// one per (batch and q-head, block of kBandRows rows, key tile of the
+// block's band).
+constexpr int kBandRows = 128;
+constexpr int kBandKeys = 64;
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map dispatch order to a logical tile order in which each XCD receives a
 // contiguous range, so neighbouring tiles (which share K/V or Q/dO bands)

@@ -186,10 +186,9 @@ template <int D>
 hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const void* o, const void* dO,
                           const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                           int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
-                          hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const bool timed = ev0 != nullptr && ev1 != nullptr;
+                          hipStream_t stream, const hipEvent_t* ev) {
   hipError_t e;
-  if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  if (ev != nullptr && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   if (Lq > 0) {
     dim3 grid((Lq + 127) / 128, Hq, B);
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, grid, dim3(128), 0, stream, (const float*)q, (const float*)k,
@@ -198,6 +197,7 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (ev != nullptr && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
   if (Lk > 0) {
     dim3 grid2((Lk + 127) / 128, Hq / group, B);
     hipLaunchKernelGGL(bwd_dkv_f32_kernel<D>, grid2, dim3(128), 0, stream, (const float*)q, (const float*)k,
@@ -206,7 +206,8 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  for (int i = 2; i < 4; i++)
+    if (ev != nullptr && (e = hipEventRecord(ev[i], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -216,8 +217,8 @@ hipError_t launch_bwd_f32(const void* q, const void* k, const void* v, const voi
                                         const AllStrides&, hipStream_t);                                    \
   template hipError_t launch_bwd_f32<D>(const void*, const void*, const void*, const void*, const void*,     \
                                         const float*, void*, void*, void*, float*, int, int, int, int, int,  \
-                                        int, int, Cut, float, const AllStrides&, hipStream_t, hipEvent_t,    \
-                                        hipEvent_t);
+                                        int, int, Cut, float, const AllStrides&, hipStream_t,                \
+                                        const hipEvent_t*);
 SDPA_INST_F32(64)
 SDPA_INST_F32(128)
 

@@ -26,6 +26,13 @@
 // A lane's C values of both row blocks (rows 4g + i and 16 + 4g + i) are
 // exactly 8 k-slots of the update's A operand; the B operand reads the same
 // rows from LDS with two transposed 4-row reads per lane group.
+//
+// DSOUT (dense D = 256 calls with a bounded band): each active wave also
+// stores its dS^T (16 keys x 32 rows, the dK update's A operand) into the band
+// buffer that dsq_kernel reads to form dQ = scale dS K (dsq_mfma.hip documents
+// the layout): a lane holds one key and rows 4g + 0..3, 16 + 4g + 0..3 of the
+// tile, which sit as two runs of 4 rows in the key-major tile, so two 8-byte
+// stores per lane and tile.
 #include "common.h"
 
 namespace sdpa {
@@ -60,12 +67,13 @@ struct LaneAddr16 {
 
 // D <= 256: two workgroups per CU (two waves per SIMD, at most 256 registers
 // per lane); D = 512: one.
-template <int D, typename E, bool DENSE>
+template <int D, typename E, bool DENSE, bool DSOUT>
 __global__ void __launch_bounds__(256, D <= 256 ? 2 : 1)
 kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
             const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
             E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-            Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
+            Cut cut_arg, float scale, float scale_log2, AllStrides st_arg, E* __restrict__ dST, int nqb, int nkb) {
+  static_assert(!DSOUT || DENSE, "the band buffer is written by the dense instantiation");
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
   constexpr int NW = 4, BKT = 16 * NW, BQ = 32, NT = D / 32, NB = D / 16, QT = BQ * D;
@@ -149,6 +157,9 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
     return (t < nq2 ? qt2_lo + t : qt_lo + (t - nq2)) * BQ;
   };
   const int kb1 = min(kb0 + 15, Lk - 1);  // this wave's last key (kb1 < kb0: none)
+  // byte offset of this lane's dS^T values (key kj, rows rg..rg+3) inside a
+  // band tile, relative to the wave's first key
+  const uint32_t ds_lane = DSOUT ? (uint32_t)(((lane & 15) * kBandRows + rg) * sizeof(E)) : 0u;
   const int wrhi = kb1 - dlo;             // last row that sees a key of the wave (dense: no cut)
   // some pair of the tile's rows [q0, q0 + 31] and the wave's keys allowed / every pair allowed
   auto tile_tests = [&](int q0, bool& active, bool& full) {
@@ -296,6 +307,22 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
       da[i] = (E)p0[i];
       da[4 + i] = (E)p1[i];
     }
+    if constexpr (DSOUT) {
+      // band buffer: row block qb's tiles start at the key tile ktl of its band
+      // (the query tile lies inside one row block; every key of this wave is
+      // inside the block's nkb tiles, since some row of the tile sees one).
+      // The block's base and the tile's offset are uniform (scalar registers);
+      // each lane adds its fixed offset ds_lane.
+      const int hq = g * group + it / nq, qb = q0 / kBandRows;
+      const int ktl = max(0, qb * kBandRows + dlo) / kBandKeys;
+      const size_t blk = (size_t)nkb * kBandKeys * kBandRows;  // elements per row block
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(dST + ((size_t)(b * Hq + hq) * nqb + qb) * blk, 0,
+                                                        (int)(blk * sizeof(E)), 0x00020000);
+      const int soff = ((kb0 - ktl * kBandKeys) * kBandRows + (q0 % kBandRows)) * (int)sizeof(E);
+      const i32x4 v = __builtin_bit_cast(i32x4, da);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 0, 1), rs, (int)ds_lane, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 2, 3), rs, (int)ds_lane + 32, soff, 0);
+    }
 #pragma unroll
     for (int blk = 0; blk < NB; blk++) {
       dvacc[blk] = mfma16(pa, rd_trn(dOc, blk), dvacc[blk]);
@@ -351,30 +378,35 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   }
 }
 
+// dst (D = 256, dense only): the band buffer to fill with dS^T (nqb blocks of
+// 128 rows, nkb key tiles each), or null.
 template <int D, typename E>
 hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                        const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                       int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
+                       int dhi, Cut cut, float scale, const AllStrides& st, void* dst, int nqb, int nkb,
+                       hipStream_t stream) {
   const long nwg = (long)((Lk + 63) / 64) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
-  auto kernel = kv16_kernel<D, E, true>;
+  auto kernel = kv16_kernel<D, E, true, false>;
   if constexpr (D > 256) {
-    if (!dense) kernel = kv16_kernel<D, E, false>;
-  } else if (!dense) {
-    return hipErrorInvalidValue;  // below D = 512 only dense calls come here (the strided kind would spill)
+    if (dst != nullptr) return hipErrorInvalidValue;
+    if (!dense) kernel = kv16_kernel<D, E, false, false>;
+  } else {
+    if (!dense) return hipErrorInvalidValue;  // below D = 512 only dense calls come here (the strided kind would spill)
+    if (dst != nullptr) kernel = kv16_kernel<D, E, true, true>;
   }
   hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                      (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk, dlo, dhi, cut, scale,
-                     scale * kLog2e, st);
+                     scale * kLog2e, st, (E*)dst, nqb, nkb);
   return hipGetLastError();
 }
 
 #define SDPA_INST_KV16(D, E)                                                                              \
   template hipError_t launch_kv16<D, E>(const void*, const void*, const void*, const void*, const float*,  \
                                         const float*, void*, void*, int, int, int, int, int, int, int, Cut, \
-                                        float, const AllStrides&, hipStream_t);
+                                        float, const AllStrides&, void*, int, int, hipStream_t);
 SDPA_INST_KV16(256, bf16)
 SDPA_INST_KV16(256, f16)
 SDPA_INST_KV16(512, bf16)

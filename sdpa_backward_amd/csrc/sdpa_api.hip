@@ -30,7 +30,13 @@ int kv_split_shares(int B, int Hq, int group, int Lq, int Lk, bool dense);
 template <int D, typename E>
 hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                        const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                       int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
+                       int dhi, Cut cut, float scale, const AllStrides& st, void* dst, int nqb, int nkb,
+                       hipStream_t stream);
+template <int D, typename E>
+hipError_t launch_delta(const void* o, const void* dO, float* delta, long long rows, hipStream_t stream);
+template <int D, typename E>
+hipError_t launch_dsq(const void* dst, const void* k, void* dq, int B, int Hq, int group, int Lq, int Lk, int dlo,
+                      int dhi, int nqb, int nkb, float scale, hipStream_t stream);
 template <int D>
 hipError_t launch_fwd_f32(const void*, const void*, const void*, void*, float*, int, int, const float*, int, int,
                           int, int, int, Cut, float, const AllStrides&, hipStream_t);
@@ -39,38 +45,73 @@ hipError_t launch_dsinks(const float* lse, const float* delta, const float* sink
 template <int D>
 hipError_t launch_bwd_f32(const void*, const void*, const void*, const void*, const void*, const float*,
                           void*, void*, void*, float*, int, int, int, int, int, int, int, Cut, float,
-                          const AllStrides&, hipStream_t, hipEvent_t, hipEvent_t);
+                          const AllStrides&, hipStream_t, const hipEvent_t*);
 
-// 16-bit backward: dQ pass (also writes Delta), then the dK/dV pass (split
-// into nseg shares summed into part when nseg > 1); the optional events
-// bracket the dK/dV pass.
+// Optional timing events of a backward: [0] before its first kernel, [1] after
+// the first pass, [2] after the dK/dV pass, [3] after the last pass.
+hipError_t mark(const hipEvent_t* ev, int i, hipStream_t stream) {
+  return ev != nullptr ? hipEventRecord(ev[i], stream) : hipSuccess;
+}
+
+// How a 16-bit backward runs (chosen by the host from the shape, the layout
+// and the workspace given).
+struct BwdPlan {
+  bool wide;     // dense, and the key blocks alone fill the GPU: 16-key dK/dV waves at D = 256
+  float* part;   // fp32 dK/dV shares of the small-problem split (nseg > 1), or null
+  int nseg;
+  void* band;    // dS band buffer (bounded band, D = 256, wide), or null
+  int nqb, nkb;  // its row blocks and key tiles per block
+};
+
+// 16-bit backward.
+//   band buffer: Delta pass, dK/dV pass that also writes dS^T for the band,
+//                dQ = scale dS K from that buffer (no score recomputed);
+//   otherwise:   dQ pass (recomputes S and dP, also writes Delta), then the
+//                dK/dV pass (split into nseg shares summed into part when
+//                nseg > 1).
 template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int group, int Lq, int Lk, int dlo, int dhi, Cut cut, float scale, const AllStrides& st,
-                           bool wide, float* part, int nseg, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  hipError_t e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group,
-                                        Lq, Lk, dlo, dhi, cut, scale, st, stream);
+                           const BwdPlan& plan, hipStream_t stream, const hipEvent_t* ev) {
+  hipError_t e;
+  if ((e = mark(ev, 0, stream)) != hipSuccess) return e;
+  if constexpr (D == 256) {
+    if (plan.band != nullptr) {
+      if ((e = launch_delta<D, E>(o, dO, delta, (long long)B * Hq * Lq, stream)) != hipSuccess) return e;
+      if ((e = mark(ev, 1, stream)) != hipSuccess) return e;
+      e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st,
+                            plan.band, plan.nqb, plan.nkb, stream);
+      if (e != hipSuccess) return e;
+      if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
+      e = launch_dsq<D, E>(plan.band, k, dq, B, Hq, group, Lq, Lk, dlo, dhi, plan.nqb, plan.nkb, scale, stream);
+      if (e != hipSuccess) return e;
+      return mark(ev, 3, stream);
+    }
+  }
+  e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group, Lq, Lk, dlo,
+                             dhi, cut, scale, st, stream);
   if (e != hipSuccess) return e;
-  const bool timed = ev0 != nullptr && ev1 != nullptr;
-  if (timed && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  if ((e = mark(ev, 1, stream)) != hipSuccess) return e;
   // 16-key waves (v_mfma_f32_16x16x32): at D = 512 always (32-key waves would
   // not fit their accumulators in registers there), at D = 256 for dense calls
   // whose key blocks fill the GPU (two workgroups per CU; measured faster than
   // the 32-key kernel there); otherwise 32-key waves. The choice depends on
   // the shape and layout only, never on the workspace given.
   if constexpr (D == 512) {
-    e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
+    e = launch_kv16<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, nullptr,
+                          0, 0, stream);
   } else {
-    if (D == 256 && wide)
-      e = launch_kv16<256, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, stream);
+    if (D == 256 && plan.wide)
+      e = launch_kv16<256, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st,
+                              nullptr, 0, 0, stream);
     else
-      e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st, part,
-                          nseg, stream);
+      e = launch_kv<D, E>(q, k, v, dO, lse, delta, dk, dv, B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, st,
+                          plan.part, plan.nseg, stream);
   }
   if (e != hipSuccess) return e;
-  if (timed && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
-  return hipSuccess;
+  if ((e = mark(ev, 2, stream)) != hipSuccess) return e;
+  return mark(ev, 3, stream);
 }
 }  // namespace sdpa
 
@@ -150,10 +191,39 @@ int split_shares(const Shape& s, bool dense) {
   }
 }
 
+bool wide_call(const Shape& s, bool dense) { return s.D == 256 && dense && split_shares(s, dense) == 1; }
+
 // Bytes of the split's fp32 dK and dV shares.
 size_t split_bytes(const Shape& s, int nseg) {
   return nseg > 1 ? align_up(2 * (size_t)nseg * s.B * (s.Hq / s.group) * s.Lk * s.D * sizeof(float)) : 0;
 }
+
+int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Whether this shape's dense call keeps dS for its band (16-bit, D = 256, the
+// 16-key dK/dV kernel), and the band buffer's geometry and bytes (0: it does
+// not). A block of kBandRows rows at i0 sees keys [i0 + dlo, i0 + 127 + dhi]
+// (clipped to [0, Lk)); i0 is a multiple of the tile width, so unclipped
+// blocks all span floor((127 + dhi) / 64) - floor(dlo / 64) + 1 key tiles and
+// clipped ones no more. The buffer is used only when a block's band is at most
+// 8 D keys wide, so it never exceeds 8 times the size of Q (a window of up to
+// about 1900 keys at D = 256): memory stays linear in Lq at any length, and
+// wider bands (causal, no mask) recompute S and dP for dQ instead.
+size_t band_bytes(const Shape& s, int dlo, int dhi, int& nqb, int& nkb) {
+  nqb = nkb = 0;
+  if (s.dtype == SDPA_F32 || s.D != 256 || s.no_rows() || s.no_keys() || dlo > dhi) return 0;
+  const int64_t tiles = floor_div(sdpa::kBandRows - 1 + (int64_t)dhi, sdpa::kBandKeys) -
+                        floor_div(dlo, sdpa::kBandKeys) + 1;
+  const int64_t n = std::min<int64_t>(tiles, (s.Lk + sdpa::kBandKeys - 1) / sdpa::kBandKeys);
+  if (n * sdpa::kBandKeys > 8 * (int64_t)s.D) return 0;
+  nqb = (s.Lq + sdpa::kBandRows - 1) / sdpa::kBandRows;
+  nkb = (int)n;
+  return align_up((size_t)s.B * s.Hq * nqb * nkb * sdpa::kBandKeys * sdpa::kBandRows * 2);
+}
+
+// Whether a dense 16-bit call runs the 16-key dK/dV kernel at D = 256 (its key
+// blocks alone fill the GPU, so no split).
+
 
 int to_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH; }
 
@@ -218,7 +288,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 302; }
+int sdpa_abi_version(void) { return 400; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -238,11 +308,15 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
 }
 
 size_t sdpa_bwd_workspace_bytes_ex(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
-                                   int32_t dtype) {
-  Shape s{B, Hq, group, Lq, Lk, D, dtype, SDPA_MASK_CAUSAL, 1, 1.f};
+                                   int32_t dtype, int32_t mask, int32_t window) {
+  Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, 1.f};
   if (check_shape(s) != SDPA_OK) return 0;
   const size_t base = workspace_for(s);
-  return base == 0 || s.no_keys() ? base : base + split_bytes(s, split_shares(s, true));
+  if (base == 0 || s.no_keys()) return base;
+  int dlo, dhi, nqb, nkb;
+  s.band(dlo, dhi);
+  const size_t band = wide_call(s, true) ? band_bytes(s, dlo, dhi, nqb, nkb) : 0;
+  return base + std::max(split_bytes(s, split_shares(s, true)), band);
 }
 
 int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
@@ -301,7 +375,7 @@ namespace {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t B, int32_t Hq,
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
-             float scale, const sdpa_ext* ext, hipStream_t stream, hipEvent_t main_begin, hipEvent_t main_end) {
+             float scale, const sdpa_ext* ext, hipStream_t stream, const hipEvent_t* events) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -325,20 +399,26 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return SDPA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
-  // the dK/dV split of a small dense call, when the workspace holds its shares
-  const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
-  int nseg = split_shares(s, dense);
-  const bool wide = dense && nseg == 1;  // dense, and the key blocks alone fill the GPU
-  if (nseg > 1 && workspace_bytes < need + split_bytes(s, nseg)) nseg = 1;
-  float* part = nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need) : nullptr;
   int dlo, dhi;
   s.band(dlo, dhi);
+  // the dK/dV split of a small dense call, or the dS band buffer of a bounded
+  // band, when the workspace holds them (after the Delta rows)
+  const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
+  char* extra = static_cast<char*>(workspace) + need;
+  sdpa::BwdPlan plan{dense && split_shares(s, dense) == 1, nullptr, split_shares(s, dense), nullptr, 0, 0};
+  if (plan.nseg > 1 && workspace_bytes < need + split_bytes(s, plan.nseg)) plan.nseg = 1;
+  if (plan.nseg > 1) plan.part = reinterpret_cast<float*>(extra);
+  if (wide_call(s, dense)) {
+    int nqb, nkb;
+    const size_t bb = band_bytes(s, dlo, dhi, nqb, nkb);
+    if (bb > 0 && workspace_bytes >= need + bb) plan.band = extra, plan.nqb = nqb, plan.nkb = nkb;
+  }
   hipError_t e;
   switch (dtype * 1000 + D) {
 #define SDPA_BWD_CASE(DT, E, DD)                                                                              \
   case DT * 1000 + DD:                                                                                        \
     e = sdpa::launch_bwd_mfma<DD, E>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi,   \
-                                     cut, scale, str, wide, part, nseg, stream, main_begin, main_end);        \
+                                     cut, scale, str, plan, stream, events);                                  \
     break;
     SDPA_BWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_BWD_CASE(SDPA_BF16, bf16, 128)
@@ -351,11 +431,11 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 #undef SDPA_BWD_CASE
     case SDPA_F32 * 1000 + 64:
       e = sdpa::launch_bwd_f32<64>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
-                                   scale, str, stream, main_begin, main_end);
+                                   scale, str, stream, events);
       break;
     case SDPA_F32 * 1000 + 128:
       e = sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
-                                    scale, str, stream, main_begin, main_end);
+                                    scale, str, stream, events);
       break;
     default:
       return SDPA_ERR_UNSUPPORTED;
@@ -375,16 +455,18 @@ int sdpa_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
                 float scale, const sdpa_ext* ext, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, ext, stream, nullptr, nullptr);
+                  mask, window, scale, ext, stream, nullptr);
 }
 
 int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                    int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype,
-                   int32_t mask, int32_t window, float scale, hipStream_t stream, hipEvent_t main_begin,
-                   hipEvent_t main_end) {
+                   int32_t mask, int32_t window, float scale, hipStream_t stream, const hipEvent_t* events) {
+  if (events != nullptr)
+    for (int i = 0; i < 4; i++)
+      if (events[i] == nullptr) return SDPA_ERR_INVALID_ARG;
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, stream, main_begin, main_end);
+                  mask, window, scale, nullptr, stream, events);
 }
 
 int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -392,7 +474,7 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
              float scale, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
-                  mask, window, scale, nullptr, stream, nullptr, nullptr);
+                  mask, window, scale, nullptr, stream, nullptr);
 }
 
 }  // extern "C"

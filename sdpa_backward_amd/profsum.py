@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 # they were taken on
 KERNEL_SOURCES = {"kv16_kernel": ["sdpa_backward_amd/csrc/kv16_mfma.hip", "sdpa_backward_amd/csrc/common.h",
                                   "sdpa_backward_amd/build.py"],
+                  "dsq_kernel": ["sdpa_backward_amd/csrc/dsq_mfma.hip", "sdpa_backward_amd/csrc/common.h",
+                                 "sdpa_backward_amd/build.py"],
                   "kv_kernel": ["sdpa_backward_amd/csrc/kv_mfma.hip", "sdpa_backward_amd/csrc/common.h",
                                 "sdpa_backward_amd/build.py"]}
 COPY_KERNEL = "copyBuffer"   # the 1 GiB device copy bench.py --copy-probe runs
@@ -51,12 +53,37 @@ def tag(w) -> str:
 
 def short(name: str) -> str:
     """Kernel name without its signature and element type: sdpa::kv_kernel<256, 0>."""
+    m = re.match(r"_ZN4sdpa\d+(\w+?_kernel)I((?:Li\d+E)+)", name)  # names the tool left mangled
+    if m:
+        ints = re.findall(r"Li(\d+)E", m.group(2))
+        keep = 2 if m.group(1) in ("qs_kernel",) else 1
+        return f"sdpa::{m.group(1)}<{', '.join(ints[:keep])}>"
     name = name.replace("void ", "")
     name = re.sub(r"\(.*", "", name)
     name = re.sub(r"<(\d+), (\d+), [^<>]+>", r"<\1, \2>", name)  # the workloads here are bf16
     name = re.sub(r"^(sdpa::kv16_kernel)<(\d+), [^<>]+>", r"\1<\2>", name)
     name = re.sub(r"^(sdpa::kv_reduce_kernel)<[^<>]+>", r"\1", name)
+    name = re.sub(r"^(sdpa::(dsq|delta)_kernel)<(\d+), [^<>]+>", r"\1<\3>", name)
     return name
+
+
+def band_geometry(w):
+    """(row blocks, key tiles per block) of the dS band buffer for this workload (the library's
+    rule: D = 256 with the 16-key dK/dV kernel, i.e. at least 256 blocks of 128 keys; 128-row
+    blocks, 64-key tiles, a block's band at most 8 D keys wide), or None."""
+    if w.D != 256 or w.dtype == "f32" or -(-w.Lkv // 128) * w.Hkv * w.B < 256:
+        return None
+    off = w.Lkv - w.L
+    lo, hi = -(w.L - 1), w.Lkv - 1
+    if w.mask == "causal":
+        hi = off
+    if w.mask == "causal_window":
+        lo, hi = off - w.window + 1, off
+    if w.mask == "window":
+        lo, hi = off - w.window + 1, off + w.window - 1
+    lo, hi = max(lo, -(w.L - 1)), min(hi, w.Lkv - 1)
+    nkb = min((127 + hi) // 64 - lo // 64 + 1, -(-w.Lkv // 64))
+    return (-(-w.L // 128), nkb) if nkb * 64 <= 8 * w.D else None
 
 
 def roles(w):
@@ -68,12 +95,20 @@ def roles(w):
     kv = w.B * w.Hkv * w.Lkv * w.D * e
     row = w.B * w.Hq * w.L * 4
     D = w.D
-    return {
+    r = {
         f"sdpa::qs_kernel<{D}, 0>": ("forward (O, lse)", 4 * D * N, q + 2 * kv, q + row),
         f"sdpa::qs_kernel<{D}, 1>": ("dQ pass (+Delta)", 6 * D * N, 3 * q + 2 * kv + row, q + row),
         f"sdpa::kv_kernel<{D}, 0>": ("dK/dV pass (32-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
         f"sdpa::kv16_kernel<{D}>": ("dK/dV pass (16-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
     }
+    bg = band_geometry(w)
+    if bg:  # the backward that keeps dS for the band: the dK/dV pass also writes it
+        band = w.B * w.Hq * bg[0] * bg[1] * 64 * 128 * e
+        r[f"sdpa::delta_kernel<{D}>"] = ("Delta pass", 0, 2 * q, row)
+        r[f"sdpa::kv16_kernel<{D}>"] = ("dK/dV pass writing dS (16-key waves)", 8 * D * N,
+                                        2 * q + 2 * kv + 2 * row, 2 * kv + band)
+        r[f"sdpa::dsq_kernel<{D}>"] = ("dQ = scale dS K pass", 2 * D * N, band + kv, q)
+    return r
 
 
 def read_trace(d):
@@ -162,7 +197,7 @@ def main():
     open(os.path.join(out, f"kernel_stats_{t}.md"), "w").write("\n".join(lines) + "\n")
 
     # ---------------------------------------------------------------- counters
-    p = {i: read_counters(os.path.join(out, f"p{i}")) for i in (1, 2, 3, 4)}
+    p = {i: read_counters(os.path.join(out, f"p{i}")) for i in range(1, len(PASSES) + 1)}
 
     def mean_of(i, k, c):
         v = p[i].get(k, {}).get(c)
@@ -181,20 +216,22 @@ def main():
               f"HBM byte scaling from the 1 GiB device copy in the same runs: FETCH_SIZE KiB x {fetch_scale:.3f} "
               f"= bytes read / 1024, WRITE_SIZE KiB x {write_scale:.3f} = bytes written / 1024.", "",
               "| kernel | MFMA busy | VALU instr / MFMA instr | LDS bank-conflict cycles / LDS active cycles "
-              "| HBM read | algorithmic read | HBM write | algorithmic write |",
-              "|---|---|---|---|---|---|---|---|"]
+              "| L2 hit rate | HBM read | algorithmic read | HBM write | algorithmic write |",
+              "|---|---|---|---|---|---|---|---|---|"]
     traffic = None
     for k in R:
         if k not in timed:
             continue
         role, flop, ar, aw = R[k]
         busy = mean_of(1, k, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * timed[k] * 1e-6 * 2.4e9)
-        valu = mean_of(1, k, "SQ_INSTS_VALU") / mean_of(1, k, "SQ_INSTS_MFMA")
+        mf = mean_of(1, k, "SQ_INSTS_MFMA")
+        valu = mean_of(1, k, "SQ_INSTS_VALU") / mf if mf > 0 else float("nan")
         bank = mean_of(2, k, "SQ_LDS_BANK_CONFLICT") / mean_of(2, k, "SQ_ACTIVE_INST_LDS")
         rd = mean_of(3, k, "FETCH_SIZE") * 1024 * fetch_scale
         wr = mean_of(4, k, "WRITE_SIZE") * 1024 * write_scale
-        lines.append(f"| `{k}` | {100 * busy:.1f} % | {valu:.2f} | {bank:.3f} | {rd / 1e9:.3f} GB | {ar / 1e9:.3f} GB "
-                     f"| {wr / 1e9:.3f} GB | {aw / 1e9:.3f} GB |")
+        hit, miss = mean_of(5, k, "TCC_HIT_sum"), mean_of(5, k, "TCC_MISS_sum")
+        lines.append(f"| `{k}` | {100 * busy:.1f} % | {valu:.2f} | {bank:.3f} | {100 * hit / (hit + miss):.1f} % "
+                     f"| {rd / 1e9:.3f} GB | {ar / 1e9:.3f} GB | {wr / 1e9:.3f} GB | {aw / 1e9:.3f} GB |")
         if k == main_k:
             traffic = {"kernel": f"{main_k[len('sdpa::'):]} (dK/dV pass)", "workload": w.name,
                        "sources_sha256": sources_sha256("kv16_kernel" if "kv16" in main_k else "kv_kernel"),
@@ -218,6 +255,7 @@ PASSES = [
     "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_ADDR_CONFLICT SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_WAIT_INST_ANY SQ_LDS_IDX_ACTIVE",
     "FETCH_SIZE",
     "WRITE_SIZE",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum",
 ]
 
 if __name__ == "__main__":

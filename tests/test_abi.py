@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 302
+    assert lib.sdpa_abi_version() == 400
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -248,9 +248,10 @@ def test_extension_errors(lib):
 
 
 def test_split_workspace_sizes(lib):
-    ex = lib.sdpa_bwd_workspace_bytes_ex
-    ex.argtypes = [ctypes.c_int32] * 7
-    ex.restype = ctypes.c_size_t
+    ex9 = lib.sdpa_bwd_workspace_bytes_ex
+    ex9.argtypes = [ctypes.c_int32] * 9
+    ex9.restype = ctypes.c_size_t
+    ex = lambda *a: ex9(*a, CAUSAL, 0)
     delta = lambda B, Hq, Lq: -(-(B * Hq * Lq * 4) // 256) * 256
     # causal L=2048 D=256 8/4: 16 key blocks x 4 kv heads = 64 workgroups -> 4 shares of fp32 dK, dV
     assert ex(1, 8, 2, 2048, 2048, 256, BF16) == delta(1, 8, 2048) + 2 * 4 * 4 * 2048 * 256 * 4
@@ -266,6 +267,37 @@ def test_split_workspace_sizes(lib):
     assert ex(1, 8, 2, 2048, 0, 256, BF16) == delta(1, 8, 2048)
     assert ex(0, 8, 2, 2048, 2048, 256, BF16) == 0
     assert ex(1, 8, 3, 2048, 2048, 256, BF16) == 0
+
+
+def test_band_workspace_sizes(lib):
+    ex = lib.sdpa_bwd_workspace_bytes_ex
+    ex.argtypes = [ctypes.c_int32] * 9
+    ex.restype = ctypes.c_size_t
+    delta = lambda B, Hq, Lq: -(-(B * Hq * Lq * 4) // 256) * 256
+    tile = 64 * 128 * 2  # one band tile: 64 keys x 128 rows, 16-bit
+    # window 1024 at D = 256 (16-key dK/dV kernel): a block of 128 rows sees
+    # keys i0 - 1023 .. i0 + 127, i.e. 18 key tiles of 64, for each of
+    # 32 heads x 128 row blocks
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 1024) == delta(1, 32, 16384) + 32 * 128 * 18 * tile
+    assert ex(1, 32, 2, 16384, 16384, 256, F16, WINDOW, 1024) == delta(1, 32, 16384) + 32 * 128 * 18 * tile
+    # ragged length: 239 row blocks
+    assert ex(1, 32, 2, 30553, 30553, 256, BF16, WINDOW, 1024) == delta(1, 32, 30553) + 32 * 239 * 18 * tile
+    # linear in L at a fixed window
+    sizes = [ex(1, 32, 2, L, L, 256, BF16, WINDOW, 1024) for L in (4096, 8192, 16384, 32768)]
+    assert [b / a for a, b in zip(sizes, sizes[1:])] == [2.0, 2.0, 2.0]
+    # window 1: keys i0 .. i0 + 127, 2 tiles
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 1) == delta(1, 32, 16384) + 32 * 128 * 2 * tile
+    # bands wider than 8 D = 2048 keys keep no dS: the two-sided window 1024
+    # (34 tiles), causal and no mask at long lengths; and only D = 256 keeps it
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, TWO_SIDED, 1024) == delta(1, 32, 16384)
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, CAUSAL, 0) == delta(1, 32, 16384)
+    assert ex(1, 32, 2, 4096, 4096, 256, BF16, NONE, 0) == delta(1, 32, 4096)
+    assert ex(1, 32, 2, 16384, 16384, 128, BF16, WINDOW, 1024) == delta(1, 32, 16384)
+    assert ex(1, 16, 4, 16384, 16384, 512, BF16, WINDOW, 1024) == delta(1, 16, 16384)
+    # short sequences: the band is capped by the key tiles that exist, and the
+    # dS buffer only comes with the 16-key kernel (at least 256 key blocks of 128)
+    assert ex(2, 16, 1, 1024, 1024, 256, BF16, CAUSAL, 0) == delta(2, 16, 1024) + 2 * 16 * 8 * 16 * tile
+    assert ex(1, 8, 2, 2048, 2048, 256, BF16, WINDOW, 100) == delta(1, 8, 2048) + 2 * 4 * 4 * 2048 * 256 * 4
 
 
 def test_ext_layout_matches_header(tmp_path):

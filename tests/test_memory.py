@@ -43,7 +43,7 @@ def peak_above_inputs(Hq, Hkv, D, mask, window, L, seed):
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated(DEV) - base
     outs = sum(t.numel() * t.element_size() for t in (o, lse, dq, dk, dv))
-    ws = bwd_workspace_bytes(1, Hq, Hq // Hkv, L, L, D, q.dtype)
+    ws = bwd_workspace_bytes(1, Hq, Hq // Hkv, L, L, D, q.dtype, mask, window)
     finite = all(bool(torch.isfinite(t).all()) for t in (o, dq, dk, dv))
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
@@ -59,8 +59,10 @@ def test_peak_memory_is_linear_in_L(geom):
         print(f"{geom} L={L}: peak above inputs {peak / 1e9:.3f} GB (outputs + workspace {expect / 1e9:.3f} GB, "
               f"workspace {ws / 1e9:.3f} GB)", flush=True)
         assert finite, L
-        # torch rounds each allocation up to 512 bytes
-        assert expect <= peak <= expect + 8 * 512, (L, peak, expect)
+        # torch's allocator counts a tensor at a multiple of 512 bytes, and one
+        # above 1 MiB at its whole segment (2 MiB granularity) unless more than
+        # 1 MiB of it is left over: at most 1 MiB more for each of the six tensors
+        assert expect <= peak <= expect + 6 * 2**20, (L, peak, expect)
         peaks.append(peak)
     for a, b in zip(peaks, peaks[1:]):
         assert abs(b / a - 2.0) < 0.01, peaks

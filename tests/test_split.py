@@ -43,7 +43,8 @@ def test_split_matches_unsplit_and_oracle(case):
     w = Workload(name, B, Hq, Hkv, Lq, D, dtype, mask, window, seed=9800 + Lq, Lk=Lk)
     inp = make_inputs(w)
     dt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
-    small, big = workspace_bytes(B, Hq, Lq, D, dt), bwd_workspace_bytes(B, Hq, Hq // Hkv, Lq, Lk, D, dt)
+    small = workspace_bytes(B, Hq, Lq, D, dt)
+    big = bwd_workspace_bytes(B, Hq, Hq // Hkv, Lq, Lk, D, dt, mask, window)
     assert big > small, "the case must take the split"
     one = _run(w, inp, small)
     split = _run(w, inp, big)
