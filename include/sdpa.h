@@ -89,7 +89,9 @@ enum sdpa_status {
                                 (bf16, f16) / {64,128} (f32); Lq + Lk > 2^30;
                                 B or Hq > 65535 */
   SDPA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
-  SDPA_ERR_LAUNCH = -4       /* the HIP runtime reported a launch error */
+  SDPA_ERR_LAUNCH = -4,      /* the HIP runtime reported a launch error */
+  SDPA_ERR_SCRATCH_LIMIT = -5 /* sdpa_bwd_noalloc: the problem needs more
+                                scratch than its fixed array holds */
 };
 
 enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F32 = 1, SDPA_F16 = 2 };
@@ -245,6 +247,30 @@ int sdpa_bwd_timed(const void* q, const void* k, const void* v, const void* o, c
                    int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
                    int32_t dtype, int32_t mask, int32_t window, float scale,
                    hipStream_t stream, const hipEvent_t* events);
+
+/* Size of the fixed scratch array behind sdpa_bwd_noalloc (64 MiB). */
+#define SDPA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* Backward that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments as sdpa_bwd minus
+ * the workspace, same results: its scratch is a fixed device array of
+ * SDPA_NOALLOC_SCRATCH_BYTES per GPU, held by the library until the process
+ * ends (its address is looked up on the first call on each device, with that
+ * device current; the stream must belong to the current device). Problems
+ * whose Delta rows (4 * B * Hq * Lq bytes) exceed it return
+ * SDPA_ERR_SCRATCH_LIMIT before anything is launched; the small-problem split
+ * and the dS band buffer (see sdpa_bwd_workspace_bytes_ex) are used only when
+ * they fit as well. Nothing in the array needs clearing between calls (every
+ * pass writes what a later pass reads). All calls on one GPU share the array:
+ * calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race and must not be issued; stream-ordered calls are
+ * safe. No hipMalloc, hipFree or allocating library call is made. */
+int sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                     int32_t dtype, int32_t mask, int32_t window, float scale,
+                     hipStream_t stream);
 
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);

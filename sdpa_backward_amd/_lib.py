@@ -26,11 +26,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 
 SDPA_OK = 0
 STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", -3: "SDPA_ERR_WORKSPACE",
-          -4: "SDPA_ERR_LAUNCH"}
+          -4: "SDPA_ERR_LAUNCH", -5: "SDPA_ERR_SCRATCH_LIMIT"}
 DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
-EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed",
+EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed", "sdpa_bwd_noalloc",
            "sdpa_bwd_workspace_bytes", "sdpa_bwd_workspace_bytes_ex", "sdpa_status_string", "sdpa_abi_version")
 
 _lib = None
@@ -70,7 +70,8 @@ def load(path: str = LIB_PATH):
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
     lib.sdpa_bwd_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [ext, p]
     lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, ctypes.POINTER(ctypes.c_void_p)]
-    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed"):
+    lib.sdpa_bwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, p] + dims + [p]
+    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed", "sdpa_bwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
@@ -258,3 +259,20 @@ def sdpa_bwd(q, k, v, o, do, lse, mask="causal", window=0, scale=None, workspace
         arr = (ctypes.c_void_p * 4)(*events)
         _check("sdpa_bwd_timed", load().sdpa_bwd_timed(*args, _stream(q.device), arr))
     return (dq, dk, dv) if sinks is None else (dq, dk, dv, dsinks)
+
+
+def sdpa_bwd_noalloc(q, k, v, o, do, lse, mask="causal", window=0, scale=None, out=None):
+    """sdpa_bwd through the allocation-free entry point (the library's fixed per-GPU scratch, no
+    workspace): contiguous tensors; ``out`` = (dq, dk, dv) buffers, or None to allocate them here."""
+    B, Hq, group, L, Lk, D = _validate(q, k, v, (("o", o), ("do", do)))
+    if not all(t.is_contiguous() for t in (q, k, v, o, do, lse)):
+        raise ValueError("sdpa_bwd_noalloc takes contiguous tensors")
+    scale = default_scale(D) if scale is None else float(scale)
+    m, w = _mask_args(mask, window)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v)) if out is None else out
+    if not all(x.is_contiguous() and x.shape == t.shape and x.dtype == t.dtype for x, t in zip((dq, dk, dv), (q, k, v))):
+        raise ValueError("output buffers must be contiguous and match q, k, v")
+    st = load().sdpa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, Hq, group, L, Lk, D, DTYPE[q.dtype], m, w, scale, _stream(q.device))
+    _check("sdpa_bwd_noalloc", st)
+    return dq, dk, dv

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sdpa.h"
 #include "common.h"
@@ -297,6 +298,8 @@ const char* sdpa_status_string(int status) {
     case SDPA_ERR_UNSUPPORTED: return "unsupported combination (not built; no fallback)";
     case SDPA_ERR_WORKSPACE: return "workspace missing or too small";
     case SDPA_ERR_LAUNCH: return "kernel launch failed";
+    case SDPA_ERR_SCRATCH_LIMIT:
+      return "the allocation-free backward's fixed scratch is too small for this problem (use sdpa_bwd)";
     default: return "unknown status";
   }
 }
@@ -475,6 +478,59 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              float scale, hipStream_t stream) {
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype,
                   mask, window, scale, nullptr, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free backward
+namespace {
+
+// The backward's scratch for sdpa_bwd_noalloc: one fixed array per GPU, held
+// until the process ends. Host code must not use the array's name as a device
+// address; each device's address comes from hipGetSymbolAddress (below).
+constexpr size_t kScratchBytes = size_t(SDPA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// This device's copy of `scratch` (looked up once per device, with that
+// device current).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDPA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SDPA_ERR_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t Hq, int32_t group,
+                     int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window, float scale,
+                     hipStream_t stream) {
+  const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
+  const int st = check_shape(s);
+  if (st != SDPA_OK) return st;
+  // the Delta rows must fit; the split shares or the dS band buffer are used
+  // only when they fit as well (otherwise the plan without them runs)
+  if (workspace_for(s) > kScratchBytes) return SDPA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (workspace_for(s) > 0) {
+    const int e = current_scratch(&ws);
+    if (e != SDPA_OK) return e;
+  }
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, ws, ws != nullptr ? kScratchBytes : 0, B, Hq, group, Lq, Lk, D,
+                  dtype, mask, window, scale, nullptr, stream, nullptr);
 }
 
 }  // extern "C"

@@ -321,3 +321,22 @@ def test_ext_layout_matches_header(tmp_path):
     got = tuple(int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split())
     E = _lib.SdpaExt
     assert got == (ctypes.sizeof(E), E.sinks.offset, E.dsinks.offset, E.cut_row.offset, E.cut_logical.offset)
+
+
+def noalloc(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, window=0, scale=0.125,
+            ptrs=(FAKE,) * 9):
+    """sdpa_bwd_noalloc; pointer order q, k, v, o, dO, lse, dq, dk, dv."""
+    return lib.sdpa_bwd_noalloc(*[ctypes.c_void_p(p) for p in ptrs], B, Hq, group, Lq, Lk, D, dtype, mask, window,
+                                scale, None)
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    # argument errors, and a problem whose Delta rows (4 B Hq Lq bytes) exceed the
+    # fixed 64 MiB scratch, are refused before the first device call (no GPU here)
+    assert noalloc(lib, dtype=7) == INVALID
+    assert noalloc(lib, Hq=6, group=4) == INVALID
+    assert noalloc(lib, D=96) == UNSUPPORTED
+    SCRATCH_LIMIT = -5
+    assert 4 * 1 * 64 * 262145 > 64 << 20
+    assert noalloc(lib, B=1, Hq=64, group=2, Lq=262145, Lk=262145) == SCRATCH_LIMIT
+    assert lib.sdpa_status_string(SCRATCH_LIMIT) != lib.sdpa_status_string(-99)
