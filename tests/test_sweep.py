@@ -1,15 +1,17 @@
-"""A seeded parity sweep over random small problems (run on an MI355X).
+"""A seeded parity sweep over random problems (run on an MI355X).
 
 Modelled on the pages' own parity sweep of the windowed backward (page "Lab
 028 lab detail: Off NVIDIA, you fix the platform yourself", section "Gradient
 parity": fp32 / fp16 / bf16, head dims 64 to 512, GQA ratios, lengths with
-queries shorter than keys, windows from 1 up, causal and not). Every case
+queries shorter than keys, windows from 1 up, causal and not): 160 small
+cases (keys below 700, 400 at D = 512) and 24 longer ones (300 to 3000 keys,
+1500 at D = 512; windows up to 5000). Every case
 draws its shape, mask, window, dtype, layout and optional sinks / cut from a
 seeded generator, runs forward and backward through the library and is
 compared with the fp64 oracle: O and dV within the dtype's relative gate, lse
 within 1e-4 where finite, the same -inf / exact zeros where the oracle has
 them, and dQ, dK, d sinks within the gate plus the error their conditioning
-allows (below). Sizes stay small so the whole sweep runs in about a minute.
+allows (below). Head counts stay small so the whole sweep runs in a few minutes.
 
 Why dQ, dK and d sinks get a conditioning term: they depend on
 Delta_i = <dO_i, O_i>, which the backward forms from the forward's O rounded
@@ -77,10 +79,30 @@ def on_gpu(x, layout):
     return x.transpose(1, 2).contiguous().transpose(1, 2) if layout == "blhd" else x
 
 
+def draw_long(rng):
+    """Longer sequences, as in the pages' sweep (lengths 300 to 3000, queries
+    shorter than keys, windows up to 5000), at few heads so the fp64 oracle
+    stays within seconds per case."""
+    dtype = str(rng.choice(["bf16", "bf16", "f16", "f32"]))
+    D = int(rng.choice([64, 128]) if dtype == "f32" else rng.choice([64, 128, 256, 256, 512]))
+    Hkv = int(rng.choice([1, 2]))
+    group = int(rng.choice([1, 2, 4]))
+    Lk = int(rng.integers(300, 1500 if D == 512 else 3001))
+    Lq = int(rng.choice([Lk, int(rng.integers(1, Lk + 1)), int(rng.integers(1, Lk + 1))]))
+    mask = str(rng.choice(["causal", "causal_window", "causal_window", "window", "none"]))
+    window = int(rng.choice([1, 64, 333, 1000, 2048, 5000])) if "window" in mask else 0
+    scale = float(rng.choice([D ** -0.5, D ** -0.5, 1.0]))
+    return dict(dtype=dtype, D=D, Hq=Hkv * group, Hkv=Hkv, B=1, Lq=Lq, Lk=Lk, mask=mask, window=window,
+                scale=scale, layout=str(rng.choice(["bhld", "bhld", "blhd"])), sinks=bool(rng.random() < 0.2),
+                cut=None)
+
+
+N_LONG = 24
 CASES = [draw(np.random.default_rng(12000 + i)) for i in range(N_CASES)]
+CASES += [draw_long(np.random.default_rng(14000 + i)) for i in range(N_LONG)]
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(N_CASES + N_LONG))
 def test_sweep_case(i):
     c = CASES[i]
     q, k, v, do, sinks = inputs(c, 13000 + i)
