@@ -52,8 +52,10 @@ def tag(w) -> str:
 
 
 def short(name: str) -> str:
-    """Kernel name without its signature and element type: sdpa::kv_kernel<256, 0>."""
+    """Kernel name without its signature and element type: sdpa::qs_kernel<256, 0>, sdpa::kv_kernel<256>."""
     m = re.match(r"_ZN4sdpa\d+(\w+?_kernel)I((?:Li\d+E)+)", name)  # names the tool left mangled
+    if re.match(r"_ZN4sdpa\d+kv_reduce_kernel", name):
+        return "sdpa::kv_reduce_kernel"
     if m:
         ints = re.findall(r"Li(\d+)E", m.group(2))
         keep = 2 if m.group(1) in ("qs_kernel",) else 1
@@ -61,7 +63,7 @@ def short(name: str) -> str:
     name = name.replace("void ", "")
     name = re.sub(r"\(.*", "", name)
     name = re.sub(r"<(\d+), (\d+), [^<>]+>", r"<\1, \2>", name)  # the workloads here are bf16
-    name = re.sub(r"^(sdpa::kv16_kernel)<(\d+), [^<>]+>", r"\1<\2>", name)
+    name = re.sub(r"^(sdpa::kv(?:16)?_kernel)<(\d+), [^<>]+>", r"\1<\2>", name)
     name = re.sub(r"^(sdpa::kv_reduce_kernel)<[^<>]+>", r"\1", name)
     name = re.sub(r"^(sdpa::(dsq|delta)_kernel)<(\d+), [^<>]+>", r"\1<\3>", name)
     return name
@@ -98,7 +100,8 @@ def roles(w):
     r = {
         f"sdpa::qs_kernel<{D}, 0>": ("forward (O, lse)", 4 * D * N, q + 2 * kv, q + row),
         f"sdpa::qs_kernel<{D}, 1>": ("dQ pass (+Delta)", 6 * D * N, 3 * q + 2 * kv + row, q + row),
-        f"sdpa::kv_kernel<{D}, 0>": ("dK/dV pass (32-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
+        f"sdpa::kv_kernel<{D}>": ("dK/dV pass (32-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
+        "sdpa::kv_reduce_kernel": ("dK/dV share reduce (split pass)", 0, 0, 2 * kv),
         f"sdpa::kv16_kernel<{D}>": ("dK/dV pass (16-key waves)", 8 * D * N, 2 * q + 2 * kv + 2 * row, 2 * kv),
     }
     bg = band_geometry(w)
@@ -179,7 +182,7 @@ def main():
         timed[k] = ta
         lines.append(f"| `{k}` | {role} | {len(v)} | {statistics.mean(v):.1f} | {ta:.1f} | {min(v):.1f} | "
                      f"{flop:.4e} | {flop / ta / 1e6:.1f} |")
-    main_k = next((k for k in (f"sdpa::kv16_kernel<{w.D}>", f"sdpa::kv_kernel<{w.D}, 0>") if k in timed), None)
+    main_k = next((k for k in (f"sdpa::kv16_kernel<{w.D}>", f"sdpa::kv_kernel<{w.D}>") if k in timed), None)
     if bl and main_k in timed:
         ev = bl["roofline"]["avg_launch_ms"] * 1e3
         red = next((k for k in tr if "kv_reduce_kernel" in k), None)
@@ -192,8 +195,9 @@ def main():
                   f"{ev:.1f} us; rocprofv3 timed average: {t_ref:.1f} us "
                   f"({abs(ev - t_ref) / t_ref * 100:.1f} % apart)."]
     lines += ["", "Useful FLOP per call: forward 4*D*N, dQ pass 6*D*N (S, dP, dQ), dK/dV pass 8*D*N "
-              "(S, dP, dV, dK); N = allowed (query, key) pairs over all heads. The backward's useful work "
-              "is 10*D*N; the two-pass backward computes 14*D*N (S and dP in both passes)."]
+              "(S, dP, dV, dK), dQ = scale dS K pass 2*D*N; N = allowed (query, key) pairs over all heads. The "
+              "backward's useful work is 10*D*N: with the dS band buffer (Delta pass, dK/dV pass writing dS, "
+              "dS K pass) it computes 10*D*N, with the dQ pass that recomputes S and dP 14*D*N."]
     open(os.path.join(out, f"kernel_stats_{t}.md"), "w").write("\n".join(lines) + "\n")
 
     # ---------------------------------------------------------------- counters
@@ -226,7 +230,8 @@ def main():
         busy = mean_of(1, k, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * timed[k] * 1e-6 * 2.4e9)
         mf = mean_of(1, k, "SQ_INSTS_MFMA")
         valu = mean_of(1, k, "SQ_INSTS_VALU") / mf if mf > 0 else float("nan")
-        bank = mean_of(2, k, "SQ_LDS_BANK_CONFLICT") / mean_of(2, k, "SQ_ACTIVE_INST_LDS")
+        lds_act = mean_of(2, k, "SQ_ACTIVE_INST_LDS")
+        bank = mean_of(2, k, "SQ_LDS_BANK_CONFLICT") / lds_act if lds_act > 0 else float("nan")
         rd = mean_of(3, k, "FETCH_SIZE") * 1024 * fetch_scale
         wr = mean_of(4, k, "WRITE_SIZE") * 1024 * write_scale
         hit, miss = mean_of(5, k, "TCC_HIT_sum"), mean_of(5, k, "TCC_MISS_sum")
