@@ -251,6 +251,9 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws_bytes = sdpa.bwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, q.dtype, w.mask, w.window)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    # the forward's key-range split of small problems (empty: no split)
+    fws = torch.empty(sdpa.fwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, q.dtype, w.mask, w.window),
+                      dtype=torch.uint8, device=dev)
     band = uses_band(w, sdpa, q.dtype)
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = HipEvents()
@@ -261,7 +264,7 @@ def main():
     def step(e=None):
         if e:
             ev.record(e[0], stream)
-        sdpa.sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale, out=o, lse=lse)
+        sdpa.sdpa_fwd_lse(q, k, v, w.mask, w.window, w.scale, out=o, lse=lse, workspace=fws)
         sdpa.sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, w.scale, workspace=ws, out=(dq, dk, dv),
                       events=e[1:] if e else None)
 

@@ -173,6 +173,33 @@ int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float*
                     int32_t dtype, int32_t mask, int32_t window, float scale,
                     const sdpa_ext* ext, hipStream_t stream);
 
+/* Bytes of workspace with which sdpa_fwd_lse_ws splits the key range of each
+ * query tile over 2 or 4 workgroups (0: it would not split). The split
+ * applies to 16-bit calls whose query tiles (128 rows, 64 at D = 512, per
+ * batch and q-head) number at most 128, so that the GPU's 256 CUs would
+ * otherwise sit partly idle: 2 shares, or 4 when they number at most 64,
+ * while the longest query tile still spans two key tiles (64 keys, 32 at
+ * D = 512) per share. Each workgroup keeps the online softmax over its own key range
+ * and writes fp32 partial rows (unnormalised O, used max, row sum); a combine
+ * pass merges them into O and lse. nseg * B * Hq * Lq * (D + 2) float32, so
+ * linear in Lq. Returns 0 for invalid arguments. (A throughput choice, not
+ * part of the pages' method; the result equals the unsplit call's up to fp32
+ * rounding of the merge.) */
+size_t sdpa_fwd_workspace_bytes(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                                int32_t dtype, int32_t mask, int32_t window);
+
+/* sdpa_fwd_lse with a caller-provided device workspace (non-null and 16-byte
+ * aligned when workspace_bytes > 0, else SDPA_ERR_WORKSPACE; null with
+ * workspace_bytes 0 is sdpa_fwd_lse): with at least
+ * sdpa_fwd_workspace_bytes(...) bytes the split above runs, otherwise the
+ * call is sdpa_fwd_lse's. Contiguous tensors only (the strided, sink and cut
+ * forms are sdpa_fwd_lse_ex's). The workspace's contents on entry do not
+ * matter and are clobbered; calls that share it must be stream-ordered. */
+int sdpa_fwd_lse_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                    int32_t dtype, int32_t mask, int32_t window, float scale, hipStream_t stream);
+
 /* Bytes of caller-provided workspace sdpa_bwd needs for this shape: the row
  * terms Delta_i = <dO_i, O_i>, one float32 per query row ([B, Hq, Lq]),
  * rounded up to 256 bytes. Linear in Lq. Returns 0 for empty shapes and for
@@ -196,8 +223,12 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
  *    recomputes the scores (page "Lab 028 lab detail: Off NVIDIA, you fix the
  *    platform yourself", section "What I changed, in plain terms", item 5(a):
  *    dQ summed over the key tiles). At most 8 times the bytes of q, and
- *    linear in Lq at a fixed window.
- * Both apply to calls with contiguous tensors and no cut, and only when the
+ *    linear in Lq at a fixed window;
+ *  - when there is no band buffer, the dQ pass's key-range split: the same
+ *    split and condition as sdpa_fwd_workspace_bytes, with fp32 dQ partials
+ *    (nseg * B * Hq * Lq * D float32) summed by a combine pass; they share
+ *    their memory with the dK/dV shares, which are written after that pass.
+ * All of them apply to calls with contiguous tensors and no cut, and only when the
  * workspace given holds them; with sdpa_bwd_workspace_bytes(...) bytes the
  * results are the same up to fp32 summation order. Returns 0 for empty
  * shapes and invalid arguments. (Both are throughput choices, not part of
@@ -275,7 +306,7 @@ int sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
 /* Static description of a status code. */
 const char* sdpa_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 400. */
+/* ABI version of this header (major * 100 + minor): 500. */
 int sdpa_abi_version(void);
 
 #ifdef __cplusplus

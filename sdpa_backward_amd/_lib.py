@@ -30,8 +30,9 @@ STATUS = {0: "SDPA_OK", -1: "SDPA_ERR_INVALID_ARG", -2: "SDPA_ERR_UNSUPPORTED", 
 DTYPE = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
 MASK = {"none": 0, "causal": 1, "causal_window": 2, "window": 3}
 
-EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed", "sdpa_bwd_noalloc",
-           "sdpa_bwd_workspace_bytes", "sdpa_bwd_workspace_bytes_ex", "sdpa_status_string", "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_fwd_lse_ws", "sdpa_fwd_workspace_bytes", "sdpa_bwd",
+           "sdpa_bwd_ex", "sdpa_bwd_timed", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes",
+           "sdpa_bwd_workspace_bytes_ex", "sdpa_status_string", "sdpa_abi_version")
 
 _lib = None
 
@@ -67,12 +68,16 @@ def load(path: str = LIB_PATH):
     ext = ctypes.POINTER(SdpaExt)
     lib.sdpa_fwd_lse.argtypes = [p, p, p, p, p] + dims + [p]
     lib.sdpa_fwd_lse_ex.argtypes = [p, p, p, p, p] + dims + [ext, p]
+    lib.sdpa_fwd_lse_ws.argtypes = [p, p, p, p, p, p, sz] + dims + [p]
     lib.sdpa_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p]
     lib.sdpa_bwd_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [ext, p]
     lib.sdpa_bwd_timed.argtypes = [p, p, p, p, p, p, p, p, p, p, sz] + dims + [p, ctypes.POINTER(ctypes.c_void_p)]
     lib.sdpa_bwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, p] + dims + [p]
-    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed", "sdpa_bwd_noalloc"):
+    for f in ("sdpa_fwd_lse", "sdpa_fwd_lse_ex", "sdpa_fwd_lse_ws", "sdpa_bwd", "sdpa_bwd_ex", "sdpa_bwd_timed",
+              "sdpa_bwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.sdpa_fwd_workspace_bytes.argtypes = [i32] * 9
+    lib.sdpa_fwd_workspace_bytes.restype = sz
     lib.sdpa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sdpa_bwd_workspace_bytes.restype = sz
     lib.sdpa_bwd_workspace_bytes_ex.argtypes = [i32] * 9
@@ -179,7 +184,14 @@ def _out_like(t, out):
     return o
 
 
-def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None, sinks=None, cut=None):
+def fwd_workspace_bytes(B, Hq, group, Lq, Lk, D, dtype, mask="causal", window=0):
+    """Workspace with which the forward splits each query tile's key range (small problems; 0: no split)."""
+    m, w = _mask_args(mask, window)
+    return int(load().sdpa_fwd_workspace_bytes(B, Hq, group, Lq, Lk, D, DTYPE[dtype], m, w))
+
+
+def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=None, sinks=None, cut=None,
+                 workspace=None):
     """O [B,Hq,Lq,D] (q.dtype) and lse [B,Hq,Lq] (float32, natural log).
 
     k, v are [B, Hkv, Lk, D]; with Lk != Lq the queries are the last Lq key
@@ -190,7 +202,9 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
     prefix-sharing mask), or (r0, c0, c1, True): besides, rows from r0 on
     place the keys before c0 at their position plus c1 - c0 (the window at
     logical positions). O takes q's strides when q is dense (e.g. a
-    [B, L, H, D] layout stays one)."""
+    [B, L, H, D] layout stays one). workspace: device bytes for the key-range
+    split of small problems (contiguous tensors, no sinks, no cut); None
+    allocates fwd_workspace_bytes(...) of them, an empty tensor runs unsplit."""
     B, Hq, group, L, Lk, D = _validate(q, k, v)
     sinks = _sinks_arg(sinks, q, Hq)
     k, v = _same_rows(k, v)
@@ -200,6 +214,16 @@ def sdpa_fwd_lse(q, k, v, mask="causal", window=0, scale=None, out=None, lse=Non
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
     if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, L]")
+    if sinks is None and cut is None and all(t.is_contiguous() for t in (q, k, v, o)):
+        if workspace is None:
+            need = fwd_workspace_bytes(B, Hq, group, L, Lk, D, q.dtype, mask, window)
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = load().sdpa_fwd_lse_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    _ptr(workspace) if nbytes > 0 else ctypes.c_void_p(0), nbytes, B, Hq, group, L,
+                                    Lk, D, DTYPE[q.dtype], m, w, scale, _stream(q.device))
+        _check("sdpa_fwd_lse_ws", st)
+        return o, lse
     ext, _keep = _ext(_strides(q, k, v, o), sinks, cut=cut)
     st = load().sdpa_fwd_lse_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, group, L, Lk, D,
                                 DTYPE[q.dtype], m, w, scale, ext, _stream(q.device))

@@ -27,6 +27,15 @@
 //        dQ^T += K^T . dS^T                 A: K (transposed reads) B: dS^T (C tile reused)
 // S, P, dP stay fp32; only P and dS are rounded to the input type as MFMA operands
 // (section "fp32 score tiles" of the Lab 028 page).
+//
+// Small grids (fewer workgroups than CUs): each query tile's key tiles are
+// split into nseg consecutive ranges, one workgroup each. A workgroup then
+// writes fp32 partial results instead of its outputs: the forward its
+// unnormalised O rows with their used max m and row sum l, the dQ pass its
+// unscaled dQ rows; a combine pass merges them (O = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s with M = max_s m_s, and lse from M and that sum; dQ
+// = scale sum_s dQ_s), the split-softmax merge of the online softmax.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -78,7 +87,8 @@ __global__ void __launch_bounds__(256, 1)
 qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
           const E* __restrict__ O, const E* __restrict__ dO, float* __restrict__ LSE,
           float* __restrict__ Delta, E* __restrict__ Out, const float* __restrict__ Sinks, int Hq, int group,
-          int Lq, int Lk, int dlo, int dhi, Cut cut_arg, float scale, float scale_log2, AllStrides st_arg) {
+          int Lq, int Lk, int dlo, int dhi, Cut cut_arg, float scale, float scale_log2, AllStrides st_arg,
+          int nseg, float* __restrict__ part) {
   using C = QsCfg<D>;
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
@@ -104,8 +114,9 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   const int qwi = w / C::DS, dsi = w % C::DS, dw0 = dsi * DW;
   const int nqt = (Lq + C::BQ - 1) / C::BQ;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = nqt - 1 - logical % nqt;  // longest causal rows first within a head
-  const int h = (logical / nqt) % Hq, b = logical / (nqt * Hq);
+  const int seg = logical % nseg, lw = logical / nseg;  // key range seg of query tile lw
+  const int qt = nqt - 1 - lw % nqt;  // longest causal rows first within a head
+  const int h = (lw / nqt) % Hq, b = lw / (nqt * Hq);
   const int Hkv = Hq / group, g = h / group;
   const size_t hrow = (size_t)b * Hq + h;  // lse / Delta row block
   const E* Kg = DENSE ? K + ((size_t)b * Hkv + g) * Lk * D : K + b * st.k.b + g * st.k.h;
@@ -154,7 +165,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
     dlt = dot + __shfl_xor(dot, 32);
     lse2 = qok ? LSE[hrow * Lq + qi] * kLog2e : 0.f;  // -inf for a row with no key (then every p is masked)
-    if (qok && dsi == 0 && hh == 0) Delta[hrow * Lq + qi] = dlt;
+    if (qok && dsi == 0 && hh == 0 && seg == 0) Delta[hrow * Lq + qi] = dlt;
   }
 
   f32x16 acc[NDB];
@@ -164,7 +175,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   if constexpr (MODE == QS_FWD) {
     // a sink logit joins the normalizer from the start: it becomes the used
     // max, contributing exp2(m - m) = 1 to the sum (and nothing to O)
-    if (Sinks != nullptr) {
+    if (Sinks != nullptr && seg == 0) {
       const float sg = Sinks[h] * kLog2e;
       if (sg != -INFINITY) m = sg, lsum = 1.f;
     }
@@ -188,6 +199,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
   const int nt = nt2 + max(0, kt_hi - kt_lo + 1);
   auto kt_of = [&](int t) { return t < nt2 ? kt2_lo + t : kt_lo + (t - nt2); };
+  // this workgroup's tiles [t_b, t_e) of the nt (all of them without a split)
+  const int t_b = (int)((long long)seg * nt / nseg), t_e = (int)((long long)(seg + 1) * nt / nseg);
   const int wr0 = iw0, wr1 = min(iw0 + 31, Lq - 1);  // this wave's rows (wr1 < wr0: none)
 
   auto step = [&](int t, const E* Kc, const E* Vc, E* Kn, E* Vn) {
@@ -199,7 +212,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // (it writes LDS), so the operand reads are software-pipelined by hand and
     // the loads slot in between them. On the last tile the resources cover no
     // rows and the loads read nothing.
-    const bool more = t + 1 < nt;
+    const bool more = t + 1 < t_e;
     const int jn = more ? kt_of(t + 1) * BK : 0;
     const auto krs = ldk.rsrc(Kg + (long long)jn * st.k.l, more ? Lk - jn : 0);
     const auto vrs = ldv.rsrc(Vg + (long long)jn * st.v.l, more ? Lk - jn : 0);
@@ -353,8 +366,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
   };
 
-  if (nt > 0) {  // first tile (uniform over the workgroup)
-    const int j0 = kt_of(0) * BK;
+  if (t_e > t_b) {  // first tile (uniform over the workgroup)
+    const int j0 = kt_of(t_b) * BK;
     zero_lds(kb0, C::TILE, tid);
     zero_lds(kb1, C::TILE, tid);
     zero_lds(vb0, C::TILE, tid);
@@ -364,15 +377,32 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     ldv.issue(vb0, Vg + (long long)j0 * st.v.l, Lk - j0, w);
     wait_all_and_barrier();
   }
-  for (int t = 0; t < nt; t += 2) {
+  for (int t = t_b; t < t_e; t += 2) {
     step(t, kb0, vb0, kb1, vb1);
     wait_all_and_barrier();
-    if (t + 1 >= nt) break;
+    if (t + 1 >= t_e) break;
     step(t + 1, kb1, vb1, kb0, vb0);
     wait_all_and_barrier();
   }
 
   if (!qok) return;
+  if (nseg > 1) {  // fp32 partial rows (and the forward's m, l) for the combine pass
+    const size_t rows = (size_t)(gridDim.x / nseg / nqt) * Lq;  // B * Hq * Lq: one partial's rows
+    float* prow = part + ((size_t)seg * rows + hrow * Lq + qi) * D;
+#pragma unroll
+    for (int d = 0; d < NDB; d++)
+#pragma unroll
+      for (int blk = 0; blk < 4; blk++) {
+        const f32x4 v = {acc[d][4 * blk], acc[d][4 * blk + 1], acc[d][4 * blk + 2], acc[d][4 * blk + 3]};
+        *(f32x4*)(prow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+      }
+    if (MODE == QS_FWD && dsi == 0 && hh == 0) {
+      float* pml = part + (size_t)nseg * rows * D + ((size_t)seg * rows + hrow * Lq + qi) * 2;
+      pml[0] = m;
+      pml[1] = lsum;
+    }
+    return;
+  }
   const Strides so = MODE == QS_FWD ? st.o : st.dq;
   E* orow = Out + b * so.b + h * so.h + (long long)qi * so.l;
   if constexpr (MODE == QS_FWD) {
@@ -400,28 +430,97 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   }
 }
 
+// Combine pass of a split call: one thread per 8 columns of a row (rows =
+// B * Hq * Lq). Forward: O and lse from the nseg partial (O, m, l) of the row,
+// as the online softmax would have reached them over all its key tiles; a row
+// whose partials saw no key (and no sink) gets O = 0 and lse = -inf. dQ pass:
+// scale times the sum of the partials, in segment order.
+template <int D, int MODE, typename E>
+__global__ void __launch_bounds__(256)
+qs_combine_kernel(const float* __restrict__ part, E* __restrict__ Out, float* __restrict__ LSE, int nseg,
+                  long long rows, int Hq, int Lq, Strides so, float scale) {
+  using ex8 = typename Vec<E>::x8;
+  constexpr int C8 = D / 8;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * C8) return;
+  const long long row = idx / C8;
+  const int c = (int)(idx % C8) * 8;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float mul = scale, M = -INFINITY, L = 0.f;
+  if constexpr (MODE == QS_FWD) {
+    const float* pml = part + (size_t)nseg * rows * D;
+    for (int sg = 0; sg < nseg; sg++) M = fmaxf(M, pml[((size_t)sg * rows + row) * 2]);
+    for (int sg = 0; sg < nseg; sg++) {
+      const float ms = pml[((size_t)sg * rows + row) * 2], ls = pml[((size_t)sg * rows + row) * 2 + 1];
+      if (ls > 0.f) L += __builtin_amdgcn_exp2f(ms - M) * ls;
+    }
+    mul = L > 0.f ? 1.f / L : 0.f;
+  }
+  for (int sg = 0; sg < nseg; sg++) {
+    float wgt = 1.f;
+    if constexpr (MODE == QS_FWD) {
+      const float ms = part[(size_t)nseg * rows * D + ((size_t)sg * rows + row) * 2];
+      wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    }
+    const f32x4* p = (const f32x4*)(part + ((size_t)sg * rows + row) * D + c);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int j = 0; j < 4; j++) o[j] += wgt * a[j], o[4 + j] += wgt * b[j];
+  }
+  ex8 v;
+#pragma unroll
+  for (int j = 0; j < 8; j++) v[j] = (E)(o[j] * mul);
+  const int bb = (int)(row / ((long long)Hq * Lq)), h = (int)(row / Lq % Hq), i = (int)(row % Lq);
+  *(ex8*)(Out + bb * so.b + h * so.h + (long long)i * so.l + c) = v;
+  if (MODE == QS_FWD && c == 0) LSE[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Key-range shares per query tile for a dense 16-bit call (1: no split): when
+// the query tiles alone give at most half as many workgroups as the 256 CUs,
+// the largest power of two up to 4 that keeps the grid within 256 workgroups
+// and the longest query tile at two or more key tiles per share.
+template <int D>
+int qs_split_shares(int B, int Hq, int Lq, int Lk, int dlo, int dhi, bool dense) {
+  using C = QsCfg<D>;
+  if (!dense || Lq <= 0 || Lk <= 0 || dlo > dhi) return 1;
+  const long long nwg = (long long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
+  const long long width = std::min<long long>(Lk, (long long)C::BQ - 1 + dhi - dlo + 1);  // keys of a query tile
+  const long long ntmax = (width + C::BK - 1) / C::BK + 1;
+  int n = 1;
+  while (n < 4 && nwg * 2 * n <= 256 && ntmax >= 4 * n) n *= 2;
+  return n;
+}
+
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk,
-                     int dlo, int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream) {
+                     int dlo, int dhi, Cut cut, float scale, const AllStrides& st, int nseg, float* part,
+                     hipStream_t stream) {
   using C = QsCfg<D>;
-  const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B;
+  if (nseg < 1 || (nseg > 1 && part == nullptr)) return hipErrorInvalidValue;
+  const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B * nseg;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   auto kernel = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1 ? qs_kernel<D, MODE, E, true> : qs_kernel<D, MODE, E, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                      (const E*)o, (const E*)dO, lse, delta, (E*)out, sinks, Hq, group, Lq, Lk, dlo, dhi, cut,
-                     scale, scale * kLog2e, st);
+                     scale, scale * kLog2e, st, nseg, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nseg == 1) return e;
+  const long long rows = (long long)B * Hq * Lq, threads = rows * (D / 8);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((qs_combine_kernel<D, MODE, E>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)part, (E*)out, lse, nseg, rows, Hq, Lq, MODE == QS_FWD ? st.o : st.dq, scale);
   return hipGetLastError();
 }
 
 #define SDPA_INST_QS(D, E)                                                                                  \
   template hipError_t launch_qs<D, QS_FWD, E>(const void*, const void*, const void*, const void*, const void*, \
                                               float*, float*, void*, const float*, int, int, int, int, int, int, \
-                                              int, Cut, float, const AllStrides&, hipStream_t);                \
+                                              int, Cut, float, const AllStrides&, int, float*, hipStream_t);   \
   template hipError_t launch_qs<D, QS_DQ, E>(const void*, const void*, const void*, const void*, const void*,  \
                                              float*, float*, void*, const float*, int, int, int, int, int, int,  \
-                                             int, Cut, float, const AllStrides&, hipStream_t);
+                                             int, Cut, float, const AllStrides&, int, float*, hipStream_t);
 SDPA_INST_QS(64, bf16)
 SDPA_INST_QS(128, bf16)
 SDPA_INST_QS(256, bf16)
@@ -430,5 +529,9 @@ SDPA_INST_QS(64, f16)
 SDPA_INST_QS(128, f16)
 SDPA_INST_QS(256, f16)
 SDPA_INST_QS(512, f16)
+template int qs_split_shares<64>(int, int, int, int, int, int, bool);
+template int qs_split_shares<128>(int, int, int, int, int, int, bool);
+template int qs_split_shares<256>(int, int, int, int, int, int, bool);
+template int qs_split_shares<512>(int, int, int, int, int, int, bool);
 
 }  // namespace sdpa

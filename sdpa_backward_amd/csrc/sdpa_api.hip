@@ -20,7 +20,9 @@ enum { QS_FWD = 0, QS_DQ = 1 };
 template <int D, int MODE, typename E>
 hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o, const void* dO, float* lse,
                      float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk, int dlo,
-                     int dhi, Cut cut, float scale, const AllStrides& st, hipStream_t stream);
+                     int dhi, Cut cut, float scale, const AllStrides& st, int nseg, float* part, hipStream_t stream);
+template <int D>
+int qs_split_shares(int B, int Hq, int Lq, int Lk, int dlo, int dhi, bool dense);
 template <int D, typename E>
 hipError_t launch_kv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
@@ -62,14 +64,18 @@ struct BwdPlan {
   int nseg;
   void* band;    // dS band buffer (bounded band, D = 256, wide), or null
   int nqb, nkb;  // its row blocks and key tiles per block
+  float* qpart;  // fp32 dQ partials of the dQ pass's key-range split (qseg > 1), or null
+  int qseg;
 };
 
 // 16-bit backward.
 //   band buffer: Delta pass, dK/dV pass that also writes dS^T for the band,
 //                dQ = scale dS K from that buffer (no score recomputed);
-//   otherwise:   dQ pass (recomputes S and dP, also writes Delta), then the
-//                dK/dV pass (split into nseg shares summed into part when
-//                nseg > 1).
+//   otherwise:   dQ pass (recomputes S and dP, also writes Delta; each query
+//                tile's key range split into qseg shares when qseg > 1), then
+//                the dK/dV pass (split into nseg shares summed into part when
+//                nseg > 1; part may reuse the dQ partials' memory, which the
+//                dQ pass's combine has read by then).
 template <int D, typename E>
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
@@ -91,7 +97,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     }
   }
   e = launch_qs<D, QS_DQ, E>(q, k, v, o, dO, const_cast<float*>(lse), delta, dq, nullptr, B, Hq, group, Lq, Lk, dlo,
-                             dhi, cut, scale, st, stream);
+                             dhi, cut, scale, st, plan.qseg, plan.qpart, stream);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, stream)) != hipSuccess) return e;
   // 16-key waves (v_mfma_f32_16x16x32): at D = 512 always (32-key waves would
@@ -194,6 +200,28 @@ int split_shares(const Shape& s, bool dense) {
 
 bool wide_call(const Shape& s, bool dense) { return s.D == 256 && dense && split_shares(s, dense) == 1; }
 
+// Key-range shares per query tile of the forward and the dQ pass for a 16-bit
+// call (1: none), and the bytes of their fp32 partials (the forward's with a
+// used max and row sum per row).
+int qsplit_shares(const Shape& s, bool dense) {
+  if (s.dtype == SDPA_F32 || s.no_rows() || s.no_keys()) return 1;
+  int dlo, dhi;
+  s.band(dlo, dhi);
+  switch (s.D) {
+    case 64: return sdpa::qs_split_shares<64>(s.B, s.Hq, s.Lq, s.Lk, dlo, dhi, dense);
+    case 128: return sdpa::qs_split_shares<128>(s.B, s.Hq, s.Lq, s.Lk, dlo, dhi, dense);
+    case 256: return sdpa::qs_split_shares<256>(s.B, s.Hq, s.Lq, s.Lk, dlo, dhi, dense);
+    case 512: return sdpa::qs_split_shares<512>(s.B, s.Hq, s.Lq, s.Lk, dlo, dhi, dense);
+    default: return 1;
+  }
+}
+
+size_t qsplit_bytes(const Shape& s, int nseg, bool forward) {
+  if (nseg <= 1) return 0;
+  const size_t rows = (size_t)s.B * s.Hq * s.Lq;
+  return align_up((size_t)nseg * rows * ((size_t)s.D + (forward ? 2 : 0)) * sizeof(float));
+}
+
 // Bytes of the split's fp32 dK and dV shares.
 size_t split_bytes(const Shape& s, int nseg) {
   return nseg > 1 ? align_up(2 * (size_t)nseg * s.B * (s.Hq / s.group) * s.Lk * s.D * sizeof(float)) : 0;
@@ -289,7 +317,7 @@ bool ptr_ok(const void* p, bool used) { return !used || (p != nullptr && aligned
 
 extern "C" {
 
-int sdpa_abi_version(void) { return 400; }
+int sdpa_abi_version(void) { return 500; }
 
 const char* sdpa_status_string(int status) {
   switch (status) {
@@ -319,12 +347,24 @@ size_t sdpa_bwd_workspace_bytes_ex(int32_t B, int32_t Hq, int32_t group, int32_t
   int dlo, dhi, nqb, nkb;
   s.band(dlo, dhi);
   const size_t band = wide_call(s, true) ? band_bytes(s, dlo, dhi, nqb, nkb) : 0;
-  return base + std::max(split_bytes(s, split_shares(s, true)), band);
+  const size_t dq_split = band > 0 ? 0 : qsplit_bytes(s, qsplit_shares(s, true), false);
+  return base + std::max(std::max(split_bytes(s, split_shares(s, true)), band), dq_split);
 }
 
-int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
-                    int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
-                    float scale, const sdpa_ext* ext, hipStream_t stream) {
+size_t sdpa_fwd_workspace_bytes(int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                                int32_t dtype, int32_t mask, int32_t window) {
+  Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, 1.f};
+  if (check_shape(s) != SDPA_OK) return 0;
+  return qsplit_bytes(s, qsplit_shares(s, true), true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+             int32_t dtype, int32_t mask, int32_t window, float scale, const sdpa_ext* ext, hipStream_t stream) {
   const Shape s{B, Hq, group, Lq, Lk, D, dtype, mask, window, scale};
   int st = check_shape(s);
   if (st != SDPA_OK) return st;
@@ -340,12 +380,18 @@ int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float*
   if ((st = take_cut(s, ext, cut)) != SDPA_OK) return st;
   int dlo, dhi;
   s.band(dlo, dhi);
+  if (workspace_bytes > 0 && (workspace == nullptr || !aligned16(workspace))) return SDPA_ERR_WORKSPACE;
+  // the key-range split of a small dense call, when the workspace holds its partials
+  const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
+  int qseg = qsplit_shares(s, dense);
+  if (qseg > 1 && workspace_bytes < qsplit_bytes(s, qseg, true)) qseg = 1;
+  float* part = qseg > 1 ? static_cast<float*>(workspace) : nullptr;
   switch (dtype * 1000 + D) {
 #define SDPA_FWD_CASE(DT, E, DD)                                                                          \
   case DT * 1000 + DD:                                                                                    \
     return to_status(sdpa::launch_qs<DD, sdpa::QS_FWD, E>(q, k, v, nullptr, nullptr, lse, nullptr, o, sinks, \
                                                           B, Hq, group, Lq, Lk, dlo, dhi, cut, scale, str,    \
-                                                          stream));
+                                                          qseg, part, stream));
     SDPA_FWD_CASE(SDPA_BF16, bf16, 64)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 128)
     SDPA_FWD_CASE(SDPA_BF16, bf16, 256)
@@ -365,10 +411,27 @@ int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float*
   return SDPA_ERR_UNSUPPORTED;
 }
 
+}  // namespace
+
+extern "C" {
+
+int sdpa_fwd_lse_ex(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
+                    int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
+                    float scale, const sdpa_ext* ext, hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, nullptr, 0, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, ext, stream);
+}
+
+int sdpa_fwd_lse_ws(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int32_t B, int32_t Hq, int32_t group, int32_t Lq, int32_t Lk, int32_t D,
+                    int32_t dtype, int32_t mask, int32_t window, float scale, hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale,
+                  nullptr, stream);
+}
+
 int sdpa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B, int32_t Hq,
                  int32_t group, int32_t Lq, int32_t Lk, int32_t D, int32_t dtype, int32_t mask, int32_t window,
                  float scale, hipStream_t stream) {
-  return sdpa_fwd_lse_ex(q, k, v, o, lse, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr, stream);
+  return fwd_impl(q, k, v, o, lse, nullptr, 0, B, Hq, group, Lq, Lk, D, dtype, mask, window, scale, nullptr, stream);
 }
 
 }  // extern "C"
@@ -408,7 +471,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   // band, when the workspace holds them (after the Delta rows)
   const bool dense = is_dense_call(s, str) && cut.c0 == cut.c1;
   char* extra = static_cast<char*>(workspace) + need;
-  sdpa::BwdPlan plan{dense && split_shares(s, dense) == 1, nullptr, split_shares(s, dense), nullptr, 0, 0};
+  sdpa::BwdPlan plan{dense && split_shares(s, dense) == 1, nullptr, split_shares(s, dense), nullptr, 0, 0,
+                     nullptr, qsplit_shares(s, dense)};
   if (plan.nseg > 1 && workspace_bytes < need + split_bytes(s, plan.nseg)) plan.nseg = 1;
   if (plan.nseg > 1) plan.part = reinterpret_cast<float*>(extra);
   if (wide_call(s, dense)) {
@@ -416,6 +480,11 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     const size_t bb = band_bytes(s, dlo, dhi, nqb, nkb);
     if (bb > 0 && workspace_bytes >= need + bb) plan.band = extra, plan.nqb = nqb, plan.nkb = nkb;
   }
+  // the dQ pass's key-range split (not with the band buffer, which forms dQ
+  // without that pass); its partials share the memory after the Delta rows
+  // with the dK/dV shares, which are written only after its combine
+  if (plan.band != nullptr || workspace_bytes < need + qsplit_bytes(s, plan.qseg, false)) plan.qseg = 1;
+  if (plan.qseg > 1) plan.qpart = reinterpret_cast<float*>(extra);
   hipError_t e;
   switch (dtype * 1000 + D) {
 #define SDPA_BWD_CASE(DT, E, DD)                                                                              \

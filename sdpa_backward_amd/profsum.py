@@ -58,7 +58,7 @@ def short(name: str) -> str:
         return "sdpa::kv_reduce_kernel"
     if m:
         ints = re.findall(r"Li(\d+)E", m.group(2))
-        keep = 2 if m.group(1) in ("qs_kernel",) else 1
+        keep = 2 if m.group(1) in ("qs_kernel", "qs_combine_kernel") else 1
         return f"sdpa::{m.group(1)}<{', '.join(ints[:keep])}>"
     name = name.replace("void ", "")
     name = re.sub(r"\(.*", "", name)
@@ -88,6 +88,15 @@ def band_geometry(w):
     return (-(-w.L // 128), nkb) if nkb * 64 <= 8 * w.D else None
 
 
+def key_range_shares(w):
+    """Shares of the forward's (and, without the dS band buffer, the dQ pass's) key-range split
+    on this workload (1: none), from the library's own workspace rule."""
+    import torch
+    from sdpa_backward_amd import fwd_workspace_bytes
+    b = fwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, torch.bfloat16, w.mask, w.window)
+    return b // (w.B * w.Hq * w.L * (w.D + 2) * 4) if b else 1
+
+
 def roles(w):
     """kernel-name prefix -> (role, useful FLOP per call, algorithmic bytes read, written)."""
     from bench import allowed_pairs
@@ -111,6 +120,15 @@ def roles(w):
         r[f"sdpa::kv16_kernel<{D}>"] = ("dK/dV pass writing dS (16-key waves)", 8 * D * N,
                                         2 * q + 2 * kv + 2 * row, 2 * kv + band)
         r[f"sdpa::dsq_kernel<{D}>"] = ("dQ = scale dS K pass", 2 * D * N, band + kv, q)
+    ns = key_range_shares(w)
+    if ns > 1:  # small grid: each query tile's key range split into ns shares, fp32 partials merged
+        part = ns * w.B * w.Hq * w.L * 4
+        r[f"sdpa::qs_kernel<{D}, 0>"] = (f"forward, key range split in {ns}", 4 * D * N, q + 2 * kv, part * (D + 2))
+        r[f"sdpa::qs_combine_kernel<{D}, 0>"] = ("forward split merge (O, lse)", 0, part * (D + 2), q + row)
+        if not bg:
+            r[f"sdpa::qs_kernel<{D}, 1>"] = (f"dQ pass (+Delta), key range split in {ns}", 6 * D * N,
+                                             3 * q + 2 * kv + row, part * D + row)
+            r[f"sdpa::qs_combine_kernel<{D}, 1>"] = ("dQ split merge", 0, part * D, q)
     return r
 
 

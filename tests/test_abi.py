@@ -58,7 +58,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 400
+    assert lib.sdpa_abi_version() == 500
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
         assert isinstance(lib.sdpa_status_string(code), bytes)
     assert lib.sdpa_status_string(OK) == b"ok"
@@ -267,6 +267,52 @@ def test_split_workspace_sizes(lib):
     assert ex(1, 8, 2, 2048, 0, 256, BF16) == delta(1, 8, 2048)
     assert ex(0, 8, 2, 2048, 2048, 256, BF16) == 0
     assert ex(1, 8, 3, 2048, 2048, 256, BF16) == 0
+
+
+def test_forward_split_workspace_sizes(lib):
+    fb = lib.sdpa_fwd_workspace_bytes
+    fb.argtypes = [ctypes.c_int32] * 9
+    fb.restype = ctypes.c_size_t
+    ex = lib.sdpa_bwd_workspace_bytes_ex
+    ex.argtypes = [ctypes.c_int32] * 9
+    ex.restype = ctypes.c_size_t
+    delta = lambda B, Hq, Lq: -(-(B * Hq * Lq * 4) // 256) * 256
+    # causal L = 2048, D = 256, 8 q-heads: 16 query tiles of 128 rows x 8 = 128
+    # workgroups -> 2 key-range shares of fp32 (O row, used max, row sum)
+    assert fb(1, 8, 2, 2048, 2048, 256, BF16, CAUSAL, 0) == 2 * 8 * 2048 * (256 + 2) * 4
+    assert fb(1, 8, 2, 2048, 2048, 256, F16, CAUSAL, 0) == 2 * 8 * 2048 * (256 + 2) * 4
+    # at most 64 workgroups (D = 512 tiles hold 64 rows: 16 x 2 = 32): 4 shares
+    assert fb(1, 2, 1, 1024, 1024, 512, BF16, CAUSAL, 0) == 4 * 2 * 1024 * (512 + 2) * 4
+    # the longest query tile needs two key tiles per share: window 64 spans
+    # 191 keys (4 tiles of 64) -> 2 shares; window 1 spans 128 keys (3) -> none
+    assert fb(1, 8, 2, 2048, 2048, 256, BF16, WINDOW, 64) == 2 * 8 * 2048 * (256 + 2) * 4
+    assert fb(1, 8, 2, 2048, 2048, 256, BF16, WINDOW, 1) == 0
+    # grids that fill the GPU, fp32, no keys, invalid shapes: none
+    assert fb(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 1024) == 0
+    assert fb(2, 8, 1, 2048, 2048, 256, BF16, CAUSAL, 0) == 0   # 256 workgroups
+    assert fb(1, 9, 1, 2048, 2048, 256, BF16, CAUSAL, 0) == 0   # 144: two shares would exceed 256
+    assert fb(1, 2, 2, 128, 128, 64, F32, CAUSAL, 0) == 0
+    assert fb(1, 8, 2, 2048, 0, 256, BF16, CAUSAL, 0) == 0
+    assert fb(1, 8, 3, 2048, 2048, 256, BF16, CAUSAL, 0) == 0
+    # the backward's dQ pass splits the same way (fp32 dQ rows only); its
+    # partials and the dK/dV shares share memory, so the larger one counts
+    assert ex(1, 2, 1, 1024, 1024, 512, BF16, CAUSAL, 0) == delta(1, 2, 1024) + 4 * 2 * 1024 * 512 * 4
+    assert ex(1, 8, 2, 2048, 2048, 256, BF16, CAUSAL, 0) == delta(1, 8, 2048) + 2 * 4 * 4 * 2048 * 256 * 4
+
+
+def test_forward_workspace_errors(lib):
+    fws = lib.sdpa_fwd_lse_ws
+    fws.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [ctypes.c_int32] * 9 + [ctypes.c_float,
+                                                                                          ctypes.c_void_p]
+    fws.restype = ctypes.c_int
+    p = [ctypes.c_void_p(FAKE)] * 5
+    dims = (1, 8, 2, 2048, 2048, 256, BF16, CAUSAL, 0, 0.0625)
+    # a workspace of nonzero size must be non-null and 16-byte aligned; the
+    # shape is checked first
+    assert fws(*p, None, 1024, *dims, None) == WORKSPACE
+    assert fws(*p, ctypes.c_void_p(FAKE + 8), 1024, *dims, None) == WORKSPACE
+    assert fws(*p, None, 1024, 1, 8, 2, 2048, 2048, 256, 3, CAUSAL, 0, 0.0625, None) == INVALID
+    assert fws(*[ctypes.c_void_p(0)] * 5, None, 0, 0, 8, 2, 2048, 2048, 256, BF16, CAUSAL, 0, 0.0625, None) == OK
 
 
 def test_band_workspace_sizes(lib):

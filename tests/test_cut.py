@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from sdpa_backward_amd import attention, sdpa_bwd, sdpa_fwd_lse
+from sdpa_backward_amd import attention, sdpa_bwd, sdpa_fwd_lse, workspace_bytes
 from tests.oracle_pins import rel_fro
 from tests.test_parity import DEV, LSE_TOL, TOL, _np
 from workloads import MASK_CAUSAL, MASK_NONE, MASK_TWO_SIDED, MASK_WINDOW, Workload, make_inputs
@@ -81,12 +81,18 @@ def test_shared_prompt_pass_equals_two_branches():
     ia = torch.arange(P + Rc, device=DEV)
     ib = torch.cat([torch.arange(P, device=DEV), torch.arange(P + Rc, L, device=DEV)])
     sel = lambda t, idx: t.index_select(2, idx).contiguous()
-    oa, la = sdpa_fwd_lse(sel(q, ia), sel(k, ia), sel(v, ia), "causal")
-    ga = sdpa_bwd(sel(q, ia), sel(k, ia), sel(v, ia), oa, sel(do, ia), la, "causal")
+    # the branch passes run unsplit, as the cut pass does (calls with a cut
+    # never split their key ranges or dK/dV shares): an empty forward
+    # workspace and a backward workspace with only the Delta rows, so that
+    # tiles and summation order match
+    fws = torch.empty(0, dtype=torch.uint8, device=DEV)
+    bws = lambda n: torch.empty(workspace_bytes(1, 4, n, D, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    oa, la = sdpa_fwd_lse(sel(q, ia), sel(k, ia), sel(v, ia), "causal", workspace=fws)
+    ga = sdpa_bwd(sel(q, ia), sel(k, ia), sel(v, ia), oa, sel(do, ia), la, "causal", workspace=bws(P + Rc))
     do_b = sel(do, ib)
     do_b[:, :, :P] = 0
-    ob, lb = sdpa_fwd_lse(sel(q, ib), sel(k, ib), sel(v, ib), "causal")
-    gb = sdpa_bwd(sel(q, ib), sel(k, ib), sel(v, ib), ob, do_b, lb, "causal")
+    ob, lb = sdpa_fwd_lse(sel(q, ib), sel(k, ib), sel(v, ib), "causal", workspace=fws)
+    gb = sdpa_bwd(sel(q, ib), sel(k, ib), sel(v, ib), ob, do_b, lb, "causal", workspace=bws(P + Rr))
     torch.cuda.synchronize()
     # rows of [prompt; chosen] see the same keys at the same positions: bitwise equal
     assert torch.equal(o[:, :, :P + Rc], oa) and torch.equal(lse[:, :, :P + Rc], la)

@@ -71,9 +71,10 @@ def test_strided_equals_contiguous_bitwise(kind, dtype):
     w = Workload(f"strided_{kind}", 2, 4, 2, 333, D, dtype, MASK_WINDOW, 100, seed=9600, Lk=333)
     inp = {n: t.to(DEV) for n, t in make_inputs(w).items()}
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
-    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window)
-    # strided calls never take the small-problem dK/dV split (its shares are
-    # summed in another order): the contiguous reference runs unsplit too
+    # strided calls never take the small-problem splits (key ranges of the
+    # forward and dQ pass, dK/dV shares; their partials are summed in another
+    # order): the contiguous reference runs unsplit too
+    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
     ws = torch.empty(max(1, workspace_bytes(2, 4, 333, D, q.dtype)), dtype=torch.uint8, device=DEV)
     dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window, workspace=ws)
     if kind == "fused":

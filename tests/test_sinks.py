@@ -75,7 +75,9 @@ def test_sink_at_minus_infinity_is_no_sink_bitwise():
     w = Workload("sink_inf", 2, 4, 2, 333, 256, "bf16", MASK_WINDOW, 100, seed=9901)
     inp = make_inputs(w)
     q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
-    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window)
+    # calls with sinks never split the forward's key ranges: the reference
+    # forward runs unsplit too (an empty workspace)
+    o, lse = sdpa_fwd_lse(q, k, v, w.mask, w.window, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
     dq, dk, dv = sdpa_bwd(q, k, v, o, do, lse, w.mask, w.window)
     g = run_sinks(w, inp, torch.full((4,), -math.inf))
     for a, n in ((o, "O"), (lse, "lse"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):

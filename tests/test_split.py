@@ -4,8 +4,9 @@ When a call's key blocks (128 keys per kv head and batch) number fewer than
 256, the backward may split each key block's query tiles over 2, 4 or 8
 workgroups that write fp32 shares of dK and dV into the workspace, summed in a
 fixed order afterwards. Given sdpa_bwd_workspace_bytes(...) bytes it runs
-unsplit; given sdpa_bwd_workspace_bytes_ex(...) bytes it splits. Both must
-match the fp64 oracle, and each other up to fp32 summation order.
+unsplit; given sdpa_bwd_workspace_bytes_ex(...) bytes it splits (and so does
+the dQ pass's key range when the query tiles are as few). Both must match the
+fp64 oracle, and each other up to fp32 summation order.
 """
 import pytest
 import torch
@@ -49,9 +50,10 @@ def test_split_matches_unsplit_and_oracle(case):
     one = _run(w, inp, small)
     split = _run(w, inp, big)
     ref = oracle.sdpa_fwd_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.mask, w.window)
-    # dQ does not depend on the split: bitwise equal
-    assert torch.equal(one["dQ"], split["dQ"])
     errs = {}
+    # the full workspace also splits the dQ pass's key ranges (fp32 partials
+    # summed in another order) when the query tiles are as few
+    errs["dQ"] = (rel_fro(_np(split["dQ"]), ref["dQ"]), rel_fro(_np(split["dQ"]), _np(one["dQ"])))
     for n in ("dK", "dV"):
         errs[n] = (rel_fro(_np(split[n]), ref[n]), rel_fro(_np(split[n]), _np(one[n])))
     print(name, {k: f"{a:.2e}/{b:.2e}" for k, (a, b) in errs.items()}, flush=True)
