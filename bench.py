@@ -64,6 +64,11 @@ def tile_config(w):
     bq = 128 if w.D <= 256 else 64
     bk = 64 if w.D <= 256 else 32
     split = "" if w.D <= 256 else ", head dim split over wave pairs"
+    import torch
+    import sdpa_backward_amd as sdpa
+    fb = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, torch.bfloat16, w.mask, w.window)
+    if fb:
+        split += f"; each query tile's key range split over {fb // (w.B * w.Hq * w.L * (w.D + 2) * 4)} workgroups"
     return (f"forward and dQ: {bq} query rows x {bk}-key tiles per workgroup (4 waves, 32x32x16 MFMA{split}); "
             f"dK/dV: {dkdv_kernel(w)}")
 
