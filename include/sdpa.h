@@ -85,9 +85,8 @@ enum sdpa_status {
   SDPA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % group != 0,
                                 window < 1 with a window mask, scale not
                                 finite or <= 0, unknown enum, misaligned ptr */
-  SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64,128,256,512}
-                                (bf16, f16) / {64,128} (f32); Lq + Lk > 2^30;
-                                B or Hq > 65535 */
+  SDPA_ERR_UNSUPPORTED = -2, /* valid but not built: D not in {64,128,256,512};
+                                Lq + Lk > 2^30; B or Hq > 65535 */
   SDPA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
   SDPA_ERR_LAUNCH = -4,      /* the HIP runtime reported a launch error */
   SDPA_ERR_SCRATCH_LIMIT = -5 /* sdpa_bwd_noalloc: the problem needs more

@@ -156,8 +156,7 @@ struct Shape {
 };
 
 bool d_supported(int dtype, int D) {
-  if (dtype == SDPA_BF16 || dtype == SDPA_F16) return D == 64 || D == 128 || D == 256 || D == 512;
-  return D == 64 || D == 128;
+  return D == 64 || D == 128 || D == 256 || D == 512;
 }
 
 bool windowed(int mask) { return mask == SDPA_MASK_CAUSAL_WINDOW || mask == SDPA_MASK_WINDOW; }
@@ -407,6 +406,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, v
     case SDPA_F32 * 1000 + 128:
       return to_status(
           sdpa::launch_fwd_f32<128>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, cut, scale, str, stream));
+    case SDPA_F32 * 1000 + 256:
+      return to_status(
+          sdpa::launch_fwd_f32<256>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, cut, scale, str, stream));
+    case SDPA_F32 * 1000 + 512:
+      return to_status(
+          sdpa::launch_fwd_f32<512>(q, k, v, o, lse, B, Hq, sinks, group, Lq, Lk, dlo, dhi, cut, scale, str, stream));
   }
   return SDPA_ERR_UNSUPPORTED;
 }
@@ -507,6 +512,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
       break;
     case SDPA_F32 * 1000 + 128:
       e = sdpa::launch_bwd_f32<128>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
+                                    scale, str, stream, events);
+      break;
+    case SDPA_F32 * 1000 + 256:
+      e = sdpa::launch_bwd_f32<256>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
+                                    scale, str, stream, events);
+      break;
+    case SDPA_F32 * 1000 + 512:
+      e = sdpa::launch_bwd_f32<512>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, group, Lq, Lk, dlo, dhi, cut,
                                     scale, str, stream, events);
       break;
     default:

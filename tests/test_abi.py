@@ -113,7 +113,7 @@ def bwd(lib, B=1, Hq=4, group=2, Lq=64, Lk=64, D=64, dtype=BF16, mask=CAUSAL, wi
     ({"scale": float("nan")}, INVALID),
     ({"D": 96}, UNSUPPORTED),
     ({"D": 1024}, UNSUPPORTED),
-    ({"dtype": F32, "D": 256}, UNSUPPORTED),
+    ({"dtype": F32, "D": 32}, UNSUPPORTED),
     ({"dtype": F16, "D": 96}, UNSUPPORTED),
     ({"Hq": 70000, "group": 1}, UNSUPPORTED),
     ({"Lq": 1 << 29, "Lk": (1 << 29) + 1}, UNSUPPORTED),   # row / key indices plus offsets must fit int32

@@ -80,6 +80,8 @@ SMALL = [
     ("f32_D64", 2, 1, 128, 64, "f32", MASK_CAUSAL, 0),
     ("f32_w17_D128", 4, 2, 100, 128, "f32", MASK_WINDOW, 17),
     ("f32_ragged_D64", 2, 2, 33, 64, "f32", MASK_WINDOW, 5),
+    ("f32_causal_D256", 2, 1, 150, 256, "f32", MASK_CAUSAL, 0),
+    ("f32_w40_D512_g2", 4, 2, 97, 512, "f32", MASK_WINDOW, 40),
     ("f16_causal_D64", 2, 1, 200, 64, "f16", MASK_CAUSAL, 0),
     ("f16_ragged_D128", 4, 2, 129, 128, "f16", MASK_CAUSAL, 0),
     ("f16_w63_D256", 4, 1, 300, 256, "f16", MASK_WINDOW, 63),

@@ -33,6 +33,7 @@ CASES = [
     ("f16_w64_D256", 1, 4, 2, 400, 400, 256, "f16", MASK_WINDOW, 64),
     ("f32_causal_D64", 2, 2, 1, 100, 100, 64, "f32", MASK_CAUSAL, 0),
     ("f32_prefix_D128", 1, 2, 2, 90, 40, 128, "f32", MASK_CAUSAL, 0),
+    ("f32_w30_D256", 1, 2, 1, 120, 120, 256, "f32", MASK_WINDOW, 30),
 ]
 
 

@@ -46,7 +46,7 @@ DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 def draw(rng):
     dtype = rng.choice(["bf16", "bf16", "f16", "f32"])
-    D = int(rng.choice([64, 128]) if dtype == "f32" else rng.choice([64, 128, 256, 512]))
+    D = int(rng.choice([64, 128, 256, 512]))
     Hkv = int(rng.choice([1, 2, 4]))
     group = int(rng.choice([1, 2, 4]))
     B = int(rng.choice([1, 1, 2]))
@@ -84,7 +84,7 @@ def draw_long(rng):
     shorter than keys, windows up to 5000), at few heads so the fp64 oracle
     stays within seconds per case."""
     dtype = str(rng.choice(["bf16", "bf16", "f16", "f32"]))
-    D = int(rng.choice([64, 128]) if dtype == "f32" else rng.choice([64, 128, 256, 256, 512]))
+    D = int(rng.choice([64, 128, 256, 256, 512]))
     Hkv = int(rng.choice([1, 2]))
     group = int(rng.choice([1, 2, 4]))
     Lk = int(rng.integers(300, 1500 if D == 512 else 3001))
