@@ -222,7 +222,8 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
  *    recomputes the scores (page "Lab 028 lab detail: Off NVIDIA, you fix the
  *    platform yourself", section "What I changed, in plain terms", item 5(a):
  *    dQ summed over the key tiles). At most 8 times the bytes of q, and
- *    linear in Lq at a fixed window;
+ *    linear in Lq at a fixed window; used only while the part of one kv
+ *    head's q-heads (group * ceil(Lq / 128) * nkb tiles) stays under 2 GiB;
  *  - when there is no band buffer, the dQ pass's key-range split: the same
  *    split and condition as sdpa_fwd_workspace_bytes, with fp32 dQ partials
  *    (nseg * B * Hq * Lq * D float32) summed by a combine pass; they share

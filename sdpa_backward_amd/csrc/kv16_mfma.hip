@@ -160,6 +160,12 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   // byte offset of this lane's dS^T values (key kj, rows rg..rg+3) inside a
   // band tile, relative to the wave's first key
   const uint32_t ds_lane = DSOUT ? (uint32_t)(((lane & 15) * kBandRows + rg) * sizeof(E)) : 0u;
+  // the band buffer of this kv head's q-heads (group * nqb row blocks; the
+  // host keeps it under 2 GiB, so offsets into it fit 32 bits)
+  const size_t band_blk = (size_t)nkb * kBandKeys * kBandRows;  // elements per row block
+  const auto band_rs = __builtin_amdgcn_make_buffer_rsrc(
+      DSOUT ? dST + ((size_t)b * Hq + (size_t)g * group) * nqb * band_blk : dST, 0,
+      DSOUT ? (int)((size_t)group * nqb * band_blk * sizeof(E)) : 0, 0x00020000);
   const int wrhi = kb1 - dlo;             // last row that sees a key of the wave (dense: no cut)
   // some pair of the tile's rows [q0, q0 + 31] and the wave's keys allowed / every pair allowed
   auto tile_tests = [&](int q0, bool& active, bool& full) {
@@ -308,20 +314,19 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
       da[4 + i] = (E)p1[i];
     }
     if constexpr (DSOUT) {
-      // band buffer: row block qb's tiles start at the key tile ktl of its band
+      // band buffer: row block qb of q-head hl (of the group) starts at
+      // (hl nqb + qb) band_blk, and its tiles at the key tile ktl of its band
       // (the query tile lies inside one row block; every key of this wave is
       // inside the block's nkb tiles, since some row of the tile sees one).
-      // The block's base and the tile's offset are uniform (scalar registers);
-      // each lane adds its fixed offset ds_lane.
-      const int hq = g * group + it / nq, qb = q0 / kBandRows;
+      // The tile's offset is uniform (a scalar register); each lane adds its
+      // fixed offset ds_lane.
+      const int hl = it / nq, qb = q0 / kBandRows;
       const int ktl = max(0, qb * kBandRows + dlo) / kBandKeys;
-      const size_t blk = (size_t)nkb * kBandKeys * kBandRows;  // elements per row block
-      const auto rs = __builtin_amdgcn_make_buffer_rsrc(dST + ((size_t)(b * Hq + hq) * nqb + qb) * blk, 0,
-                                                        (int)(blk * sizeof(E)), 0x00020000);
-      const int soff = ((kb0 - ktl * kBandKeys) * kBandRows + (q0 % kBandRows)) * (int)sizeof(E);
+      const int soff = (int)(((uint32_t)(hl * nqb + qb) * (uint32_t)band_blk +
+                              (uint32_t)((kb0 - ktl * kBandKeys) * kBandRows + (q0 % kBandRows))) * sizeof(E));
       const i32x4 v = __builtin_bit_cast(i32x4, da);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 0, 1), rs, (int)ds_lane, soff, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 2, 3), rs, (int)ds_lane + 32, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 0, 1), band_rs, (int)ds_lane, soff, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_shufflevector(v, v, 2, 3), band_rs, (int)ds_lane + 32, soff, 0);
     }
 #pragma unroll
     for (int blk = 0; blk < NB; blk++) {

@@ -244,7 +244,10 @@ size_t band_bytes(const Shape& s, int dlo, int dhi, int& nqb, int& nkb) {
                         floor_div(dlo, sdpa::kBandKeys) + 1;
   const int64_t n = std::min<int64_t>(tiles, (s.Lk + sdpa::kBandKeys - 1) / sdpa::kBandKeys);
   if (n * sdpa::kBandKeys > 8 * (int64_t)s.D) return 0;
-  nqb = (s.Lq + sdpa::kBandRows - 1) / sdpa::kBandRows;
+  const int64_t rb = (s.Lq + sdpa::kBandRows - 1) / sdpa::kBandRows;
+  // the dK/dV pass addresses the band of one kv head's q-heads with 32-bit offsets
+  if ((int64_t)s.group * rb * n * sdpa::kBandKeys * sdpa::kBandRows * 2 >= (int64_t(1) << 31)) return 0;
+  nqb = (int)rb;
   nkb = (int)n;
   return align_up((size_t)s.B * s.Hq * nqb * nkb * sdpa::kBandKeys * sdpa::kBandRows * 2);
 }

@@ -344,6 +344,10 @@ def test_band_workspace_sizes(lib):
     # dS buffer only comes with the 16-key kernel (at least 256 key blocks of 128)
     assert ex(2, 16, 1, 1024, 1024, 256, BF16, CAUSAL, 0) == delta(2, 16, 1024) + 2 * 16 * 8 * 16 * tile
     assert ex(1, 8, 2, 2048, 2048, 256, BF16, WINDOW, 100) == delta(1, 8, 2048) + 2 * 4 * 4 * 2048 * 256 * 4
+    # the band of one kv head's q-heads must stay under 2 GiB (the dK/dV pass
+    # addresses it with 32-bit offsets): group 32 at L = 65536 needs 4.8 GB
+    assert ex(1, 64, 32, 65536, 65536, 256, BF16, WINDOW, 1024) == delta(1, 64, 65536)
+    assert ex(1, 64, 2, 65536, 65536, 256, BF16, WINDOW, 1024) == delta(1, 64, 65536) + 64 * 512 * 18 * tile
 
 
 def test_ext_layout_matches_header(tmp_path):
