@@ -215,13 +215,14 @@ size_t sdpa_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Lq, int32_t D, in
  *    afterwards in a fixed order;
  *  - the dS band buffer: for 16-bit inputs at D = 256 with at least 256 key
  *    blocks, when every block of 128 query rows sees keys in at most
- *    nkb <= 32 tiles of 64 (a band at most 8 D = 2048 keys wide: sliding
- *    windows up to about 1900 keys), B * Hq * ceil(Lq / 128) * nkb tiles of
+ *    nkb <= 36 tiles of 64 (a band at most 9 D = 2304 keys wide: sliding
+ *    windows up to about 2150 keys, the two-sided window up to about 1080),
+ *    B * Hq * ceil(Lq / 128) * nkb tiles of
  *    64 x 128 16-bit values. The dK/dV pass then also writes dS for the band
  *    and dQ = scale * dS K is formed from it, instead of a dQ pass that
  *    recomputes the scores (page "Lab 028 lab detail: Off NVIDIA, you fix the
  *    platform yourself", section "What I changed, in plain terms", item 5(a):
- *    dQ summed over the key tiles). At most 8 times the bytes of q, and
+ *    dQ summed over the key tiles). At most 9 times the bytes of q, and
  *    linear in Lq at a fixed window; used only while the part of one kv
  *    head's q-heads (group * ceil(Lq / 128) * nkb tiles) stays under 2 GiB;
  *  - when there is no band buffer, the dQ pass's key-range split: the same

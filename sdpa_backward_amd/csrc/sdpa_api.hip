@@ -234,16 +234,17 @@ int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1)
 // (clipped to [0, Lk)); i0 is a multiple of the tile width, so unclipped
 // blocks all span floor((127 + dhi) / 64) - floor(dlo / 64) + 1 key tiles and
 // clipped ones no more. The buffer is used only when a block's band is at most
-// 8 D keys wide, so it never exceeds 8 times the size of Q (a window of up to
-// about 1900 keys at D = 256): memory stays linear in Lq at any length, and
-// wider bands (causal, no mask) recompute S and dP for dQ instead.
+// 9 D keys wide, so it never exceeds 9 times the size of Q (at D = 256 a
+// causal window of up to about 2150 keys, or the two-sided window 1024):
+// memory stays linear in Lq at any length, and wider bands (causal, no mask)
+// recompute S and dP for dQ instead.
 size_t band_bytes(const Shape& s, int dlo, int dhi, int& nqb, int& nkb) {
   nqb = nkb = 0;
   if (s.dtype == SDPA_F32 || s.D != 256 || s.no_rows() || s.no_keys() || dlo > dhi) return 0;
   const int64_t tiles = floor_div(sdpa::kBandRows - 1 + (int64_t)dhi, sdpa::kBandKeys) -
                         floor_div(dlo, sdpa::kBandKeys) + 1;
   const int64_t n = std::min<int64_t>(tiles, (s.Lk + sdpa::kBandKeys - 1) / sdpa::kBandKeys);
-  if (n * sdpa::kBandKeys > 8 * (int64_t)s.D) return 0;
+  if (n * sdpa::kBandKeys > 9 * (int64_t)s.D) return 0;
   const int64_t rb = (s.Lq + sdpa::kBandRows - 1) / sdpa::kBandRows;
   // the dK/dV pass addresses the band of one kv head's q-heads with 32-bit offsets
   if ((int64_t)s.group * rb * n * sdpa::kBandKeys * sdpa::kBandRows * 2 >= (int64_t(1) << 31)) return 0;

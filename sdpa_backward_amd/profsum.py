@@ -72,7 +72,7 @@ def short(name: str) -> str:
 def band_geometry(w):
     """(row blocks, key tiles per block) of the dS band buffer for this workload (the library's
     rule: D = 256 with the 16-key dK/dV kernel, i.e. at least 256 blocks of 128 keys; 128-row
-    blocks, 64-key tiles, a block's band at most 8 D keys wide), or None."""
+    blocks, 64-key tiles, a block's band at most 9 D keys wide), or None."""
     if w.D != 256 or w.dtype == "f32" or -(-w.Lkv // 128) * w.Hkv * w.B < 256:
         return None
     off = w.Lkv - w.L
@@ -85,7 +85,7 @@ def band_geometry(w):
         lo, hi = off - w.window + 1, off + w.window - 1
     lo, hi = max(lo, -(w.L - 1)), min(hi, w.Lkv - 1)
     nkb = min((127 + hi) // 64 - lo // 64 + 1, -(-w.Lkv // 64))
-    return (-(-w.L // 128), nkb) if nkb * 64 <= 8 * w.D else None
+    return (-(-w.L // 128), nkb) if nkb * 64 <= 9 * w.D else None
 
 
 def key_range_shares(w):

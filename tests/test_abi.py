@@ -333,9 +333,13 @@ def test_band_workspace_sizes(lib):
     assert [b / a for a, b in zip(sizes, sizes[1:])] == [2.0, 2.0, 2.0]
     # window 1: keys i0 .. i0 + 127, 2 tiles
     assert ex(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 1) == delta(1, 32, 16384) + 32 * 128 * 2 * tile
-    # bands wider than 8 D = 2048 keys keep no dS: the two-sided window 1024
-    # (34 tiles), causal and no mask at long lengths; and only D = 256 keeps it
-    assert ex(1, 32, 2, 16384, 16384, 256, BF16, TWO_SIDED, 1024) == delta(1, 32, 16384)
+    # the two-sided window 1024 spans keys i0 - 1023 .. i0 + 127 + 1023: 34 tiles
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, TWO_SIDED, 1024) == delta(1, 32, 16384) + 32 * 128 * 34 * tile
+    # bands wider than 9 D = 2304 keys keep no dS: the two-sided window 1100
+    # (38 tiles), causal and no mask at long lengths; and only D = 256 keeps it
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, TWO_SIDED, 1100) == delta(1, 32, 16384)
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 2150) == delta(1, 32, 16384) + 32 * 128 * 36 * tile
+    assert ex(1, 32, 2, 16384, 16384, 256, BF16, WINDOW, 2200) == delta(1, 32, 16384)
     assert ex(1, 32, 2, 16384, 16384, 256, BF16, CAUSAL, 0) == delta(1, 32, 16384)
     assert ex(1, 32, 2, 4096, 4096, 256, BF16, NONE, 0) == delta(1, 32, 4096)
     assert ex(1, 32, 2, 16384, 16384, 128, BF16, WINDOW, 1024) == delta(1, 32, 16384)

@@ -1,7 +1,8 @@
 """The backward that keeps dS for a bounded band (run on an MI355X).
 
 For 16-bit inputs at D = 256 whose key blocks fill the GPU (at least 256
-blocks of 128 keys), a band at most 2048 keys wide (sliding windows) and the
+blocks of 128 keys), a band at most 2304 keys wide (sliding windows, the
+two-sided window up to about 1080) and the
 full workspace of sdpa_bwd_workspace_bytes_ex, the dK/dV pass also writes
 dS^T for the band and dQ = scale dS K is formed from it, instead of a dQ pass
 that recomputes S and dP. Every case here takes that path (checked through
@@ -34,6 +35,7 @@ CASES = [
     ("suffix_w256", 1, 32, 16, 512, 2048, "bf16", MASK_WINDOW, 256),
     ("w700_ragged_1900", 1, 32, 16, 1900, 2048, "bf16", MASK_WINDOW, 700),
     ("w130_L1153", 2, 32, 16, 1153, 1153, "bf16", MASK_WINDOW, 130),
+    ("twosided_w1024_34tiles", 1, 16, 16, 2304, 2304, "bf16", MASK_TWO_SIDED, 1024),
 ]
 
 

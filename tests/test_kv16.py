@@ -4,7 +4,7 @@ Dense 16-bit calls at D = 256 whose key blocks (128 keys per kv head and
 batch) number at least 256 run their dK/dV pass with 16-key waves on
 v_mfma_f32_16x16x32 (D = 512 always does; its cases live in the other
 files). Checked against the fp64 oracle, and against the 32-key kernel,
-which a strided copy of the same tensors takes. With a band at most 2048 keys
+which a strided copy of the same tensors takes. With a band at most 2304 keys
 wide the dense call also keeps dS for the band and forms dQ from it, while the
 strided copy recomputes S and dP for dQ: the two dQ agree to fp32 summation
 order and dS rounding.
