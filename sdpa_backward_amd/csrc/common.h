@@ -416,6 +416,14 @@ SDPA_DEV void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// LDS hand-off between the lanes of one wave: this wave's LDS writes are
+// complete, and the compiler moves no memory access across the call.
+SDPA_DEV void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Tiles of the dS band buffer that the dK/dV pass writes and the dQ pass
 // reads (bounded bands): [kBandKeys keys][kBandRows query rows], key-major,
 // one per (batch and q-head, block of kBandRows rows, key tile of the

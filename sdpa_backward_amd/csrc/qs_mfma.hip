@@ -202,6 +202,18 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // this workgroup's tiles [t_b, t_e) of the nt (all of them without a split)
   const int t_b = (int)((long long)seg * nt / nseg), t_e = (int)((long long)(seg + 1) * nt / nseg);
   const int wr0 = iw0, wr1 = min(iw0 + 31, Lq - 1);  // this wave's rows (wr1 < wr0: none)
+  // Rows [valid, BK) of a K and a V tile buffer (keys past Lk, in the last
+  // key tile only): the loads do not fill them, and every operand read must
+  // be finite (a masked score becomes -inf or p = 0, but 0 times a NaN bit
+  // pattern left in LDS is NaN), so they are zeroed before the tile's loads.
+  auto zero_tail = [&](E* Kb, E* Vb, int valid) {
+    if (valid >= BK) return;
+    const i32x4 z = {0, 0, 0, 0};
+    for (int i = max(valid, 0) * D + tid * 8; i < C::TILE; i += C::NW * 64 * 8) {
+      *(i32x4*)(Kb + i) = z;
+      *(i32x4*)(Vb + i) = z;
+    }
+  };
 
   auto step = [&](int t, const E* Kc, const E* Vc, E* Kn, E* Vn) {
     const int kt = kt_of(t);
@@ -214,6 +226,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     // rows and the loads read nothing.
     const bool more = t + 1 < t_e;
     const int jn = more ? kt_of(t + 1) * BK : 0;
+    if (more) zero_tail(Kn, Vn, Lk - jn);  // (no-op unless tile t + 1 runs past Lk)
     const auto krs = ldk.rsrc(Kg + (long long)jn * st.k.l, more ? Lk - jn : 0);
     const auto vrs = ldv.rsrc(Vg + (long long)jn * st.v.l, more ? Lk - jn : 0);
     using LD = decltype(ldk);
@@ -368,11 +381,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
 
   if (t_e > t_b) {  // first tile (uniform over the workgroup)
     const int j0 = kt_of(t_b) * BK;
-    zero_lds(kb0, C::TILE, tid);
-    zero_lds(kb1, C::TILE, tid);
-    zero_lds(vb0, C::TILE, tid);
-    zero_lds(vb1, C::TILE, tid);
-    lds_barrier();
+    zero_tail(kb0, vb0, Lk - j0);
     ldk.issue(kb0, Kg + (long long)j0 * st.k.l, Lk - j0, w);
     ldv.issue(vb0, Vg + (long long)j0 * st.v.l, Lk - j0, w);
     wait_all_and_barrier();
@@ -385,8 +394,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     wait_all_and_barrier();
   }
 
-  if (!qok) return;
   if (nseg > 1) {  // fp32 partial rows (and the forward's m, l) for the combine pass
+    if (!qok) return;
     const size_t rows = (size_t)(gridDim.x / nseg / nqt) * Lq;  // B * Hq * Lq: one partial's rows
     float* prow = part + ((size_t)seg * rows + hrow * Lq + qi) * D;
 #pragma unroll
@@ -403,31 +412,40 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
     }
     return;
   }
-  const Strides so = MODE == QS_FWD ? st.o : st.dq;
-  E* orow = Out + b * so.b + h * so.h + (long long)qi * so.l;
-  if constexpr (MODE == QS_FWD) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // The wave's 32 output rows (O / lsum, or scale dQ) go out through LDS: a
+  // lane holds 4 consecutive columns of one row per C tile, which as global
+  // stores are 8-byte pieces of 32 rows each; staged in the wave's own tile
+  // buffer (the loop ended with a barrier, so no wave reads the buffers any
+  // more; with no tile they were never used), each store writes 1 KB of whole
+  // rows instead.
+  {
+    const float mul = MODE == QS_FWD ? (lsum > 0.f ? 1.f / lsum : 0.f) : scale;
+    constexpr int SP = DW + 8;  // staging row pitch in elements (16 bytes of padding against bank conflicts)
+    static_assert(32 * SP <= C::TILE, "the staging rows fit one tile buffer");
+    E* stg = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
+    const int r = lane & 31;
 #pragma unroll
     for (int d = 0; d < NDB; d++)
 #pragma unroll
       for (int blk = 0; blk < 4; blk++) {
         ex4 v;
 #pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = (E)(acc[d][4 * blk + r] * inv);
-        *(ex4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
+        for (int rr = 0; rr < 4; rr++) v[rr] = (E)(acc[d][4 * blk + rr] * mul);
+        *(ex4*)(stg + r * SP + 32 * d + 8 * blk + 4 * hh) = v;
       }
-    if (dsi == 0 && hh == 0) LSE[hrow * Lq + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
-  } else {
+    wave_lds_sync();
+    constexpr int CPR = DW / 8, NCH = 32 * CPR / 64;  // 16-byte chunks per row, per lane
+    const Strides so = MODE == QS_FWD ? st.o : st.dq;
+    E* o0 = Out + b * so.b + h * so.h + (long long)iw0 * so.l + dw0;
 #pragma unroll
-    for (int d = 0; d < NDB; d++)
-#pragma unroll
-      for (int blk = 0; blk < 4; blk++) {
-        ex4 v;
-#pragma unroll
-        for (int r = 0; r < 4; r++) v[r] = (E)(acc[d][4 * blk + r] * scale);
-        *(ex4*)(orow + dw0 + 32 * d + 8 * blk + 4 * hh) = v;
-      }
+    for (int k = 0; k < NCH; k++) {
+      const int c = lane + 64 * k, row = c / CPR, col = (c % CPR) * 8;
+      const ex8 v = *(const ex8*)(stg + row * SP + col);
+      if (iw0 + row < Lq) *(ex8*)(o0 + (long long)row * so.l + col) = v;
+    }
   }
+  if (MODE == QS_FWD && qok && dsi == 0 && hh == 0)
+    LSE[hrow * Lq + qi] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 // Combine pass of a split call: one thread per 8 columns of a row (rows =
