@@ -164,9 +164,9 @@ def _sample(n_total, rng, fixed, n=20):
 
 
 @pytest.mark.parametrize("name", [w.name for w in BY_NAME.values() if w.name.startswith(
-    ("bf16_twosided", "bf16_window1024_Lq", "bf16_nomask"))])
+    ("bf16_twosided", "bf16_window1024_Lq", "bf16_nomask", "bf16_window1024_L16384_D256_h4"))])
 def test_variant_workloads_sampled(name):
-    """The benchmark's variant workloads, in its launch configuration: sampled
+    """The benchmark's variant and one-GPU-share workloads, in its launch configuration: sampled
     rows (O, lse, dQ) and keys (dK, dV) against the oracle, which computes them
     one by one; NaN-filled outputs must be fully overwritten."""
     w = BY_NAME[name]

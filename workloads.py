@@ -84,7 +84,16 @@ VARIANTS = [
              Lk=16384),
     Workload("bf16_nomask_L4096_D256_h32kv16", 1, 32, 16, 4096, 256, "bf16", MASK_NONE, 0, 1007),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + VARIANTS}
+# One GPU's share of the L = 16384 window layer when it is split over eight:
+# by kv-heads (2 of 16, with their 4 q-heads), or by sequence (a 2048-query
+# chunk with the 1023 keys before it that its window reaches, a halo the left
+# neighbour would send).
+SHARES = [
+    Workload("bf16_window1024_L16384_D256_h4kv2", 1, 4, 2, 16384, 256, "bf16", MASK_WINDOW, 1024, 1008),
+    Workload("bf16_window1024_Lq2048_Lk3071_D256_h32kv16", 1, 32, 16, 2048, 256, "bf16", MASK_WINDOW, 1024, 1009,
+             Lk=3071),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + VARIANTS + SHARES}
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
