@@ -69,8 +69,15 @@ def tile_config(w):
     fb = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, torch.bfloat16, w.mask, w.window)
     if fb:
         split += f"; each query tile's key range split over {fb // (w.B * w.Hq * w.L * (w.D + 2) * 4)} workgroups"
+    kv = dkdv_kernel(w)
+    if kv.startswith("kv16") and w.D == 256:
+        # the launcher's choice: 8-wave workgroups when every key sees at least 2048 query rows (no band)
+        from workloads import MASK_TWO_SIDED, MASK_WINDOW
+        span = {MASK_WINDOW: w.window, MASK_TWO_SIDED: 2 * w.window - 1}.get(w.mask, w.L)
+        eight = not uses_band(w, sdpa, torch.bfloat16) and min(span, w.L) >= 2048
+        kv += f", {8 if eight else 4}-wave workgroups"
     return (f"forward and dQ: {bq} query rows x {bk}-key tiles per workgroup (4 waves, 32x32x16 MFMA{split}); "
-            f"dK/dV: {dkdv_kernel(w)}")
+            f"dK/dV: {kv}")
 
 
 def log(*a):

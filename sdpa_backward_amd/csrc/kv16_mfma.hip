@@ -65,10 +65,15 @@ struct LaneAddr16 {
   }
 };
 
-// D <= 256: two workgroups per CU (two waves per SIMD, at most 256 registers
-// per lane); D = 512: one.
-template <int D, typename E, bool DENSE, bool DSOUT>
-__global__ void __launch_bounds__(256, D <= 256 ? 2 : 1)
+// NW waves per workgroup (16 NW keys). At D <= 256 two waves share a SIMD (at
+// most 256 registers per lane): two 4-wave workgroups per CU, or one 8-wave
+// workgroup, which streams each Q / dO tile into LDS once for 128 keys instead
+// of once per 64 (the launcher takes it when every key sees at least 2048
+// query rows: on narrower bands the extra score work of waves that miss a
+// tile costs more than the loads save). At D = 512 one 4-wave workgroup per CU
+// (one wave per SIMD).
+template <int D, typename E, bool DENSE, bool DSOUT, int NW>
+__global__ void __launch_bounds__(64 * NW, D <= 256 ? 8 / NW : 1)
 kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
             const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
             E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
@@ -76,7 +81,8 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   static_assert(!DSOUT || DENSE, "the band buffer is written by the dense instantiation");
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
-  constexpr int NW = 4, BKT = 16 * NW, BQ = 32, NT = D / 32, NB = D / 16, QT = BQ * D;
+  static_assert(NW == 4 || (NW == 8 && D <= 256), "8-wave workgroups need two waves per SIMD");
+  constexpr int BKT = 16 * NW, BQ = 32, NT = D / 32, NB = D / 16, QT = BQ * D;
   __shared__ __attribute__((aligned(16))) E qb0[QT];
   __shared__ __attribute__((aligned(16))) E db0[QT];
   __shared__ __attribute__((aligned(16))) E qb1[QT];
@@ -342,6 +348,7 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
     }
   };
 
+  // (with 8 waves the upper 256 threads repeat zero stores of the lower ones)
   zero_lds(qb0, QT, tid);
   zero_lds(db0, QT, tid);
   zero_lds(qb1, QT, tid);
@@ -390,19 +397,23 @@ hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* 
                        const float* delta, void* dk, void* dv, int B, int Hq, int group, int Lq, int Lk, int dlo,
                        int dhi, Cut cut, float scale, const AllStrides& st, void* dst, int nqb, int nkb,
                        hipStream_t stream) {
-  const long nwg = (long)((Lk + 63) / 64) * (Hq / group) * B;
+  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
+  // query rows a key may see (band height, at most Lq)
+  const long long span = std::min<long long>((long long)dhi - dlo + 1, Lq);
+  const int NW = D <= 256 && dst == nullptr && span >= 2048 ? 8 : 4;
+  const long nwg = (long)((Lk + 16 * NW - 1) / (16 * NW)) * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
-  const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
-  auto kernel = kv16_kernel<D, E, true, false>;
+  auto kernel = kv16_kernel<D, E, true, false, 4>;
   if constexpr (D > 256) {
     if (dst != nullptr) return hipErrorInvalidValue;
-    if (!dense) kernel = kv16_kernel<D, E, false, false>;
+    if (!dense) kernel = kv16_kernel<D, E, false, false, 4>;
   } else {
     if (!dense) return hipErrorInvalidValue;  // below D = 512 only dense calls come here (the strided kind would spill)
-    if (dst != nullptr) kernel = kv16_kernel<D, E, true, true>;
+    if (dst != nullptr) kernel = kv16_kernel<D, E, true, true, 4>;
+    else if (NW == 8) kernel = kv16_kernel<D, E, true, false, 8>;
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(256), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(64 * NW), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                      (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk, dlo, dhi, cut, scale,
                      scale * kLog2e, st, (E*)dst, nqb, nkb);
   return hipGetLastError();

@@ -54,6 +54,10 @@ CASES = [
     ("f16_two_w80_D256", 2, 1, 400, 400, 256, "f16", MASK_TWO_SIDED, 80),
     ("f16_suffix_w64_D512", 2, 1, 150, 700, 512, "f16", MASK_WINDOW, 64),
     ("f16_prefix_causal_D64", 2, 2, 300, 120, 64, "f16", MASK_CAUSAL, 0),
+    # D = 256 calls whose keys each see >= 2048 rows and whose band is too wide
+    # to keep dS: the dK/dV pass runs 8-wave workgroups (128 keys)
+    ("none_wide_8wave_D256", 16, 16, 2400, 2400, 256, "bf16", MASK_NONE, 0),
+    ("suffix_causal_8wave_D256_g2", 32, 16, 2200, 2600, 256, "bf16", MASK_CAUSAL, 0),
 ]
 
 
