@@ -66,6 +66,8 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
   constexpr int NW = 4, BQ = kBandRows, BK = 32, NDB = D / 32, NKS = BK / 16;
   constexpr int KT = BK * D, ST = BK * BQ;
   static_assert(kBandKeys % BK == 0, "a band tile holds whole key tiles of this kernel");
+  // (separate arrays: the compiler then knows that loads into one buffer
+  // cannot change another and keeps the LDS waits partial)
   __shared__ __attribute__((aligned(16))) E kb0[KT];
   __shared__ __attribute__((aligned(16))) E kb1[KT];
   __shared__ __attribute__((aligned(16))) E kb2[KT];
@@ -199,19 +201,39 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
   }
   wait_all_and_barrier();  // (the last steps' no-op loads)
 
-  if (qi >= Lq) return;
   // C tile = dQ^T: lane's column is its row, accumulator slot i holds head-dim
-  // index 32 d + c_row(i, hh)
-  E* orow = dQ + ((size_t)bh * Lq + qi) * D;
+  // index 32 d + c_row(i, hh). The wave's 32 rows go out through LDS (no wave
+  // reads the tile buffers any more): as global stores a lane's 4 consecutive
+  // columns are 8-byte pieces of 32 rows each, staged each store writes 1 KB
+  // of whole rows. Waves 0-2 stage in their K buffer (32 x D), wave 3 rows
+  // 0-15 in sb0 and 16-31 in sb1 (16 x D each). Staging rows have a pitch of
+  // D, their 16-byte chunks permuted (chunk c of row r at c ^ (r mod CPR)) so
+  // that the 32 rows one store instruction writes fall in distinct banks.
+  {
+    constexpr int CPR = D / 8, NCH = 32 * CPR / 64;  // 16-byte chunks per row, per lane
+    static_assert(KT == 32 * D && ST >= 16 * D, "a K buffer holds 32 staged rows, a dS^T buffer 16");
+    E* const lo = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? kb2 : sb0;  // rows 0-15
+    E* const hi = w == 3 ? sb1 : lo + 16 * D;                        // rows 16-31
+    auto stg = [&](int row) { return row < 16 ? lo + row * D : hi + (row - 16) * D; };
+    const int r = lane & 31;
 #pragma unroll
-  for (int d = 0; d < NDB; d++)
+    for (int d = 0; d < NDB; d++)
 #pragma unroll
-    for (int blk = 0; blk < 4; blk++) {
-      ex4 v;
+      for (int blk = 0; blk < 4; blk++) {
+        ex4 v;
 #pragma unroll
-      for (int r = 0; r < 4; r++) v[r] = (E)(acc[d][4 * blk + r] * scale);
-      *(ex4*)(orow + 32 * d + 8 * blk + 4 * hh) = v;
+        for (int i = 0; i < 4; i++) v[i] = (E)(acc[d][4 * blk + i] * scale);
+        *(ex4*)(stg(r) + (((4 * d + blk) ^ (r % CPR)) * 8) + 4 * hh) = v;
+      }
+    wave_lds_sync();
+    E* o0 = dQ + ((size_t)bh * Lq + wr0) * D;
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const int c = lane + 64 * k, row = c / CPR, j = c % CPR;
+      const ex8 v = *(const ex8*)(stg(row) + ((j ^ (row % CPR)) * 8));
+      if (wr0 + row < Lq) *(ex8*)(o0 + (size_t)row * D + 8 * j) = v;
     }
+  }
 }
 
 template <int D, typename E>
