@@ -61,9 +61,8 @@ def tile_config(w):
     """The kernels' tile shapes for this workload (as the library picks them)."""
     if w.dtype == "f32":
         return "fp32 VALU kernels (one query row per lane; one key per lane in dK/dV)"
-    bq = 128 if w.D <= 256 else 64
     bk = 64 if w.D <= 256 else 32
-    split = "" if w.D <= 256 else ", head dim split over wave pairs"
+    split = "" if w.D <= 256 else "; the dQ pass: 64 rows, head dim split over wave pairs"
     import torch
     import sdpa_backward_amd as sdpa
     fb = sdpa.fwd_workspace_bytes(w.B, w.Hq, w.group, w.L, w.Lkv, w.D, torch.bfloat16, w.mask, w.window)
@@ -76,7 +75,7 @@ def tile_config(w):
         span = {MASK_WINDOW: w.window, MASK_TWO_SIDED: 2 * w.window - 1}.get(w.mask, w.L)
         eight = not uses_band(w, sdpa, torch.bfloat16) and min(span, w.L) >= 2048
         kv += f", {8 if eight else 4}-wave workgroups"
-    return (f"forward and dQ: {bq} query rows x {bk}-key tiles per workgroup (4 waves, 32x32x16 MFMA{split}); "
+    return (f"forward and dQ: 128 query rows x {bk}-key tiles per workgroup (4 waves, 32x32x16 MFMA{split}); "
             f"dK/dV: {kv}")
 
 

@@ -54,10 +54,16 @@ enum { QS_FWD = 0, QS_DQ = 1 };
 #define QS_AHEAD_O 4
 #endif
 
-template <int D>
+// Head dim 512 in the forward: each wave holds all of a row block's O (256
+// accumulator registers) and its Q rows in VGPRs (QS_FWD512_FULL), or wave
+// pairs split the head dim.
+#ifndef QS_FWD512_FULL
+#define QS_FWD512_FULL 1
+#endif
+template <int D, int MODE = 1>
 struct QsCfg {
   static constexpr int NW = 4;
-  static constexpr int DS = D > 256 ? 2 : 1;    // waves sharing one 32-row block (head-dim split)
+  static constexpr int DS = D > 256 && !(MODE == 0 && QS_FWD512_FULL) ? 2 : 1;  // waves sharing one 32-row block (head-dim split)
   static constexpr int NQW = NW / DS;           // 32-row blocks per workgroup
   static constexpr int BQ = 32 * NQW;           // query rows per workgroup
   static constexpr int DW = D / DS;             // head-dim slice of one wave
@@ -89,7 +95,7 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
           float* __restrict__ Delta, E* __restrict__ Out, const float* __restrict__ Sinks, int Hq, int group,
           int Lq, int Lk, int dlo, int dhi, Cut cut_arg, float scale, float scale_log2, AllStrides st_arg,
           int nseg, float* __restrict__ part) {
-  using C = QsCfg<D>;
+  using C = QsCfg<D, MODE>;
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
   constexpr int BK = C::BK, NMB = C::NMB, DW = C::DW, NKS = DW / 16, NDB = DW / 32;
@@ -239,7 +245,8 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
       else ldv.issue_one(Vn, vrs, j - NJ, w);
     };
 #pragma unroll
-    for (int s = 0; s < NKS; s++) keep_in_agpr(qreg[s]);
+    for (int s = 0; s < NKS; s++)
+      if constexpr (4 * NKS + 16 * NDB <= 256) keep_in_agpr(qreg[s]);  // (at D = 512, Q stays in VGPRs)
 #pragma unroll
     for (int d = 0; d < NDB; d++) keep_in_agpr(acc[d]);
     const int j0 = kt * BK;
@@ -417,11 +424,13 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
   // stores are 8-byte pieces of 32 rows each; staged in the wave's own tile
   // buffer (the loop ended with a barrier, so no wave reads the buffers any
   // more; with no tile they were never used), each store writes 1 KB of whole
-  // rows instead.
+  // rows instead. Staging rows have a pitch of DW elements, their 16-byte
+  // chunks permuted (chunk c of row r at c ^ (r mod CPR)) so that the 32 rows
+  // one store instruction writes fall in distinct banks.
   {
     const float mul = MODE == QS_FWD ? (lsum > 0.f ? 1.f / lsum : 0.f) : scale;
-    constexpr int SP = DW + 8;  // staging row pitch in elements (16 bytes of padding against bank conflicts)
-    static_assert(32 * SP <= C::TILE, "the staging rows fit one tile buffer");
+    constexpr int CPR = DW / 8, NCH = 32 * CPR / 64;  // 16-byte chunks per row, per lane
+    static_assert(32 * DW <= C::TILE, "the staging rows fit one tile buffer");
     E* stg = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
     const int r = lane & 31;
 #pragma unroll
@@ -431,17 +440,16 @@ qs_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict_
         ex4 v;
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) v[rr] = (E)(acc[d][4 * blk + rr] * mul);
-        *(ex4*)(stg + r * SP + 32 * d + 8 * blk + 4 * hh) = v;
+        *(ex4*)(stg + r * DW + (((4 * d + blk) ^ (r % CPR)) * 8) + 4 * hh) = v;
       }
     wave_lds_sync();
-    constexpr int CPR = DW / 8, NCH = 32 * CPR / 64;  // 16-byte chunks per row, per lane
     const Strides so = MODE == QS_FWD ? st.o : st.dq;
     E* o0 = Out + b * so.b + h * so.h + (long long)iw0 * so.l + dw0;
 #pragma unroll
     for (int k = 0; k < NCH; k++) {
-      const int c = lane + 64 * k, row = c / CPR, col = (c % CPR) * 8;
-      const ex8 v = *(const ex8*)(stg + row * SP + col);
-      if (iw0 + row < Lq) *(ex8*)(o0 + (long long)row * so.l + col) = v;
+      const int c = lane + 64 * k, row = c / CPR, j = c % CPR;
+      const ex8 v = *(const ex8*)(stg + row * DW + ((j ^ (row % CPR)) * 8));
+      if (iw0 + row < Lq) *(ex8*)(o0 + (long long)row * so.l + 8 * j) = v;
     }
   }
   if (MODE == QS_FWD && qok && dsi == 0 && hh == 0)
@@ -496,7 +504,9 @@ qs_combine_kernel(const float* __restrict__ part, E* __restrict__ Out, float* __
 // Key-range shares per query tile for a dense 16-bit call (1: no split): when
 // the query tiles alone give at most half as many workgroups as the 256 CUs,
 // the largest power of two up to 4 that keeps the grid within 256 workgroups
-// and the longest query tile at two or more key tiles per share.
+// and the longest query tile at two or more key tiles per share (counted with
+// the dQ pass's tiles, which at D = 512 are half as tall as the forward's;
+// both passes take the same shares).
 template <int D>
 int qs_split_shares(int B, int Hq, int Lq, int Lk, int dlo, int dhi, bool dense) {
   using C = QsCfg<D>;
@@ -514,7 +524,7 @@ hipError_t launch_qs(const void* q, const void* k, const void* v, const void* o,
                      float* delta, void* out, const float* sinks, int B, int Hq, int group, int Lq, int Lk,
                      int dlo, int dhi, Cut cut, float scale, const AllStrides& st, int nseg, float* part,
                      hipStream_t stream) {
-  using C = QsCfg<D>;
+  using C = QsCfg<D, MODE>;
   if (nseg < 1 || (nseg > 1 && part == nullptr)) return hipErrorInvalidValue;
   const long nwg = (long)((Lq + C::BQ - 1) / C::BQ) * Hq * B * nseg;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
