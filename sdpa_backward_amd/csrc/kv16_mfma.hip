@@ -77,7 +77,8 @@ __global__ void __launch_bounds__(64 * NW, D <= 256 ? 8 / NW : 1)
 kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
             const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
             E* __restrict__ dK, E* __restrict__ dV, int Hq, int group, int Lq, int Lk, int dlo, int dhi,
-            Cut cut_arg, float scale, float scale_log2, AllStrides st_arg, E* __restrict__ dST, int nqb, int nkb) {
+            Cut cut_arg, float scale, float scale_log2, AllStrides st_arg, E* __restrict__ dST, int nqb, int nkb,
+            int kt0, int nkt) {
   static_assert(!DSOUT || DENSE, "the band buffer is written by the dense instantiation");
   using ex8 = typename Vec<E>::x8;
   using ex4 = typename Vec<E>::x4;
@@ -97,9 +98,10 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   const int Hkv = Hq / group;
   const AllStrides st = DENSE ? dense_strides<D>(Hq, Hkv, Lq, Lk) : st_arg;
   const Cut cut = DENSE ? kNoCut : cut_arg;  // no cut in the dense instantiation
-  const int nkt = (Lk + BKT - 1) / BKT;
+  // key blocks kt0 .. kt0 + nkt - 1 of each kv head (the launcher leaves out
+  // blocks that no row sees and zeroes their dK / dV rows itself)
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
+  const int kt = kt0 + logical % nkt, g = (logical / nkt) % Hkv, b = logical / (nkt * Hkv);
   const int k0 = kt * BKT;
   const int kb0 = k0 + 16 * w;        // first key of this wave
   const int kj = kb0 + (lane & 15);   // key held by this lane (C-tile column of S and dP)
@@ -390,6 +392,21 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
   }
 }
 
+// dK and dV rows [0, lo) and [hi, Lk) of every (batch, kv head) of a dense
+// call (rows of D elements): the keys that no query row sees.
+template <typename E>
+__global__ void __launch_bounds__(256) kv_zero_kernel(E* __restrict__ dK, E* __restrict__ dV, int Lk, int D, int lo,
+                                                      int hi) {
+  const size_t head = (size_t)blockIdx.y * Lk * D;
+  const long long n1 = (long long)lo * D, n = n1 + (long long)(Lk - hi) * D;  // (multiples of 8)
+  const i32x4 z = {0, 0, 0, 0};
+  for (long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long long)gridDim.x * 256 * 8) {
+    const size_t off = head + (size_t)(i < n1 ? i : (long long)hi * D + (i - n1));
+    *(i32x4*)(dK + off) = z;
+    *(i32x4*)(dV + off) = z;
+  }
+}
+
 // dst (D = 256, dense only): the band buffer to fill with dS^T (nqb blocks of
 // 128 rows, nkb key tiles each), or null.
 template <int D, typename E>
@@ -400,8 +417,27 @@ hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* 
   const bool dense = is_dense<D>(st, Hq, Hq / group, Lq, Lk) && cut.c0 == cut.c1;
   // query rows a key may see (band height, at most Lq)
   const long long span = std::min<long long>((long long)dhi - dlo + 1, Lq);
-  const int NW = D <= 256 && dst == nullptr && span >= 2048 ? 8 : 4;
-  const long nwg = (long)((Lk + 16 * NW - 1) / (16 * NW)) * (Hq / group) * B;
+  const int NW = D <= 256 && dst == nullptr && span >= 2048 ? 8 : 4, BKT = 16 * NW;
+  // key blocks to visit: with a dense call only those holding a key some row
+  // sees (keys [max(0, dlo), min(Lk - 1, Lq - 1 + dhi)]); the rows of the
+  // others are zeroed here
+  int kt0 = 0, nkt = (Lk + BKT - 1) / BKT;
+  if (dense && Lq > 0 && Lk > 0) {
+    const long long klo = std::max<long long>(0, dlo), khi = std::min<long long>(Lk - 1, (long long)Lq - 1 + dhi);
+    const int a = klo <= khi ? (int)(klo / BKT) : 0, z = klo <= khi ? (int)(khi / BKT) + 1 : 0;  // blocks [a, z)
+    if (a > 0 || z < nkt) {
+      const int lo = a * BKT, hi = std::min(z * BKT, Lk);
+      const long long n = ((long long)lo + (Lk - hi)) * D / 8;  // 16-byte stores per head
+      const int gx = (int)std::min<long long>((n + 255) / 256, 1024);
+      if ((long long)B * (Hq / group) > 65535) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((kv_zero_kernel<E>), dim3((unsigned)gx, (unsigned)(B * (Hq / group))), dim3(256), 0, stream,
+                         (E*)dk, (E*)dv, Lk, D, lo, hi);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    kt0 = a;
+    nkt = z - a;
+  }
+  const long nwg = (long)nkt * (Hq / group) * B;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   if (nwg == 0) return hipSuccess;
   auto kernel = kv16_kernel<D, E, true, false, 4>;
@@ -415,7 +451,7 @@ hipError_t launch_kv16(const void* q, const void* k, const void* v, const void* 
   }
   hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(64 * NW), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                      (const E*)dO, lse, delta, (E*)dk, (E*)dv, Hq, group, Lq, Lk, dlo, dhi, cut, scale,
-                     scale * kLog2e, st, (E*)dst, nqb, nkb);
+                     scale * kLog2e, st, (E*)dst, nqb, nkb, kt0, nkt);
   return hipGetLastError();
 }
 

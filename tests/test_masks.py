@@ -58,6 +58,9 @@ CASES = [
     # to keep dS: the dK/dV pass runs 8-wave workgroups (128 keys)
     ("none_wide_8wave_D256", 16, 16, 2400, 2400, 256, "bf16", MASK_NONE, 0),
     ("suffix_causal_8wave_D256_g2", 32, 16, 2200, 2600, 256, "bf16", MASK_CAUSAL, 0),
+    # 16-key dK/dV pass with the dS band: keys below 1601 are behind every
+    # window, so their blocks are zeroed by the launcher and not visited
+    ("suffix_w200_wide_D256", 32, 16, 300, 2100, 256, "bf16", MASK_WINDOW, 200),
 ]
 
 
