@@ -53,10 +53,11 @@ __global__ void __launch_bounds__(256) delta_kernel(const E* __restrict__ O, con
   if (row < rows && c == 0) Delta[row] = s;
 }
 
-// Two workgroups per CU: 32-key tiles keep a workgroup's three stages of K and
-// dS^T tiles at 72 KB of LDS and its registers at 256 per lane. Tiles are
-// loaded two ahead (the dS^T tiles stream from HBM once), and one workgroup's
-// MFMAs run while the other waits.
+// Two workgroups per CU: 32-key tiles keep a workgroup's three stages of K
+// tiles and four of dS^T tiles at 80 KB of LDS (half the CU's) and its
+// registers at 256 per lane. K tiles are loaded two steps ahead, the dS^T
+// tiles (which stream from HBM once) three, and one workgroup's MFMAs run
+// while the other waits.
 template <int D, typename E>
 __global__ void __launch_bounds__(256, 2)
 dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ dQ, int Hq, int group, int Lq,
@@ -74,6 +75,7 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
   __shared__ __attribute__((aligned(16))) E sb0[ST];
   __shared__ __attribute__((aligned(16))) E sb1[ST];
   __shared__ __attribute__((aligned(16))) E sb2[ST];
+  __shared__ __attribute__((aligned(16))) E sb3[ST];
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,9 +120,10 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
   lds.init(w, lane, BQ);
   using LK = decltype(ldk);
   using LS = decltype(lds);
-  // every step issues the same number of loads per wave (past the last tile
-  // they cover no rows), so "tile t + 1 landed" is: at most that many of this
-  // wave's loads still outstanding (they complete in order)
+  // every step issues the same number of loads per wave, K blocks first (past
+  // the last tile they cover no rows), so "tile t + 1 landed" after step t
+  // is: at most step t's loads and step t - 1's dS^T loads still outstanding
+  // (they complete in order)
   constexpr int NLD = LK::NJ + LS::NJ;
   static_assert(LK::PER % NW == 0 && LS::PER % NW == 0, "every wave issues every step's loads");
 
@@ -128,25 +131,27 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
 #pragma unroll
   for (int d = 0; d < NDB; d++) acc[d] = zero16();
 
-  // one key tile: the K and dS^T loads of tile t + 2 (into the buffers tile
-  // t - 1 used) spread between the MFMAs
+  // one key tile: first the loads of K tile t + 2 and dS^T tile t + 3 (into the
+  // buffers tile t - 1 used), from every wave whether or not its rows meet
+  // this tile. Issued ahead of the branch, they leave the compiler's tracking
+  // of loads into LDS exact at the first operand read: after a branch that
+  // issued them on one side only, it made that read wait for every load in
+  // flight, the next tiles' included.
   auto step = [&](int t, const E* Kc, const E* Sc, E* Kn, E* Sn) {
     const int j0 = (kt_lo + t) * BK;
-    const bool more = t + 2 < nt;
+    const bool more = t + 2 < nt, more3 = t + 3 < nt;
     const int jn = more ? j0 + 2 * BK : 0;
     const auto krs = ldk.rsrc(Kg + (size_t)jn * D, more ? Lk - jn : 0);
-    const auto srs = lds.rsrc(Sb + (size_t)(t + 2) * ST, more ? BK : 0);
+    const auto srs = lds.rsrc(Sb + (size_t)(more3 ? t + 3 : 0) * ST, more3 ? BK : 0);
     auto load_one = [&, krs, srs](int j) {  // K blocks, then dS^T blocks
       if (j < LK::NJ) ldk.issue_one(Kn, krs, j, w);
       else lds.issue_one(Sn, srs, j - LK::NJ, w);
     };
     const bool active = wr0 <= wr1 && j0 <= wr1 + dhi && j0 + BK - 1 >= wr0 + dlo;
     const bool full = wr1 == wr0 + 31 && j0 >= wr1 + dlo && j0 + BK - 1 <= wr0 + dhi && j0 + BK <= Lk;
-    if (!active) {
 #pragma unroll
-      for (int j = 0; j < NLD; j++) load_one(j);
-      return;
-    }
+    for (int j = 0; j < NLD; j++) load_one(j);
+    if (!active) return;
     // B operands: dS^T rows [16 s, 16 s + 16) (keys), column = this lane's row,
     // paired k-slots j <-> key 16 s + 8 (j / 4) + 4 hh + (j % 4); masked on edge tiles
     ex8 bop[NKS];
@@ -162,7 +167,7 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
           if (!in_band(kb, 8 * (j >> 2) + (j & 3), span)) bop[s][j] = (E)0.f;
       }
     }
-    constexpr int NM = NKS * NDB, AH = 4, EVERY = NM / NLD > 0 ? NM / NLD : 1;
+    constexpr int NM = NKS * NDB, AH = 4;
     ex8 ka[AH];
     auto rd = [&](int k) { ka[k % AH] = op_tr<D, E>(Kc, la, 16 * (k / NDB), 32 * (k % NDB)); };
 #pragma unroll
@@ -171,12 +176,10 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
     for (int k = 0; k < NM; k++) {
       acc[k % NDB] = mfma(ka[k % AH], bop[k / NDB], acc[k % NDB]);
       if (k + AH < NM) rd(k + AH);
-      if (k % EVERY == EVERY - 1 && k / EVERY < NLD) load_one(k / EVERY);
     }
-#pragma unroll
-    for (int j = NM / EVERY; j < NLD; j++) load_one(j);
   };
 
+  constexpr int WAITN = NLD + LS::NJ;
   if (nt > 0) {
     zero_lds(kb0, KT, tid);
     zero_lds(kb1, KT, tid);
@@ -185,20 +188,26 @@ dsq_kernel(const E* __restrict__ dST, const E* __restrict__ K, E* __restrict__ d
     const int j1 = nt > 1 ? (kt_lo + 1) * BK : 0;
     ldk.issue(kb0, Kg + (size_t)kt_lo * BK * D, Lk - kt_lo * BK, w);
     lds.issue(sb0, Sb, BK, w);
+    lds.issue(sb1, Sb + (nt > 1 ? ST : 0), nt > 1 ? BK : 0, w);
     ldk.issue(kb1, Kg + (size_t)j1 * D, nt > 1 ? Lk - j1 : 0, w);
-    lds.issue(sb1, Sb + ST, nt > 1 ? BK : 0, w);
-    wait_vm_and_barrier<NLD>();
+    lds.issue(sb2, Sb + (nt > 2 ? 2 * ST : 0), nt > 2 ? BK : 0, w);
+    wait_vm_and_barrier<WAITN>();
   }
-  for (int t = 0; t < nt; t += 3) {
-    step(t, kb0, sb0, kb2, sb2);
-    wait_vm_and_barrier<NLD>();
-    if (t + 1 >= nt) break;
-    step(t + 1, kb1, sb1, kb0, sb0);
-    wait_vm_and_barrier<NLD>();
-    if (t + 2 >= nt) break;
-    step(t + 2, kb2, sb2, kb1, sb1);
-    wait_vm_and_barrier<NLD>();
+  // 12 steps per loop iteration (K buffers rotate by 3, dS^T buffers by 4);
+  // at the loop head the compiler still makes the first operand read wait for
+  // the loads of the step before, once per 12 steps
+#define DSQ_STEP(I)                                                                              \
+  if (t + I >= nt) break;                                                                        \
+  step(t + I, I % 3 == 0 ? kb0 : I % 3 == 1 ? kb1 : kb2,                                          \
+       I % 4 == 0 ? sb0 : I % 4 == 1 ? sb1 : I % 4 == 2 ? sb2 : sb3,                               \
+       (I + 2) % 3 == 0 ? kb0 : (I + 2) % 3 == 1 ? kb1 : kb2,                                      \
+       (I + 3) % 4 == 0 ? sb0 : (I + 3) % 4 == 1 ? sb1 : (I + 3) % 4 == 2 ? sb2 : sb3);            \
+  wait_vm_and_barrier<WAITN>();
+  for (int t = 0; t < nt; t += 12) {
+    DSQ_STEP(0) DSQ_STEP(1) DSQ_STEP(2) DSQ_STEP(3) DSQ_STEP(4) DSQ_STEP(5)
+    DSQ_STEP(6) DSQ_STEP(7) DSQ_STEP(8) DSQ_STEP(9) DSQ_STEP(10) DSQ_STEP(11)
   }
+#undef DSQ_STEP
   wait_all_and_barrier();  // (the last steps' no-op loads)
 
   // C tile = dQ^T: lane's column is its row, accumulator slot i holds head-dim

@@ -291,8 +291,23 @@ kv16_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restric
 
     // P and dS: lane's key kj, rows q0 + 16 rb + rg + i; row allowed iff it
     // lies in [ihi - kspan + 1, ihi] (or the second range)
-    const int base = ihi - q0 - rg, base2 = ihi2 - q0 - rg;
+    const int base2 = ihi2 - q0 - rg;
     auto form = [&](auto masked, f32x4& s, f32x4& p, int rb) {
+      int base = 0;
+      if constexpr (decltype(masked)::value) {
+        if constexpr (DENSE) {
+          // the row limit of the lane's key, rebuilt here from the lane id
+          // (the asm keeps it from being hoisted out of the tile loop): kept
+          // live across the loop it was spilled, and the wait for its reload
+          // (a vector-memory load) also waited for the next tile's loads on
+          // every edge tile
+          int l;
+          asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+          base = min(Lq - 1, kb0 + (l & 15) - dlo) - q0 - 4 * ((l >> 4) & 3);
+        } else {
+          base = ihi - q0 - rg;
+        }
+      }
       const float4 l4 = *(const float4*)(rv + 16 * rb + rg);
       const float4 d4 = *(const float4*)(rv + 32 + 16 * rb + rg);
 #pragma unroll
